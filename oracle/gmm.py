@@ -23,9 +23,15 @@ def gmm(X, W, expert_offsets):
 def gmm_int8(Xq, Wq, scales_x, scales_w, expert_offsets):
     """[GMM] §2.1 with the low-precision policy of §2.3 / §3.1 / §5.3:
         Y[m, n] = scales_x[m] * scales_w[e, n] * sum_k Xq[m, k] * Wq[e, n, k]
-    for m in [off[e], off[e+1]).  The integer sum is exact (int64); the two
-    scales are applied in float64.  Returns float64 [M, N]."""
-    Xq = np.asarray(Xq, dtype=np.int64)
+    for m in [off[e], off[e+1]).  The integer sum is exact: it is formed by a
+    float64 matmul of the int8 values, and every product and partial sum is
+    an integer of magnitude <= K * 127^2, below 2^53 for any K < 5e11, so no
+    step rounds whatever the summation order.  The two scales are applied in
+    float64.  Returns float64 [M, N]."""
+    K = np.asarray(Xq).shape[1]
+    if K * 127 * 127 >= 2 ** 53:
+        raise ValueError("K too large for an exact float64 integer sum")
+    Xq = np.asarray(Xq, dtype=np.float64)
     sx = np.asarray(scales_x, dtype=np.float64)
     sw = np.asarray(scales_w, dtype=np.float64)
     off = np.asarray(expert_offsets, dtype=np.int64)
@@ -35,8 +41,8 @@ def gmm_int8(Xq, Wq, scales_x, scales_w, expert_offsets):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi <= lo:
             continue
-        acc = Xq[lo:hi] @ np.asarray(Wq[e], dtype=np.int64).T   # exact
-        Y[lo:hi] = acc.astype(np.float64) * sx[lo:hi, None] * sw[e][None, :]
+        acc = Xq[lo:hi] @ np.asarray(Wq[e], dtype=np.float64).T   # exact integers
+        Y[lo:hi] = acc * sx[lo:hi, None] * sw[e][None, :]
     return Y
 
 

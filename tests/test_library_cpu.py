@@ -1,0 +1,184 @@
+"""Host-side checks of the C ABI library that need no GPU: it loads, exports
+every entry point include/moe.h declares, and its pure host functions and
+argument validation behave as documented (validation returns before any HIP
+call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def _defines():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(MOE_\w+)\s+(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def mod():
+    import moe_grouped_topk_amd as m
+    return m
+
+
+def test_header_declares_five_path_calls():
+    names = _declared()
+    for n in ["moe_route", "moe_align_block_size", "moe_grouped_gemm", "moe_forward",
+              "gmm_int8"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mod):
+    lib = ctypes.CDLL(mod.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_symbols_exported(mod):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mod.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(_declared())
+
+
+def test_codes_match_binding(mod):
+    d = _defines()
+    assert d["MOE_DTYPE_F32"] == mod.DTYPE["f32"] and d["MOE_DTYPE_BF16"] == mod.DTYPE["bf16"]
+    assert d["MOE_DTYPE_F16"] == mod.DTYPE["f16"]
+    assert d["MOE_SCORING_SOFTMAX"] == mod.SCORING["softmax"]
+    assert d["MOE_SCORING_SIGMOID"] == mod.SCORING["sigmoid"]
+
+
+def test_status_strings(mod):
+    d = _defines()
+    assert mod.moe_status_string(0) == "ok"
+    seen = set()
+    for k, v in d.items():
+        if k.startswith("MOE_ERR_"):
+            s = mod.moe_status_string(v)
+            assert s and s != "unknown status"
+            seen.add(s)
+    assert len(seen) == 6
+    assert mod.moe_status_string(12345) == "unknown status"
+
+
+def test_align_max_padded_bound(mod):
+    import oracle
+    import numpy as np
+    for P, E, B in [(0, 4, 16), (10, 8, 4), (128, 256, 16), (32768, 128, 128), (5, 1, 1)]:
+        got = mod.moe_align_max_padded(P, E, B)
+        assert got == oracle.align_max_padded(P, E, B)
+        assert got % B == 0
+    # the bound holds for adversarial counts (every expert count = 1 mod B)
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        E = int(rng.integers(1, 30)); B = int(rng.integers(1, 20))
+        ids = rng.integers(0, E, size=int(rng.integers(0, 60)))
+        _, _, total = oracle.moe_align_block_size(ids, E, B)
+        assert total <= mod.moe_align_max_padded(ids.size, E, B)
+    assert mod.moe_align_max_padded(-1, 4, 4) == -1
+
+
+def test_workspace_size(mod):
+    ws = mod.moe_forward_workspace_size(4096, 2048, 768, 128, 8)
+    P = 4096 * 8
+    maxp = mod.moe_align_max_padded(P, 128, 128)
+    assert ws >= 4 * P * 2 + 4 * maxp + 2 * maxp * 768 + 4 * P * 2048
+    assert ws % 256 == 0
+    assert mod.lib.moe_forward_workspace_size(16, 7168, 2048, 256, 8, 48) == 0   # bad block_m
+
+
+# ---- validation error paths (no HIP call is reached) -----------------------
+
+def test_route_validation(mod):
+    L, d = mod.lib, _defines()
+    fake = ctypes.c_void_p(256)
+    # E % G != 0
+    assert L.moe_route(fake, 4, 30, 2, 4, 2, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_CONFIG"]
+    # topk > Kg * E/G
+    assert L.moe_route(fake, 4, 32, 9, 4, 1, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_CONFIG"]
+    # topk_group > G
+    assert L.moe_route(fake, 4, 32, 2, 4, 5, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_CONFIG"]
+    # bad scoring
+    assert L.moe_route(fake, 4, 32, 2, 1, 1, 7, 1, 1.0, fake, fake, None) == d["MOE_ERR_CONFIG"]
+    # E too large, topk too large
+    assert L.moe_route(fake, 4, 2048, 2, 1, 1, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_route(fake, 4, 256, 65, 1, 1, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_SHAPE"]
+    # null outputs
+    assert L.moe_route(fake, 4, 32, 2, 1, 1, 0, 1, 1.0, None, fake, None) == d["MOE_ERR_NULL"]
+    assert L.moe_route(None, 4, 32, 2, 1, 1, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_NULL"]
+    assert L.moe_route(fake, -1, 32, 2, 1, 1, 0, 1, 1.0, fake, fake, None) == d["MOE_ERR_SHAPE"]
+
+
+def test_align_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    assert L.moe_align_block_size(f, 10, 8, 4, None, f, f, 36, None) == d["MOE_ERR_NULL"]
+    assert L.moe_align_block_size(None, 10, 8, 4, f, f, f, 36, None) == d["MOE_ERR_NULL"]
+    assert L.moe_align_block_size(f, 10, 8, 4, f, f, f, 35, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_align_block_size(f, 10, 2000, 4, f, f, f, 1 << 20, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_align_block_size(f, 10, 8, 0, f, f, f, 36, None) == d["MOE_ERR_CONFIG"]
+
+
+def test_gemm_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    base = dict(A=f, a_dtype=1, lda=128, a_rows=0, a_row_div=2, B=f, E=8, N=256, K=128,
+                s=f, e=f, tot=f, maxp=512, bm=64, nv=128, w=None, epi=1, C=f, c_dtype=1,
+                ldc=128, c_rows=1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.moe_grouped_gemm(a["A"], a["a_dtype"], a["lda"], a["a_rows"], a["a_row_div"],
+                                  a["B"], a["E"], a["N"], a["K"], a["s"], a["e"], a["tot"],
+                                  a["maxp"], a["bm"], a["nv"], a["w"], a["epi"], a["C"],
+                                  a["c_dtype"], a["ldc"], a["c_rows"], None)
+    assert call(A=None) == d["MOE_ERR_NULL"]
+    assert call(a_dtype=2) == d["MOE_ERR_DTYPE"]
+    assert call(c_dtype=9) == d["MOE_ERR_DTYPE"]
+    assert call(bm=48) == d["MOE_ERR_CONFIG"]
+    assert call(epi=5) == d["MOE_ERR_CONFIG"]
+    assert call(a_row_div=0) == d["MOE_ERR_CONFIG"]
+    assert call(K=100) == d["MOE_ERR_SHAPE"]
+    assert call(N=48) == d["MOE_ERR_SHAPE"]            # silu: N/2 % 16
+    assert call(lda=64) == d["MOE_ERR_SHAPE"]
+    assert call(ldc=64) == d["MOE_ERR_SHAPE"]
+    assert call(A=ctypes.c_void_p(264)) == d["MOE_ERR_SHAPE"]   # misaligned
+
+
+def test_forward_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    args = [f, 1, f, f, f, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, f, 1 << 30, None]
+    assert L.moe_forward(*args[:1], 5, *args[2:]) == d["MOE_ERR_DTYPE"]
+    a = list(args); a[19] = None
+    assert L.moe_forward(*a) == d["MOE_ERR_WORKSPACE"]
+    a = list(args); a[20] = 1024
+    assert L.moe_forward(*a) == d["MOE_ERR_WORKSPACE"]
+    a = list(args); a[6] = 100      # H % 16
+    assert L.moe_forward(*a) == d["MOE_ERR_SHAPE"]
+    a = list(args); a[15] = 24      # block_m
+    assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[0] = None
+    assert L.moe_forward(*a) == d["MOE_ERR_NULL"]
+
+
+def test_gmm_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4008, 4096, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4096, 4100, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4096, 4096, 0, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, None, f, f, f, None, f, 2048, 4096, 4096, 32, None) == d["MOE_ERR_NULL"]
+    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 1 << 20, 4096, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(None, f, None, f, f, None, None, 0, 4096, 4096, 32, None) == 0   # M = 0

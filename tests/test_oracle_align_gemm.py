@@ -247,3 +247,15 @@ def test_gmm_int8_extreme_accumulation():
     Y = oracle.gmm_int8(Xq, Wq, np.ones(2), np.ones((1, 3)), np.array([0, 2]))
     assert Y[0].tolist() == [-66064384.0] * 3
     assert Y[1].tolist() == [66064384.0] * 3
+
+
+def test_gmm_int8_sum_equals_int64_sum():
+    """The float64 integer sums equal exact int64 sums (random int8 data)."""
+    rng = np.random.default_rng(6)
+    Xq = rng.integers(-127, 128, size=(7, 512)).astype(np.int8)
+    Wq = rng.integers(-127, 128, size=(2, 9, 512)).astype(np.int8)
+    off = np.array([0, 3, 7])
+    Y = oracle.gmm_int8(Xq, Wq, np.ones(7), np.ones((2, 9)), off)
+    for e in range(2):
+        exact = Xq[off[e]:off[e + 1]].astype(np.int64) @ Wq[e].astype(np.int64).T
+        assert (Y[off[e]:off[e + 1]] == exact).all()

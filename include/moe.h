@@ -1,0 +1,235 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) fused Mixture-of-Experts forward path.
+ *
+ * Sources of the operations (cited by tag below):
+ *   [P1]  DatenLord, "From loops to fusion: the Fused MoE operator, Part 3"
+ *         (community.aijishu.com/a/1060000000523566), sections 01 and 03.
+ *   [GTK] "GroupedTopK operator optimisation primer" (blog.freezetheflame.cc),
+ *         sections 二 (interface), 三 (3.1-3.6 semantics), 七 (shortcut),
+ *         八 (top-k pitfalls).
+ *   [MSG] mini-sglang handbook, "MoE and fused MoE"
+ *         (anrans.github.io/ai-infra-handbooks/minisgl/perf/moe/), sections
+ *         路由 (select_experts), fused MoE (moe_align_block_size,
+ *         fused_moe_kernel, FusedMoeBackend.forward), 练习 (exercise 3).
+ *   [GMM] low-precision grouped GEMM article (www.pwwt.cn/news/5863887/),
+ *         sections 2.1 (definition), 3.1 (interface), 3.4 (layout), 5.3.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller, unless the
+ *     argument says otherwise.  The library never frees or keeps them.
+ *   - Tensors are dense and row-major.  Expert weights are [E, N, K] with K
+ *     contiguous ([GMM] 3.4).  bf16 means IEEE bfloat16 bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream; none synchronises the
+ *     host, so device-side totals (e.g. the padded length) stay on the device.
+ *   - Arguments are validated on the host before anything is enqueued.  On an
+ *     error nothing is launched and a negative MOE_ERR_* code is returned;
+ *     MOE_ERR_HIP reports a failed launch (hipGetLastError).  No C++
+ *     exception crosses this boundary.  Calls are reentrant and hold no
+ *     global state; calls that write the same buffers must be ordered by the
+ *     caller (same stream, or events).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK             0
+#define MOE_ERR_NULL      -1   /* a required pointer is NULL               */
+#define MOE_ERR_SHAPE     -2   /* a size is out of range or inconsistent   */
+#define MOE_ERR_CONFIG    -3   /* an option value or combination is invalid */
+#define MOE_ERR_DTYPE     -4   /* unsupported dtype code                   */
+#define MOE_ERR_WORKSPACE -5   /* workspace missing or too small           */
+#define MOE_ERR_HIP       -6   /* the HIP runtime reported a launch error  */
+
+/* ---- enumerations ------------------------------------------------------ */
+#define MOE_DTYPE_F32   0
+#define MOE_DTYPE_BF16  1
+#define MOE_DTYPE_F16   2
+
+#define MOE_SCORING_SOFTMAX 0
+#define MOE_SCORING_SIGMOID 1
+
+#define MOE_EPILOGUE_NONE     0   /* C = A_row . B[e]^T                      */
+#define MOE_EPILOGUE_SILU_MUL 1   /* C = silu(A.Bgate^T) * (A.Bup^T)         */
+
+#define MOE_ROWS_PAIR   0   /* row index = pair index (token*topk + k)      */
+#define MOE_ROWS_SORTED 1   /* row index = position in sorted_token_ids     */
+
+/* Largest supported sizes (validated; MOE_ERR_SHAPE beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK    64
+
+/* Human-readable name of a status code (static storage, never NULL). */
+MOE_API const char* moe_status_string(int status);
+
+/* ---- routing -----------------------------------------------------------
+ * moe_route: GroupedTopK routing of [GTK] 三 3.1-3.6; plain top-k routing
+ * ([MSG] 路由, select_experts) is the case num_expert_group = topk_group = 1.
+ * Per token t:
+ *   1. scores s = softmax over the row ([GTK] 3.1, max subtracted) or
+ *      sigmoid of each logit (scoring = MOE_SCORING_SIGMOID);
+ *   2. group score = MAX score inside each of the num_expert_group
+ *      contiguous groups of E / num_expert_group experts ([GTK] 3.2);
+ *   3. keep the topk_group best groups ([GTK] 3.3), mask the rest ([GTK] 3.4);
+ *   4. topk best experts among the kept groups ([GTK] 3.5);
+ *   5. if renormalize, divide the topk scores by their sum ([GTK] 3.6);
+ *   6. multiply by routed_scaling_factor (always, last; [GTK] 3.6).
+ * Ties (equal logits / equal group maxima) go to the lower index.  Outputs
+ * are ordered by descending score.  Selection compares logits directly
+ * (both scorings are monotone, [GTK] 七), so it does not depend on how the
+ * scores round.  hidden_states play no part ([GTK] 二) and are not taken.
+ *
+ *   gating          [T, E] float32 router logits, row-major (read only).
+ *   topk_weights    [T, topk] float32 out.
+ *   topk_ids        [T, topk] int32 out, expert ids in [0, E).
+ * Errors: NULL pointers (T > 0); T < 0; E < 1 or E > MOE_MAX_EXPERTS;
+ * E % num_expert_group != 0; num_expert_group > 64; topk_group outside
+ * [1, num_expert_group]; topk outside [1, MOE_MAX_TOPK] or larger than
+ * topk_group * (E / num_expert_group) -> MOE_ERR_SHAPE / MOE_ERR_CONFIG.
+ * NaN and +inf logits are outside the contract (no fault, unspecified ids);
+ * -inf logits are allowed and rank last.  T = 0 is a no-op.
+ */
+MOE_API int moe_route(const float* gating, int64_t T, int32_t E, int32_t topk,
+              int32_t num_expert_group, int32_t topk_group, int32_t scoring,
+              int32_t renormalize, float routed_scaling_factor,
+              float* topk_weights, int32_t* topk_ids, void* stream);
+
+/* ---- alignment ---------------------------------------------------------
+ * moe_align_block_size: [MSG] fused MoE, moe_align_block_size.  The pairs
+ * are the num_pairs entries of the flattened topk_ids (pair i = token
+ * i / topk, slot i % topk).  Pairs are grouped by expert in ascending expert
+ * order, keeping ascending pair order inside each expert (a stable sort);
+ * each expert's segment is padded with the placeholder value num_pairs up to
+ * a multiple of block_m; experts without pairs get no segment.
+ *
+ *   topk_ids               [num_pairs] int32 in [0, E) (read only).
+ *   sorted_token_ids       [max_padded] int32 out.  Entries [0, total) hold
+ *                          the segments; entries [total, max_padded) are set
+ *                          to num_pairs.
+ *   expert_ids             [max_padded / block_m] int32 out: the expert of
+ *                          each block of block_m entries; blocks at or past
+ *                          total / block_m are set to -1 (an extension: the
+ *                          GEMMs stop there without reading the total).
+ *   num_tokens_post_padded [1] int32 out: total (a multiple of block_m).
+ *   max_padded             capacity of sorted_token_ids; must be at least
+ *                          moe_align_max_padded(num_pairs, E, block_m).
+ * Errors: NULLs, num_pairs < 0 or >= 2^31, E outside [1, MOE_MAX_EXPERTS],
+ * block_m outside [1, 1024], max_padded too small.  Expert ids outside
+ * [0, E) are outside the contract (they are dropped, not written).
+ */
+MOE_API int64_t moe_align_max_padded(int64_t num_pairs, int32_t E, int32_t block_m);
+
+MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E,
+                         int32_t block_m, int32_t* sorted_token_ids,
+                         int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                         int64_t max_padded, void* stream);
+
+/* ---- grouped GEMM ------------------------------------------------------
+ * moe_grouped_gemm: [MSG] fused MoE, fused_moe_kernel, with the gathered
+ * weight never materialised ([P1] 01): for every block b of block_m entries
+ * of sorted_token_ids below the device total, expert e = expert_ids[b], and
+ * every entry p (pair index) < num_valid_pairs at sorted position s:
+ *     a   = A row  (p / a_row_div  if a_rows == MOE_ROWS_PAIR,
+ *                   s             if a_rows == MOE_ROWS_SORTED)
+ *     acc = a . B[e]^T                       (fp32 accumulation, bf16 MFMA)
+ *     EPILOGUE_NONE:     c = acc                               (N columns)
+ *     EPILOGUE_SILU_MUL: c[j] = silu(acc[j]) * acc[N/2 + j]    (N/2 columns;
+ *                        gate rows of B first, up rows second, [MSG] 练习 3)
+ *     c *= topk_weights[p]                   (if topk_weights != NULL)
+ *     C row (p if c_rows == MOE_ROWS_PAIR, s if MOE_ROWS_SORTED) = c.
+ * Placeholder entries (p >= num_valid_pairs) are neither read nor written.
+ *
+ *   A        rows of K elements, row stride lda elements; a_dtype BF16 or
+ *            F32 (F32 rows are rounded to bf16 on load).
+ *   B        [E, N, K] bf16, K contiguous.
+ *   C        row stride ldc elements; c_dtype F32, BF16 or F16.
+ *   sorted_token_ids / expert_ids / num_tokens_post_padded: as written by
+ *            moe_align_block_size with the same block_m; max_padded is the
+ *            capacity of sorted_token_ids (the launch is sized by it and the
+ *            device total cuts it short).
+ *   block_m  16 or 32 (weight-streaming kernel for few rows per expert) or
+ *            64 or 128 (MFMA tile kernel).
+ * Requirements: K % 8 == 0, N % 16 == 0 (SILU_MUL: (N/2) % 16 == 0),
+ * lda >= K and ldc >= output width, both multiples of 8; A, B and C
+ * 16-byte aligned.
+ */
+MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows,
+                     int32_t a_row_div, const void* B, int32_t E, int64_t N,
+                     int64_t K, const int32_t* sorted_token_ids,
+                     const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_padded, int64_t max_padded,
+                     int32_t block_m, int64_t num_valid_pairs,
+                     const float* topk_weights, int32_t epilogue, void* C,
+                     int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream);
+
+/* ---- whole layer -------------------------------------------------------
+ * moe_forward: [MSG] fused MoE, FusedMoeBackend.forward, with routing per
+ * moe_route: route -> align -> gate_up GEMM with silu(gate)*up in its
+ * epilogue (intermediate h kept in sorted order, bf16) -> down GEMM times
+ * the routing weight -> per-token sum over the topk slots, written in x's
+ * dtype.  out[t] = sum_k w[t,k] * W2[e] (silu(W1g[e] x[t]) * (W1u[e] x[t])).
+ *
+ *   x        [T, H] bf16 or f32 (x_dtype); out [T, H] in the same dtype.
+ *   gating   [T, E] f32 logits.
+ *   w1       [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)).
+ *   w2       [E, H, I] bf16.
+ *   topk_weights_out [T, topk] f32, topk_ids_out [T, topk] int32: optional
+ *            (NULL = kept in the workspace only).
+ *   block_m  0 = chosen from the shape (few pairs per expert -> 16, else 128);
+ *            otherwise one of the moe_grouped_gemm block sizes.
+ *   ws       device workspace of at least moe_forward_workspace_size(...)
+ *            bytes for the same arguments (256-byte aligned).
+ * Requirements: H % 16 == 0, I % 16 == 0, plus moe_route's.
+ */
+MOE_API size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
+                                  int32_t topk, int32_t block_m);
+
+MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
+                const void* w1, const void* w2, int64_t T, int32_t H, int32_t I,
+                int32_t E, int32_t topk, int32_t num_expert_group,
+                int32_t topk_group, int32_t scoring, int32_t renormalize,
+                float routed_scaling_factor, int32_t block_m, void* out,
+                float* topk_weights_out, int32_t* topk_ids_out, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* ---- INT8 grouped GEMM -------------------------------------------------
+ * gmm_int8: [GMM] 2.1 and 3.1.  The input rows are sorted by expert; rows
+ * [expert_offsets[e], expert_offsets[e+1]) belong to expert e, and
+ *   output[m, n] = fp16( scales_x[m] * scales_w[e, n] *
+ *                        sum_k input[m, k] * weights[e, n, k] )
+ * with the integer sum accumulated exactly in int32 ([GMM] 5.3) and the
+ * scales applied in fp32.  Output rows stay in input order.
+ *
+ *   input          [M, K] int8.       weights   [E, N, K] int8 (K contiguous).
+ *   scales_x       [M] f32 per row.   scales_w  [E, N] f32 per output channel.
+ *   expert_offsets [E + 1] int32, non-decreasing, offsets[0] = 0,
+ *                  offsets[E] = M (device memory; checked on the device only
+ *                  by clamping, so rows outside [0, M) are never touched).
+ *   expert_sizes   optional [E] int32 (may be NULL); the offsets decide.
+ *   output         [M, N] fp16.
+ * Requirements: K % 16 == 0, N % 16 == 0, K <= 131072 (exact int32 sums),
+ * E in [1, MOE_MAX_EXPERTS].
+ */
+MOE_API int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
+             const float* scales_w, const int32_t* expert_offsets,
+             const int32_t* expert_sizes, void* output, int64_t M, int64_t K,
+             int64_t N, int32_t E, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,231 @@
+"""Python binding of libmoe.so, the gfx950 fused-MoE library (include/moe.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors on the current ROCm device; outputs that
+are not passed in are allocated with torch.empty (device memory plumbing).
+Every call enqueues on torch's current stream and does not synchronise.
+
+The package fails loudly at import if the library has not been built; there
+is no CPU fallback.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "MoeError", "LIB_PATH", "lib", "moe_status_string", "moe_route",
+    "moe_align_max_padded", "moe_align_block_size", "moe_grouped_gemm",
+    "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+# Codes of include/moe.h
+DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
+SCORING = {"softmax": 0, "sigmoid": 1}
+EPILOGUE = {"none": 0, "silu_mul": 1}
+ROWS = {"pair": 0, "sorted": 1}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %d (%s)" % (fn, status, moe_status_string(status)))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libmoe.so is not built (%s); build it with "
+            "`python -m moe_grouped_topk_amd.build` or __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_float, ctypes.c_size_t)
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_route.argtypes = [vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_align_max_padded.argtypes = [i64, i32, i32]
+    L.moe_align_max_padded.restype = i64
+    L.moe_align_block_size.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, vp]
+    L.moe_align_block_size.restype = ctypes.c_int
+    L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i64, i64, vp, vp, vp, i64,
+                                   i32, i64, vp, i32, vp, i32, i64, i32, vp]
+    L.moe_grouped_gemm.restype = ctypes.c_int
+    L.moe_forward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.moe_forward_workspace_size.restype = sz
+    L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32,
+                              f32, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_forward.restype = ctypes.c_int
+    L.gmm_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.gmm_int8.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def moe_status_string(status):
+    return lib.moe_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous torch tensor on the GPU (or None)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t):
+    torch = _torch()
+    return {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}[t.dtype]
+
+
+def moe_route(gating, topk, num_expert_group=1, topk_group=1, scoring="softmax",
+              renormalize=True, routed_scaling_factor=1.0, topk_weights=None,
+              topk_ids=None, stream=None):
+    """Grouped / plain top-k routing of gating [T, E] float32 logits.
+    Returns (topk_weights [T, topk] float32, topk_ids [T, topk] int32)."""
+    torch = _torch()
+    T, E = gating.shape
+    if topk_weights is None:
+        topk_weights = torch.empty((T, topk), dtype=torch.float32, device=gating.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=gating.device)
+    _check("moe_route", lib.moe_route(
+        _ptr(gating, torch.float32, "gating"), T, E, topk, num_expert_group, topk_group,
+        SCORING[scoring], int(bool(renormalize)), float(routed_scaling_factor),
+        _ptr(topk_weights, torch.float32, "topk_weights"),
+        _ptr(topk_ids, torch.int32, "topk_ids"), _stream(stream)))
+    return topk_weights, topk_ids
+
+
+def moe_align_max_padded(num_pairs, num_experts, block_m):
+    return int(lib.moe_align_max_padded(int(num_pairs), int(num_experts), int(block_m)))
+
+
+def moe_align_block_size(topk_ids, num_experts, block_m, sorted_token_ids=None,
+                         expert_ids=None, num_tokens_post_padded=None, stream=None):
+    """Returns (sorted_token_ids [max_padded] int32, expert_ids
+    [max_padded // block_m] int32, num_tokens_post_padded [1] int32)."""
+    torch = _torch()
+    P = topk_ids.numel()
+    cap = moe_align_max_padded(P, num_experts, block_m)
+    dev = topk_ids.device
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+    if num_tokens_post_padded is None:
+        num_tokens_post_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    if expert_ids.numel() < sorted_token_ids.numel() // block_m:
+        raise ValueError("expert_ids is smaller than sorted_token_ids / block_m")
+    _check("moe_align_block_size", lib.moe_align_block_size(
+        _ptr(topk_ids, torch.int32, "topk_ids"), P, num_experts, block_m,
+        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _ptr(expert_ids, torch.int32, "expert_ids"),
+        _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
+        sorted_token_ids.numel(), _stream(stream)))
+    return sorted_token_ids, expert_ids, num_tokens_post_padded
+
+
+def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded, block_m,
+                     num_valid_pairs, a_rows="pair", a_row_div=1, topk_weights=None,
+                     epilogue="none", C=None, c_dtype=None, c_rows="pair", c_num_rows=None,
+                     stream=None):
+    """Sorted grouped GEMM.  A [rows, K] (bf16 or f32), B [E, N, K] bf16.
+    C is allocated as [c_num_rows or (num_valid_pairs if c_rows == 'pair'
+    else len(sorted_token_ids)), N or N/2] of c_dtype (default A's dtype)."""
+    torch = _torch()
+    E, N, K = B.shape
+    nout = N // 2 if epilogue == "silu_mul" else N
+    if C is None:
+        rows = c_num_rows if c_num_rows is not None else (
+            num_valid_pairs if c_rows == "pair" else sorted_token_ids.numel())
+        C = torch.empty((rows, nout), dtype=c_dtype or A.dtype, device=A.device)
+    if expert_ids.numel() < sorted_token_ids.numel() // block_m:
+        raise ValueError("expert_ids is smaller than sorted_token_ids / block_m")
+    _check("moe_grouped_gemm", lib.moe_grouped_gemm(
+        _ptr(A, None, "A"), _dtype_code(A), A.shape[-1], ROWS[a_rows], a_row_div,
+        _ptr(B, torch.bfloat16, "B"), E, N, K,
+        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _ptr(expert_ids, torch.int32, "expert_ids"),
+        _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
+        sorted_token_ids.numel(), block_m, num_valid_pairs,
+        _ptr(topk_weights, torch.float32, "topk_weights"), EPILOGUE[epilogue],
+        _ptr(C, None, "C"), _dtype_code(C), C.shape[-1], ROWS[c_rows], _stream(stream)))
+    return C
+
+
+def moe_forward_workspace_size(T, H, I, E, topk, block_m=0):
+    return int(lib.moe_forward_workspace_size(T, H, I, E, topk, block_m))
+
+
+def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,
+                scoring="softmax", renormalize=True, routed_scaling_factor=1.0,
+                block_m=0, out=None, topk_weights_out=None, topk_ids_out=None,
+                workspace=None, stream=None):
+    """Whole fused-MoE layer: x [T, H] (bf16 or f32), gating [T, E] f32,
+    w1 [E, 2I, H] bf16, w2 [E, H, I] bf16.  Returns out [T, H] in x's dtype."""
+    torch = _torch()
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    if out is None:
+        out = torch.empty_like(x)
+    need = moe_forward_workspace_size(T, H, I, E, topk, block_m)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_forward", lib.moe_forward(
+        _ptr(x, None, "x"), _dtype_code(x), _ptr(gating, torch.float32, "gating"),
+        _ptr(w1, torch.bfloat16, "w1"), _ptr(w2, torch.bfloat16, "w2"), T, H, I, E, topk,
+        num_expert_group, topk_group, SCORING[scoring], int(bool(renormalize)),
+        float(routed_scaling_factor), block_m, _ptr(out, x.dtype, "out"),
+        _ptr(topk_weights_out, torch.float32, "topk_weights_out"),
+        _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out
+
+
+def gmm_int8(input, weights, scales_x, scales_w, expert_offsets, expert_sizes=None,
+             output=None, stream=None):
+    """INT8 grouped GEMM: input [M, K] int8 sorted by expert, weights [E, N, K]
+    int8, scales_x [M] f32, scales_w [E, N] f32, expert_offsets [E+1] int32.
+    Returns output [M, N] float16."""
+    torch = _torch()
+    M, K = input.shape
+    E, N, _ = weights.shape
+    if output is None:
+        output = torch.empty((M, N), dtype=torch.float16, device=input.device)
+    _check("gmm_int8", lib.gmm_int8(
+        _ptr(input, torch.int8, "input"), _ptr(weights, torch.int8, "weights"),
+        _ptr(scales_x, torch.float32, "scales_x"), _ptr(scales_w, torch.float32, "scales_w"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(expert_sizes, torch.int32, "expert_sizes"), _ptr(output, torch.float16, "output"),
+        M, K, N, E, _stream(stream)))
+    return output

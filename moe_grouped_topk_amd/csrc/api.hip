@@ -1,0 +1,261 @@
+// C ABI of the fused-MoE library: argument validation, workspace layout and
+// the enqueue order of the layer.  Declarations and the contract of every
+// entry point are in include/moe.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape and option checks of the routing step (pointers are checked by the caller).
+int check_route_shape(int64_t T, int32_t E, int32_t topk, int32_t G, int32_t Kg, int32_t scoring) {
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (topk < 1 || topk > MOE_MAX_TOPK || topk > E) return MOE_ERR_SHAPE;
+  if (G < 1 || G > 64 || E % G != 0) return MOE_ERR_CONFIG;
+  if (Kg < 1 || Kg > G) return MOE_ERR_CONFIG;
+  if ((int64_t)topk > (int64_t)Kg * (E / G)) return MOE_ERR_CONFIG;
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SIGMOID) return MOE_ERR_CONFIG;
+  if (T * (int64_t)topk >= INT32_MAX) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+bool valid_block_m(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+int64_t align_max_padded(int64_t P, int32_t E, int32_t B) {
+  const int64_t nonempty = P < E ? P : E;
+  const int64_t bound = P + nonempty * (B - 1);
+  return (bound + B - 1) / B * B;
+}
+
+int check_gemm(const moe::MoeGemmArgs& a) {
+  if (!a.A || !a.B || !a.C || !a.sorted_ids || !a.expert_ids || !a.total) return MOE_ERR_NULL;
+  if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (a.c_dtype != MOE_DTYPE_F32 && a.c_dtype != MOE_DTYPE_BF16 && a.c_dtype != MOE_DTYPE_F16)
+    return MOE_ERR_DTYPE;
+  if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_SILU_MUL) return MOE_ERR_CONFIG;
+  if (a.a_rows != MOE_ROWS_PAIR && a.a_rows != MOE_ROWS_SORTED) return MOE_ERR_CONFIG;
+  if (a.c_rows != MOE_ROWS_PAIR && a.c_rows != MOE_ROWS_SORTED) return MOE_ERR_CONFIG;
+  if (!valid_block_m(a.block_m)) return MOE_ERR_CONFIG;
+  if (a.a_rows == MOE_ROWS_PAIR && a.a_row_div < 1) return MOE_ERR_CONFIG;
+  if (a.E < 1 || a.N < 16 || a.K < 8 || a.K % 8 != 0) return MOE_ERR_SHAPE;
+  const int64_t nout = a.epilogue == MOE_EPILOGUE_SILU_MUL ? a.N / 2 : a.N;
+  if (a.epilogue == MOE_EPILOGUE_SILU_MUL ? (a.N % 32 != 0) : (a.N % 16 != 0)) return MOE_ERR_SHAPE;
+  if (a.lda < a.K || a.lda % 8 != 0) return MOE_ERR_SHAPE;
+  if (a.ldc < nout || a.ldc % 8 != 0) return MOE_ERR_SHAPE;
+  if (a.num_valid < 0 || a.num_valid >= INT32_MAX) return MOE_ERR_SHAPE;
+  if (a.max_padded < 0 || a.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
+  if (!aligned16(a.A) || !aligned16(a.B) || !aligned16(a.C)) return MOE_ERR_SHAPE;
+  // grid sizes stay inside 32-bit workgroup counts
+  const int64_t ntile = (nout + 63) / 64 + 1;
+  if ((a.max_padded / a.block_m) * ntile >= INT32_MAX) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int enqueue_gemm(const moe::MoeGemmArgs& a, hipStream_t s) {
+  if (a.max_padded == 0) return MOE_OK;
+  const hipError_t err = a.block_m <= 32 ? moe::launch_moe_gemm_stream(a, s)
+                                         : moe::launch_moe_gemm_tile(a, s);
+  return hip_status(err);
+}
+
+int choose_block_m(int64_t T, int32_t E, int32_t topk) {
+  const double avg = (double)T * topk / (double)E;   // pairs per expert
+  if (avg < 8.0) return 16;
+  if (avg < 24.0) return 32;
+  if (avg < 96.0) return 64;
+  return 128;
+}
+
+struct ForwardLayout {
+  size_t w, ids, sorted, eids, total, h, y, bytes;
+  int64_t max_padded;
+  int block_m;
+};
+
+ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                             int32_t block_m) {
+  ForwardLayout L{};
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk);
+  const int64_t P = T * topk;
+  L.max_padded = align_max_padded(P, E, L.block_m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+  L.w = take(sizeof(float) * (size_t)P);
+  L.ids = take(sizeof(int32_t) * (size_t)P);
+  L.sorted = take(sizeof(int32_t) * (size_t)L.max_padded);
+  L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
+  L.total = take(sizeof(int32_t));
+  L.h = take(2 * (size_t)L.max_padded * (size_t)I);
+  L.y = take(sizeof(float) * (size_t)P * (size_t)H);
+  L.bytes = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer argument";
+    case MOE_ERR_SHAPE: return "size out of range or inconsistent";
+    case MOE_ERR_CONFIG: return "invalid option or option combination";
+    case MOE_ERR_DTYPE: return "unsupported dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const float* gating, int64_t T, int32_t E, int32_t topk, int32_t num_expert_group,
+              int32_t topk_group, int32_t scoring, int32_t renormalize,
+              float routed_scaling_factor, float* topk_weights, int32_t* topk_ids,
+              void* stream) {
+  const int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!gating || !topk_weights || !topk_ids)) return MOE_ERR_NULL;
+  return hip_status(moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
+                                      renormalize ? 1 : 0, routed_scaling_factor, topk_weights,
+                                      topk_ids, as_stream(stream)));
+}
+
+int64_t moe_align_max_padded(int64_t num_pairs, int32_t E, int32_t block_m) {
+  if (num_pairs < 0 || E < 1 || block_m < 1) return -1;
+  return align_max_padded(num_pairs, E, block_m);
+}
+
+int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, int32_t block_m,
+                         int32_t* sorted_token_ids, int32_t* expert_ids,
+                         int32_t* num_tokens_post_padded, int64_t max_padded, void* stream) {
+  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded) return MOE_ERR_NULL;
+  if (num_pairs > 0 && !topk_ids) return MOE_ERR_NULL;
+  if (num_pairs < 0 || num_pairs >= INT32_MAX) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (block_m < 1 || block_m > 1024) return MOE_ERR_CONFIG;
+  if (max_padded < align_max_padded(num_pairs, E, block_m) || max_padded >= INT32_MAX)
+    return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_align(topk_ids, num_pairs, E, block_m, sorted_token_ids,
+                                      expert_ids, num_tokens_post_padded, max_padded,
+                                      as_stream(stream)));
+}
+
+int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows, int32_t a_row_div,
+                     const void* B, int32_t E, int64_t N, int64_t K,
+                     const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                     const int32_t* num_tokens_post_padded, int64_t max_padded, int32_t block_m,
+                     int64_t num_valid_pairs, const float* topk_weights, int32_t epilogue, void* C,
+                     int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream) {
+  moe::MoeGemmArgs a{};
+  a.A = A; a.a_dtype = a_dtype; a.lda = lda; a.a_rows = a_rows;
+  a.a_row_div = a_row_div < 1 ? 1 : a_row_div;
+  if (a_rows == MOE_ROWS_PAIR && a_row_div < 1) return MOE_ERR_CONFIG;
+  a.B = B; a.E = E; a.N = N; a.K = K;
+  a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.total = num_tokens_post_padded;
+  a.max_padded = max_padded; a.block_m = block_m; a.num_valid = num_valid_pairs;
+  a.topk_weights = topk_weights; a.epilogue = epilogue;
+  a.C = C; a.c_dtype = c_dtype; a.ldc = ldc; a.c_rows = c_rows;
+  const int st = check_gemm(a);
+  if (st != MOE_OK) return st;
+  return enqueue_gemm(a, as_stream(stream));
+}
+
+size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                  int32_t block_m) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
+  if (block_m != 0 && !valid_block_m(block_m)) return 0;
+  return forward_layout(T, H, I, E, topk, block_m).bytes;
+}
+
+int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void* w1, const void* w2,
+                int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                int32_t num_expert_group, int32_t topk_group, int32_t scoring,
+                int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
+                float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
+  if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0) return MOE_ERR_SHAPE;
+  int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !gating || !w1 || !w2 || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_SHAPE;
+  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m);
+  if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
+  if (L.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
+
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  float* w = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(base + L.w);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(base + L.eids);
+  int32_t* total = reinterpret_cast<int32_t*>(base + L.total);
+  void* h = base + L.h;
+  float* y = reinterpret_cast<float*>(base + L.y);
+  hipStream_t s = as_stream(stream);
+  const int64_t P = T * topk;
+
+  hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
+                                     renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_align(ids, P, E, L.block_m, sorted, eids, total, L.max_padded, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+
+  moe::MoeGemmArgs g1{};
+  g1.A = x; g1.a_dtype = x_dtype; g1.lda = H; g1.a_rows = MOE_ROWS_PAIR; g1.a_row_div = topk;
+  g1.B = w1; g1.E = E; g1.N = 2 * (int64_t)I; g1.K = H;
+  g1.sorted_ids = sorted; g1.expert_ids = eids; g1.total = total; g1.max_padded = L.max_padded;
+  g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
+  g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I;
+  g1.c_rows = MOE_ROWS_SORTED;
+  st = check_gemm(g1);
+  if (st != MOE_OK) return st;
+
+  moe::MoeGemmArgs g2 = g1;
+  g2.A = h; g2.a_dtype = MOE_DTYPE_BF16; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1;
+  g2.B = w2; g2.N = H; g2.K = I; g2.topk_weights = w; g2.epilogue = MOE_EPILOGUE_NONE;
+  g2.C = y; g2.c_dtype = MOE_DTYPE_F32; g2.ldc = H; g2.c_rows = MOE_ROWS_PAIR;
+  st = check_gemm(g2);
+  if (st != MOE_OK) return st;
+
+  st = enqueue_gemm(g1, s);
+  if (st != MOE_OK) return st;
+  st = enqueue_gemm(g2, s);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_topk_reduce(y, T, topk, H, out, x_dtype, s));
+}
+
+int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
+             const float* scales_w, const int32_t* expert_offsets, const int32_t* expert_sizes,
+             void* output, int64_t M, int64_t K, int64_t N, int32_t E, void* stream) {
+  (void)expert_sizes;   // the offsets decide; sizes are redundant
+  if (M < 0 || M >= INT32_MAX / 2) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (K < 16 || K % 16 != 0 || K > 131072) return MOE_ERR_SHAPE;
+  if (N < 16 || N % 16 != 0) return MOE_ERR_SHAPE;
+  if (!weights || !scales_w || !expert_offsets) return MOE_ERR_NULL;
+  if (M > 0 && (!input || !scales_x || !output)) return MOE_ERR_NULL;
+  if (M == 0) return MOE_OK;
+  if (!aligned16(input) || !aligned16(weights) || !aligned16(scales_w) || !aligned16(output))
+    return MOE_ERR_SHAPE;
+  const int64_t grid = ((M + 127) / 128 + E) * ((N + 127) / 128);
+  if (grid >= INT32_MAX) return MOE_ERR_SHAPE;
+  moe::GmmI8Args a{input, weights, scales_x, scales_w, expert_offsets, output, M, K, N, E};
+  return hip_status(moe::launch_gmm_int8(a, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device-side helpers shared by the gfx950 kernels of the fused-MoE path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// Order-preserving 32-bit key of a float: a > b  <=>  key(a) > key(b) for
+// non-NaN values; -0.0 is folded onto +0.0 so equal values get equal keys.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_key (exact).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
+  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint32_t o = __shfl_xor(v, m, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Workgroups of a 1-D grid are handed to the XCDs round-robin (id i goes to
+// XCD i % 8).  This maps the hardware id onto a logical tile id so that each
+// XCD receives one contiguous run of logical tiles; tiles that share
+// operands then share that XCD's L2.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const int q = n / kNumXcd, r = n % kNumXcd;
+  return xcd * q + (xcd < r ? xcd : r) + slot;
+}
+
+__device__ __forceinline__ float silu_f32(float z) {
+  return z / (1.0f + __expf(-z));
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// Store 4 consecutive fp32 values converted to the output dtype
+// (0 = f32, 1 = bf16, 2 = f16).  dst is element-aligned to 4 elements.
+template <int CDT>
+__device__ __forceinline__ void store4(void* dst, float a, float b, float c, float d) {
+  if constexpr (CDT == 0) {
+    f32x4_t v = {a, b, c, d};
+    *reinterpret_cast<f32x4_t*>(dst) = v;
+  } else if constexpr (CDT == 1) {
+    uint2 v = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+    *reinterpret_cast<uint2*>(dst) = v;
+  } else {
+    uint2 v = make_uint2(pack_f16x2(a, b), pack_f16x2(c, d));
+    *reinterpret_cast<uint2*>(dst) = v;
+  }
+}
+
+template <int CDT> struct ElemBytes;
+template <> struct ElemBytes<0> { static constexpr int value = 4; };
+template <> struct ElemBytes<1> { static constexpr int value = 2; };
+template <> struct ElemBytes<2> { static constexpr int value = 2; };
+
+}  // namespace moe

@@ -1,0 +1,63 @@
+// Internal kernel launchers (host side).  Each returns hipGetLastError()
+// after enqueueing; arguments are validated by the C ABI layer beforehand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* gating, int64_t T, int E, int topk, int G,
+                        int topk_group, int scoring, int renormalize, float scale,
+                        float* out_w, int32_t* out_ids, hipStream_t stream);
+
+hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
+                        int64_t max_padded, hipStream_t stream);
+
+struct MoeGemmArgs {
+  const void* A;
+  int a_dtype;            // 0 f32, 1 bf16
+  int64_t lda;
+  int a_rows;             // 0 pair, 1 sorted
+  int a_row_div;
+  const void* B;          // [E, N, K] bf16
+  int E;
+  int64_t N, K;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* total;
+  int64_t max_padded;
+  int block_m;
+  int64_t num_valid;
+  const float* topk_weights;
+  int epilogue;           // 0 none, 1 silu_mul
+  void* C;
+  int c_dtype;            // 0 f32, 1 bf16, 2 f16
+  int64_t ldc;
+  int c_rows;             // 0 pair, 1 sorted
+};
+
+// MFMA tile kernel, block_m 64 or 128.
+hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream);
+// Weight-streaming kernel, block_m 16 or 32.
+hipError_t launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t stream);
+
+// out[t, :] = sum_k y[t * topk + k, :]   (fixed order k = 0 .. topk-1)
+hipError_t launch_topk_reduce(const float* y, int64_t T, int topk, int64_t H,
+                              void* out, int out_dtype, hipStream_t stream);
+
+struct GmmI8Args {
+  const int8_t* X;
+  const int8_t* W;
+  const float* sx;
+  const float* sw;
+  const int32_t* offsets;
+  void* Y;
+  int64_t M, K, N;
+  int E;
+};
+
+hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream);
+
+}  // namespace moe

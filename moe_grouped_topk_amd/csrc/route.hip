@@ -1,0 +1,150 @@
+// Routing kernel: GroupedTopK / plain top-k with softmax or sigmoid scores.
+//
+// Semantics: "GroupedTopK operator optimisation primer", sections 三 3.1-3.6
+// (scores, group max, top groups, mask, top-k, renormalise and scale); plain
+// top-k (mini-sglang "MoE and fused MoE", select_experts) is one group.
+//
+// Design: one 64-lane wavefront per token, everything in registers.  Lane l
+// holds experts [l*V, l*V + V).  Selection works on order-preserving integer
+// keys of the LOGITS: both scorings are monotone, so the order of the logits
+// is the order of the exact scores (the primer's section 七 shortcut), and
+// no rounding of exp() can merge or swap two candidates.  A candidate is the
+// 64-bit value (key << 32) | (0xffffffff - index): its maximum is the largest
+// logit with the lowest index among equals.  Each top-k round is a lane-local
+// max over V values plus a 6-step xor-shuffle max across the wave.
+// Weights (softmax + renormalise) are a softmax over the k selected logits
+// alone, since the full-row denominator cancels (section 七); the other
+// variants keep the full denominator or use the sigmoid scores.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+template <int V>
+__global__ void __launch_bounds__(256)
+route_kernel(const float* __restrict__ gating, int64_t T, int E, int topk,
+             int G, int topk_group, int scoring, int renormalize, float scale,
+             float* __restrict__ out_w, int32_t* __restrict__ out_ids) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (t >= T) return;
+  const float* row = gating + t * (int64_t)E;
+
+  float x[V];
+  uint64_t cand[V];
+  const int e0 = lane * V;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = e0 + j;
+    x[j] = (e < E) ? row[e] : 0.0f;
+    cand[j] = (e < E) ? (((uint64_t)float_key(x[j]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e))
+                      : 0ull;
+  }
+
+  // Group stage ([GTK] 3.2-3.4): group score = max logit of the group; keep
+  // the topk_group best groups (ties -> lower group), mask the others.
+  if (G > 1) {
+    const int P = E / G;
+    uint64_t gcand = 0ull;   // lane g < G holds group g's candidate
+    for (int g = 0; g < G; ++g) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int e = e0 + j;
+        if (e < E && e / P == g) {
+          const uint32_t k = (uint32_t)(cand[j] >> 32);
+          m = k > m ? k : m;
+        }
+      }
+      m = wave_max_u32(m);
+      if (lane == g) gcand = ((uint64_t)m << 32) | (uint64_t)(0xffffffffu - (uint32_t)g);
+    }
+    uint64_t kept = 0ull;    // bit g set: group g kept
+    for (int r = 0; r < topk_group; ++r) {
+      const uint64_t best = wave_max_u64(gcand);
+      const int g = (int)(0xffffffffu - (uint32_t)best);
+      kept |= 1ull << g;
+      if (lane == g) gcand = 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int e = e0 + j;
+      if (e < E && !((kept >> (e / P)) & 1ull)) cand[j] = 0ull;
+    }
+  }
+
+  // Top-k rounds ([GTK] 3.5, 八): lane r keeps the r-th pick.
+  int my_id = 0;
+  float my_x = 0.0f;
+  float top_x = 0.0f;
+  for (int r = 0; r < topk; ++r) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < V; ++j) best = cand[j] > best ? cand[j] : best;
+    best = wave_max_u64(best);
+    const int id = (int)(0xffffffffu - (uint32_t)best);
+    const float xv = key_float((uint32_t)(best >> 32));
+    if (r == 0) top_x = xv;
+    if (lane == r) { my_id = id; my_x = xv; }
+    if (id >= e0 && id < e0 + V) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (e0 + j == id) cand[j] = 0ull;
+    }
+  }
+
+  // Weights ([GTK] 3.1 and 3.6).
+  float w;
+  const bool mine = lane < topk;
+  if (scoring == 0) {
+    // top_x is the row maximum: the best group holds the best expert.
+    const float ek = mine ? expf(my_x - top_x) : 0.0f;
+    float den;
+    if (renormalize) {
+      den = wave_sum_f32(ek);
+    } else {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (e0 + j < E) s += expf(x[j] - top_x);
+      den = wave_sum_f32(s);
+    }
+    w = ek / den;
+  } else {
+    const float sk = mine ? 1.0f / (1.0f + expf(-my_x)) : 0.0f;
+    if (renormalize) {
+      const float den = wave_sum_f32(sk);
+      w = sk / den;
+    } else {
+      w = sk;
+    }
+  }
+  w *= scale;
+  if (mine) {
+    out_w[t * topk + lane] = w;
+    out_ids[t * topk + lane] = my_id;
+  }
+}
+
+hipError_t launch_route(const float* gating, int64_t T, int E, int topk, int G,
+                        int topk_group, int scoring, int renormalize, float scale,
+                        float* out_w, int32_t* out_ids, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int waves_per_block = 4;
+  const dim3 block(kWave * waves_per_block);
+  const dim3 grid((unsigned)((T + waves_per_block - 1) / waves_per_block));
+  const int per_lane = (E + kWave - 1) / kWave;
+#define MOE_ROUTE_CASE(VV)                                                          \
+  hipLaunchKernelGGL(route_kernel<VV>, grid, block, 0, stream, gating, T, E, topk, \
+                     G, topk_group, scoring, renormalize, scale, out_w, out_ids)
+  if (per_lane <= 1) MOE_ROUTE_CASE(1);
+  else if (per_lane <= 2) MOE_ROUTE_CASE(2);
+  else if (per_lane <= 4) MOE_ROUTE_CASE(4);
+  else if (per_lane <= 8) MOE_ROUTE_CASE(8);
+  else MOE_ROUTE_CASE(16);
+#undef MOE_ROUTE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace moe

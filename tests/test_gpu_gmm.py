@@ -1,0 +1,82 @@
+"""GPU parity of gmm_int8 against the oracle's dequantised result (exact
+integer sums times both scales).  Bar: max-abs-rel 3e-2 (the fp16 output
+rounding alone is ~5e-4)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import gmm_inputs, require_gpu
+from parity import BAR_INT8, max_abs_rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def moe(dev):
+    import moe_grouped_topk_amd as m
+    return m
+
+
+def _run_and_check(moe, dev, M, K, N, E, sizes, seed, bar=BAR_INT8):
+    h, d = gmm_inputs(M, K, N, E, sizes, seed, dev)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    moe.gmm_int8(d["xq"], d["wq"], d["sx"], d["sw"], d["off"], output=Y)
+    torch.cuda.synchronize()
+    got = Y.float().cpu().numpy()
+    ref = oracle.gmm_int8(h["xq"], h["wq"], h["sx"], h["sw"], h["off"])
+    assert np.isfinite(got).all()
+    err = max_abs_rel(got, ref)
+    assert err <= bar, err
+    return got, ref, h, err
+
+
+def test_int8_workload_zipf(moe, dev):
+    cfg = synth.CONFIGS["int8gmm"]
+    sizes = synth.zipf_group_sizes(cfg.T, cfg.E, cfg.extra["zipf_s"], cfg.cid, 9)
+    assert (sizes == 0).any() and (sizes == 1).any()
+    got, ref, h, err = _run_and_check(moe, dev, cfg.T, cfg.H, cfg.I, cfg.E, sizes, cfg.cid)
+    print("int8 gmm workload err=%.3e" % err)
+
+
+@pytest.mark.parametrize("sizes", [
+    [0, 0, 5, 0, 123, 1, 0],          # empty first/last experts, single row
+    [300],                            # one expert, several full tiles + tail
+    [1] * 9,                          # one row each
+    [128, 128, 0, 256],               # exact tile multiples
+    [0, 0, 0, 1]])
+def test_int8_edge_groups(moe, dev, sizes):
+    E = len(sizes)
+    _run_and_check(moe, dev, int(np.sum(sizes)), 256, 192, E, sizes, 50 + E)
+
+
+def test_int8_small_dims(moe, dev):
+    _run_and_check(moe, dev, 40, 16, 16, 3, [10, 20, 10], 61)
+    _run_and_check(moe, dev, 70, 144, 48, 2, [33, 37], 62)      # K tail, N < 128
+
+
+def test_int8_empty(moe, dev):
+    h, d = gmm_inputs(0, 64, 32, 2, [0, 0], 63, dev)
+    Y = moe.gmm_int8(d["xq"], d["wq"], d["sx"], d["sw"], d["off"])
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 32)
+
+
+def test_int8_quantisation_error_informational(moe, dev):
+    """Not gated beyond the bar: error of the int8 GMM against the float32
+    GEMM of the unquantised operands, as the article's quality check does."""
+    sizes = [40, 0, 88]
+    got, ref, h, _ = _run_and_check(moe, dev, 128, 512, 256, 3, sizes, 64)
+    fp = oracle.gmm(h["x"].astype(np.float64),
+                    np.stack([h["w_f32"][e] for e in range(3)]).astype(np.float64), h["off"])
+    rel = max_abs_rel(got, fp)
+    cos = float((got * fp).sum() / np.sqrt((got * got).sum() * (fp * fp).sum()))
+    print("int8 vs fp32 GEMM: max-abs-rel %.3e cosine %.6f" % (rel, cos))
+    assert cos > 0.99

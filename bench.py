@@ -1,0 +1,342 @@
+"""Benchmark of the fused-MoE forward path on one MI355X.
+
+A step is one moe_forward of the prefill-shaped layer (T=4096, H=2048,
+I=768, E=128, top-8 softmax with renormalisation): routing, alignment, the
+gate_up GEMM with SiLU*up, the down GEMM with the routing weight and the
+top-k reduce, on seeded synthetic inputs already resident in HBM.  The
+headline value is that step's throughput in TFLOP/s (6*T*topk*H*I
+algorithmic FLOPs, padding excluded).  The same run measures the
+decode-shaped layers (HBM GB/s over the touched experts' weights), the int8
+grouped GEMM, the routing workload and the tiny layer, and times the oracle
+on a bounded sample of the prefill workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
+PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def bf16_from_host(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Timer:
+    """HIP-event timing on torch's current stream (the binding's stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, reps):
+        t = self.torch
+        start = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
+        end = [t.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            start[i].record()
+            fn()
+            end[i].record()
+        t.cuda.synchronize()
+        ms = [s.elapsed_time(e) for s, e in zip(start, end)]
+        return float(np.mean(ms)), float(np.median(ms))
+
+
+def wall_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def layer_inputs(torch, cfg, dev):
+    import synth
+    sub = cfg.extra.get("sub", 0)
+    x = synth.normal_f32((cfg.T, cfg.H), cfg.cid, 0, sub)
+    g = synth.normal_f32((cfg.T, cfg.E), cfg.cid, 1, sub)
+    x_dev = (torch.from_numpy(x).to(dev) if cfg.x_dtype == "f32"
+             else bf16_from_host(torch, synth.f32_to_bf16_bits(x), dev))
+    w1 = synth.device_normal_bf16((cfg.E, 2 * cfg.I, cfg.H), cfg.cid * 1000 + 2, cfg.w_std, dev)
+    w2 = synth.device_normal_bf16((cfg.E, cfg.H, cfg.I), cfg.cid * 1000 + 3, cfg.w_std, dev)
+    return x_dev, torch.from_numpy(g).to(dev), w1, w2, x, g
+
+
+def bench_prefill(torch, moe, dev, steps, warmup, timer):
+    import synth
+    cfg = synth.CONFIGS["prefill"]
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
+    x, g, w1, w2, x_host, g_host = layer_inputs(torch, cfg, dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+
+    def step():
+        moe.moe_forward(x, g, w1, w2, K, out=out, workspace=ws)
+
+    ms = wall_steps(torch, step, steps, warmup)
+    flops = 6.0 * T * K * H * I
+    res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops)
+
+    # Per-kernel breakdown: the same five launches moe_forward makes, each
+    # timed with HIP events on the stream they run on.
+    P = T * K
+    bm = 128
+    w_t, ids_t = moe.moe_route(g, K)
+    sorted_ids, eids, total = moe.moe_align_block_size(ids_t, E, bm)
+    cap = sorted_ids.numel()
+    h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((P, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    reps = max(steps, 10)
+    parts = {
+        "route": lambda: moe.moe_route(g, K, topk_weights=w_t, topk_ids=ids_t),
+        "align": lambda: moe.moe_align_block_size(ids_t, E, bm, sorted_ids, eids, total),
+        "gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
+            x, w1, sorted_ids, eids, total, bm, P, a_rows="pair", a_row_div=K,
+            epilogue="silu_mul", C=h, c_rows="sorted"),
+        "gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
+            h, w2, sorted_ids, eids, total, bm, P, a_rows="sorted", topk_weights=w_t,
+            C=y, c_rows="pair"),
+    }
+    br = {}
+    for name, fn in parts.items():
+        for _ in range(3):
+            fn()
+        mean, med = timer.run(fn, reps)
+        br[name] = dict(mean_ms=mean, median_ms=med)
+    # top-k reduce: run through moe_forward's own path is not separable from
+    # Python, so it is the step minus the other four (reported as such).
+    gemm1_flops = 2.0 * P * H * 2 * I
+    gemm2_flops = 2.0 * P * I * H
+    br["gemm1_gate_up_silu"]["tflops"] = gemm1_flops / br["gemm1_gate_up_silu"]["mean_ms"] * 1e-9
+    br["gemm2_down_weighted"]["tflops"] = gemm2_flops / br["gemm2_down_weighted"]["mean_ms"] * 1e-9
+    br["remainder_reduce_and_gaps_ms"] = ms - sum(
+        br[k]["mean_ms"] for k in ("route", "align", "gemm1_gate_up_silu", "gemm2_down_weighted"))
+    res["breakdown"] = br
+    res["gemm1_flops"] = gemm1_flops
+    res["inputs"] = (x_host, g_host, w1, w2)
+    return res
+
+
+def touched_experts(ids):
+    return int(np.unique(ids.reshape(-1)).size)
+
+
+def bench_decode(torch, moe, dev, name, steps, warmup, timer):
+    import synth
+    cfg = synth.CONFIGS[name]
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
+    x, g, w1, w2, _, _ = layer_inputs(torch, cfg, dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+
+    def step():
+        moe.moe_forward(x, g, w1, w2, K, cfg.groups, cfg.topk_group, "softmax", True, cfg.scale,
+                        out=out, topk_ids_out=ids, workspace=ws)
+
+    ms = wall_steps(torch, step, steps, warmup)
+    n_exp = touched_experts(ids.cpu().numpy())
+    per_expert = (2 * I * H + H * I) * 2
+    nbytes = n_exp * per_expert + 2 * T * H * 2
+    mean, med = timer.run(step, max(steps, 10))
+    del w1, w2
+    torch.cuda.empty_cache()
+    return dict(ms=ms, event_mean_ms=mean, touched_experts=n_exp, bytes=nbytes,
+                gbs=nbytes / ms * 1e-6, frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
+                flops=6.0 * T * K * H * I)
+
+
+def bench_int8(torch, moe, dev, steps, warmup, timer):
+    import synth
+    cfg = synth.CONFIGS["int8gmm"]
+    M, K, N, E = cfg.T, cfg.H, cfg.I, cfg.E
+    sizes = synth.zipf_group_sizes(M, E, cfg.extra["zipf_s"], cfg.cid, 9)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    xq, sx = synth.symmetric_int8_rows(synth.normal_f32((M, K), cfg.cid, 0))
+    # weights: drawing 537M values on the host is slow; draw N(0, 0.02) on
+    # the device and quantise per output channel there (input preparation).
+    wf = synth.device_normal_f32((E, N, K), cfg.cid * 1000 + 1, cfg.w_std, dev)
+    amax = wf.abs().amax(dim=2, keepdim=True)
+    sw = torch.where(amax == 0, torch.ones_like(amax), amax / 127.0)
+    wq = torch.clamp(torch.round(wf / sw), -127, 127).to(torch.int8)
+    sw = sw.squeeze(2).contiguous()
+    del wf, amax
+    xq_d = torch.from_numpy(xq).to(dev)
+    sx_d = torch.from_numpy(sx).to(dev)
+    off_d = torch.from_numpy(off).to(dev)
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+    def step():
+        moe.gmm_int8(xq_d, wq, sx_d, sw, off_d, output=Y)
+
+    ms = wall_steps(torch, step, steps, warmup)
+    mean, med = timer.run(step, max(steps, 10))
+    nz = int((sizes > 0).sum())
+    nbytes = nz * N * K + M * K + 2 * M * N + 4 * (E * N + M)
+    ops = 2.0 * M * N * K
+    del wq
+    torch.cuda.empty_cache()
+    return dict(ms=ms, event_mean_ms=mean, tops=ops / ms * 1e-9, gbs=nbytes / ms * 1e-6,
+                frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
+                frac_int8=ops / ms * 1e-9 / PEAK_INT8_TOPS, bytes=nbytes, ops=ops,
+                group_sizes_min_max=[int(sizes.min()), int(sizes.max())])
+
+
+def bench_routing(torch, moe, dev, steps, warmup, timer):
+    import synth
+    cfg = synth.CONFIGS["routing"]
+    g = torch.from_numpy(synth.normal_f32((cfg.T, cfg.E), cfg.cid, 0)).to(dev)
+    w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=dev)
+    ids = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=dev)
+
+    def step():
+        moe.moe_route(g, cfg.topk, cfg.groups, cfg.topk_group, "softmax", True, 1.0, w, ids)
+
+    ms = wall_steps(torch, step, steps * 10, warmup)
+    mean, med = timer.run(step, 100)
+    return dict(ms_wall=ms, event_median_us=med * 1e3, event_mean_us=mean * 1e3,
+                input_bytes=cfg.T * cfg.E * 4)
+
+
+def bench_tiny(torch, moe, dev, steps, warmup, timer):
+    import synth
+    cfg = synth.CONFIGS["tiny"]
+    x = torch.from_numpy(synth.normal_f32((cfg.T, cfg.H), cfg.cid, 0)).to(dev)
+    g = torch.from_numpy(synth.normal_f32((cfg.T, cfg.E), cfg.cid, 1)).to(dev)
+    w1 = bf16_from_host(torch, synth.f32_to_bf16_bits(
+        synth.normal_f32((cfg.E, 2 * cfg.I, cfg.H), cfg.cid, 2, 0, cfg.w_std)), dev)
+    w2 = bf16_from_host(torch, synth.f32_to_bf16_bits(
+        synth.normal_f32((cfg.E, cfg.H, cfg.I), cfg.cid, 3, 0, cfg.w_std)), dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+
+    def step():
+        moe.moe_forward(x, g, w1, w2, cfg.topk, out=out, workspace=ws)
+
+    ms = wall_steps(torch, step, steps * 10, warmup)
+    mean, med = timer.run(step, 100)
+    return dict(ms_wall=ms, event_median_us=med * 1e3)
+
+
+def cpu_baseline(torch, prefill_inputs, target_s=15.0):
+    """The oracle, as it stands, on the first S tokens of the prefill batch.
+    Weights are decoded from bf16 to float64 before the timed region."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    cfg = synth.CONFIGS["prefill"]
+    x_host, g_host, w1, w2 = prefill_inputs
+    xb = oracle.bf16_bits_to_f64(synth.f32_to_bf16_bits(x_host))
+    w1h = oracle.bf16_bits_to_f64(w1.view(torch.int16).cpu().numpy().view(np.uint16))
+    w2h = oracle.bf16_bits_to_f64(w2.view(torch.int16).cpu().numpy().view(np.uint16))
+    g64 = g_host.astype(np.float64)
+    S = 64
+    while True:
+        t0 = time.perf_counter()
+        w, ids = oracle.grouped_topk(g64[:S], cfg.topk)
+        oracle.moe_layer_expert_loop(xb[:S], w1h, w2h, w, ids)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or S >= cfg.T:
+            break
+        S = min(cfg.T, int(S * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+    flops = 6.0 * S * cfg.topk * cfg.H * cfg.I
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return dict(value=flops / dt * 1e-12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                seconds=dt,
+                sample="first %d of %d tokens of the prefill layer (route + expert-loop layer, "
+                       "float64 NumPy; weights pre-decoded)" % (S, cfg.T))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="prefill headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(collectives are out of scope); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_topk_amd as moe
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+
+    log("prefill layer")
+    pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer)
+    g1 = pre["breakdown"]["gemm1_gate_up_silu"]
+    roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=g1["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                    kernel="moe_gemm_tile_kernel<128,SILU> (gate_up GEMM)",
+                    flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
+    components = {"prefill_breakdown": pre["breakdown"]}
+    if not args.quick:
+        for name in ("decode16", "decode64"):
+            log(name)
+            components[name] = bench_decode(torch, moe, dev, name, args.steps, args.warmup, timer)
+        log("int8 gmm")
+        components["int8gmm"] = bench_int8(torch, moe, dev, args.steps, args.warmup, timer)
+        log("routing")
+        components["routing"] = bench_routing(torch, moe, dev, args.steps, args.warmup, timer)
+        log("tiny")
+        components["tiny"] = bench_tiny(torch, moe, dev, args.steps, args.warmup, timer)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(torch, pre["inputs"])
+
+    line = {
+        "metric": "fused-MoE layer TFLOP/s (prefill) + decode HBM GB/s at 1 GPU, "
+                  "as % of MI355X roofline",
+        "value": round(pre["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill-shaped MoE layer forward", "T": 4096, "H": 2048,
+                   "I": 768, "E": 128, "topk": 8, "routing": "softmax top-8, renormalize",
+                   "frac_of_bf16_peak": round(pre["tflops"] / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": components,
+    }
+    if "decode16" in components:
+        line["decode_gbs"] = {k: round(components[k]["gbs"], 1) for k in ("decode16", "decode64")}
+        line["decode_frac_hbm"] = {k: round(components[k]["frac_hbm"], 4)
+                                   for k in ("decode16", "decode64")}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -126,6 +126,8 @@ MOE_API int moe_route(const float* gating, int64_t T, int32_t E, int32_t topk,
  *   num_tokens_post_padded [1] int32 out: total (a multiple of block_m).
  *   max_padded             capacity of sorted_token_ids; must be at least
  *                          moe_align_max_padded(num_pairs, E, block_m).
+ * Null pointers are accepted only for buffers of capacity 0 (and topk_ids
+ * when num_pairs = 0); num_tokens_post_padded is always written.
  * Errors: NULLs, num_pairs < 0 or >= 2^31, E outside [1, MOE_MAX_EXPERTS],
  * block_m outside [1, 1024], max_padded too small.  Expert ids outside
  * [0, E) are outside the contract (they are dropped, not written).

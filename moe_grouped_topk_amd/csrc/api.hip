@@ -40,7 +40,8 @@ int64_t align_max_padded(int64_t P, int32_t E, int32_t B) {
 }
 
 int check_gemm(const moe::MoeGemmArgs& a) {
-  if (!a.A || !a.B || !a.C || !a.sorted_ids || !a.expert_ids || !a.total) return MOE_ERR_NULL;
+  if (!a.B || !a.total) return MOE_ERR_NULL;
+  if (a.max_padded > 0 && (!a.A || !a.C || !a.sorted_ids || !a.expert_ids)) return MOE_ERR_NULL;
   if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (a.c_dtype != MOE_DTYPE_F32 && a.c_dtype != MOE_DTYPE_BF16 && a.c_dtype != MOE_DTYPE_F16)
     return MOE_ERR_DTYPE;
@@ -56,7 +57,8 @@ int check_gemm(const moe::MoeGemmArgs& a) {
   if (a.ldc < nout || a.ldc % 8 != 0) return MOE_ERR_SHAPE;
   if (a.num_valid < 0 || a.num_valid >= INT32_MAX) return MOE_ERR_SHAPE;
   if (a.max_padded < 0 || a.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
-  if (!aligned16(a.A) || !aligned16(a.B) || !aligned16(a.C)) return MOE_ERR_SHAPE;
+  if (a.max_padded > 0 && (!aligned16(a.A) || !aligned16(a.B) || !aligned16(a.C)))
+    return MOE_ERR_SHAPE;
   // grid sizes stay inside 32-bit workgroup counts
   const int64_t ntile = (nout + 63) / 64 + 1;
   if ((a.max_padded / a.block_m) * ntile >= INT32_MAX) return MOE_ERR_SHAPE;
@@ -140,8 +142,11 @@ int64_t moe_align_max_padded(int64_t num_pairs, int32_t E, int32_t block_m) {
 int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, int32_t block_m,
                          int32_t* sorted_token_ids, int32_t* expert_ids,
                          int32_t* num_tokens_post_padded, int64_t max_padded, void* stream) {
-  if (!sorted_token_ids || !expert_ids || !num_tokens_post_padded) return MOE_ERR_NULL;
+  if (!num_tokens_post_padded) return MOE_ERR_NULL;
   if (num_pairs > 0 && !topk_ids) return MOE_ERR_NULL;
+  // empty buffers (capacity 0) may come with null pointers
+  if (max_padded > 0 && !sorted_token_ids) return MOE_ERR_NULL;
+  if (block_m > 0 && max_padded / block_m > 0 && !expert_ids) return MOE_ERR_NULL;
   if (num_pairs < 0 || num_pairs >= INT32_MAX) return MOE_ERR_SHAPE;
   if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
   if (block_m < 1 || block_m > 1024) return MOE_ERR_CONFIG;

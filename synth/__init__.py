@@ -12,9 +12,11 @@ round-to-nearest-even from float32 and handled as raw 16-bit patterns.
 """
 
 from .inputs import (host_rng, normal_f32, f32_to_bf16_bits, bf16_bits_to_f32,
-                     zipf_group_sizes, symmetric_int8_rows, device_normal_bf16)
+                     zipf_group_sizes, symmetric_int8_rows, device_normal_bf16,
+                     device_normal_f32)
 from .configs import CONFIGS, Config
 
 __all__ = ["host_rng", "normal_f32", "f32_to_bf16_bits", "bf16_bits_to_f32",
            "zipf_group_sizes", "symmetric_int8_rows", "device_normal_bf16",
+           "device_normal_f32",
            "CONFIGS", "Config"]

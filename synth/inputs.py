@@ -91,3 +91,14 @@ def device_normal_bf16(shape, seed, std, device):
         tmp.mul_(std)
         flat_t[start:start + m].copy_(tmp)
     return out
+
+
+def device_normal_f32(shape, seed, std, device):
+    """float32 tensor of N(0, std^2) drawn on ``device`` with a seeded torch
+    generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+    out.mul_(std)
+    return out

@@ -98,12 +98,12 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer):
     # Per-kernel breakdown: the same five launches moe_forward makes, each
     # timed with HIP events on the stream they run on.
     P = T * K
-    bm = 128
+    bm = moe.moe_forward_block_m(T, E, K)     # the block size moe_forward uses here
     w_t, ids_t = moe.moe_route(g, K)
     sorted_ids, eids, total = moe.moe_align_block_size(ids_t, E, bm)
     cap = sorted_ids.numel()
     h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((P, H), dtype=torch.float32, device=dev)
+    y = torch.empty((P, H), dtype=torch.bfloat16, device=dev)   # y in x's dtype
     torch.cuda.synchronize()
     reps = max(steps, 10)
     parts = {
@@ -132,6 +132,7 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer):
         br[k]["mean_ms"] for k in ("route", "align", "gemm1_gate_up_silu", "gemm2_down_weighted"))
     res["breakdown"] = br
     res["gemm1_flops"] = gemm1_flops
+    res["block_m"] = bm
     res["inputs"] = (x_host, g_host, w1, w2)
     return res
 
@@ -292,7 +293,8 @@ def main():
     g1 = pre["breakdown"]["gemm1_gate_up_silu"]
     roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=g1["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
-                    kernel="moe_gemm_tile_kernel<128,SILU> (gate_up GEMM)",
+                    kernel="moe_gemm_tile_kernel (gate_up GEMM, SiLU*up epilogue)",
+                    block_m=pre["block_m"],
                     flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
     components = {"prefill_breakdown": pre["breakdown"]}
     if not args.quick:

@@ -163,7 +163,7 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
  *            capacity of sorted_token_ids (the launch is sized by it and the
  *            device total cuts it short).
  *   block_m  16 or 32 (weight-streaming kernel for few rows per expert) or
- *            64 or 128 (MFMA tile kernel).
+ *            64, 128 or 256 (MFMA tile kernel; 256 needs bf16 A).
  * Requirements: K % 8 == 0, N % 16 == 0 (SILU_MUL: (N/2) % 16 == 0),
  * lda >= K and ldc >= output width, both multiples of 8; A, B and C
  * 16-byte aligned.
@@ -190,12 +190,17 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
  *   w2       [E, H, I] bf16.
  *   topk_weights_out [T, topk] f32, topk_ids_out [T, topk] int32: optional
  *            (NULL = kept in the workspace only).
- *   block_m  0 = chosen from the shape (few pairs per expert -> 16, else 128);
+ *   block_m  0 = chosen from the average pairs per expert (16, 32, 64, 128,
+ *            or 256 for bf16 x with at least 192 pairs per expert);
  *            otherwise one of the moe_grouped_gemm block sizes.
  *   ws       device workspace of at least moe_forward_workspace_size(...)
  *            bytes for the same arguments (256-byte aligned).
  * Requirements: H % 16 == 0, I % 16 == 0, plus moe_route's.
  */
+/* Block size moe_forward uses when called with block_m = 0 (the choice is a
+ * pure function of the shape and x's dtype); -1 on invalid arguments. */
+MOE_API int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype);
+
 MOE_API size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
                                   int32_t topk, int32_t block_m);
 

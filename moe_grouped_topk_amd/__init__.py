@@ -15,7 +15,7 @@ import os
 __all__ = [
     "MoeError", "LIB_PATH", "lib", "moe_status_string", "moe_route",
     "moe_align_max_padded", "moe_align_block_size", "moe_grouped_gemm",
-    "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
+    "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -52,6 +52,8 @@ def _load():
     L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i64, i64, vp, vp, vp, i64,
                                    i32, i64, vp, i32, vp, i32, i64, i32, vp]
     L.moe_grouped_gemm.restype = ctypes.c_int
+    L.moe_forward_block_m.argtypes = [i64, i32, i32, i32]
+    L.moe_forward_block_m.restype = i32
     L.moe_forward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     L.moe_forward_workspace_size.restype = sz
     L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32,
@@ -180,6 +182,11 @@ def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded,
         _ptr(topk_weights, torch.float32, "topk_weights"), EPILOGUE[epilogue],
         _ptr(C, None, "C"), _dtype_code(C), C.shape[-1], ROWS[c_rows], _stream(stream)))
     return C
+
+
+def moe_forward_block_m(T, E, topk, x_dtype="bf16"):
+    """Block size moe_forward picks for block_m=0."""
+    return int(lib.moe_forward_block_m(T, E, topk, DTYPE[x_dtype]))
 
 
 def moe_forward_workspace_size(T, H, I, E, topk, block_m=0):

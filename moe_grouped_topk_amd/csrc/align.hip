@@ -6,7 +6,8 @@
 //
 // Design: a single 1024-thread workgroup (16 waves); totals never leave the
 // device.  Wave w owns a contiguous chunk of the pairs.
-//   pass 1: per-wave histograms counts[w][e] in LDS (LDS atomics);
+//   pass 1: per-wave histograms counts[w][e] in LDS (LDS atomics), the ids
+//           read in batches so many loads are in flight at once;
 //   scan:   per expert, exclusive prefix over waves (so wave w knows where its
 //           pairs of expert e start inside the segment), padded sizes, and an
 //           exclusive scan over experts for the segment starts;
@@ -26,6 +27,7 @@ namespace moe {
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
+constexpr int kBatch = 16;   // ids per lane read together
 
 __global__ void __launch_bounds__(kAlignThreads)
 align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
@@ -34,7 +36,7 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   extern __shared__ int smem[];
   int* counts = smem;                          // [kAlignWaves][E]
   int* seg_start = smem + kAlignWaves * E;     // [E + 1]
-  int* scan_tmp = seg_start + (E + 1);         // [kAlignThreads]
+  int* scan_tmp = seg_start + (E + 1);         // [2 * kAlignWaves]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -47,10 +49,19 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   const int c0 = wave * chunk;
   const int c1 = min(P, c0 + chunk);
 
+  // The wave's chunk is read in batches of kBatch ids per lane, all loads of
+  // a batch in flight together (the loop is latency-bound otherwise).
   // pass 1: histogram of this wave's chunk
-  for (int i = c0 + lane; i < c1; i += kWave) {
-    const int e = topk_ids[i];
-    if (e >= 0 && e < E) atomicAdd(&counts[wave * E + e], 1);
+  for (int base = c0; base < c1; base += kWave * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kWave + lane;
+      ids[j] = i < c1 ? topk_ids[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (ids[j] >= 0 && ids[j] < E) atomicAdd(&counts[wave * E + ids[j]], 1);
   }
   __syncthreads();
 
@@ -66,19 +77,31 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   }
   __syncthreads();
 
-  // exclusive scan of padded sizes over experts (E <= 1024 = one per thread)
+  // exclusive scan of padded sizes over experts (E <= 1024 = one per thread):
+  // inclusive scan inside each wave by shuffles, then over the wave totals.
   {
-    int v = (tid < E) ? seg_start[tid] : 0;
-    scan_tmp[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kAlignThreads; off <<= 1) {
-      const int add = (tid >= off) ? scan_tmp[tid - off] : 0;
-      __syncthreads();
-      scan_tmp[tid] += add;
-      __syncthreads();
+    const int v = (tid < E) ? seg_start[tid] : 0;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
     }
-    if (tid < E) seg_start[tid] = scan_tmp[tid] - v;   // exclusive
-    if (tid == kAlignThreads - 1) seg_start[E] = scan_tmp[tid];
+    if (lane == kWave - 1) scan_tmp[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int w = lane < kAlignWaves ? scan_tmp[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kAlignWaves; off <<= 1) {
+        const int y = __shfl_up(w, off, kWave);
+        if (lane >= off) w += y;
+      }
+      if (lane < kAlignWaves) scan_tmp[kAlignWaves + lane] = w;   // inclusive wave totals
+    }
+    __syncthreads();
+    const int before = wave ? scan_tmp[kAlignWaves + wave - 1] : 0;
+    if (tid < E) seg_start[tid] = before + x - v;   // exclusive
+    if (tid == 0) seg_start[E] = scan_tmp[2 * kAlignWaves - 1];
   }
   __syncthreads();
   const int total = seg_start[E];
@@ -87,23 +110,31 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = c0; base < c1; base += kWave) {
-    const int i = base + lane;
-    const bool valid = i < c1;
-    const int e = valid ? topk_ids[i] : -1;
-    const bool ok = valid && e >= 0 && e < E;
-    uint64_t match = __ballot(ok);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = ok && ((e >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      match &= bit ? m : ~m;
+  for (int base = c0; base < c1; base += kWave * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kWave + lane;
+      ids[j] = i < c1 ? topk_ids[i] : -1;
     }
-    if (ok) {
-      const int rank = __popcll(match & lt_mask);
-      const int cur = counts[wave * E + e];
-      sorted_ids[seg_start[e] + cur + rank] = i;
-      // the highest lane of the group advances the cursor
-      if ((match >> lane) == 1ull) counts[wave * E + e] = cur + __popcll(match);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kWave + lane;
+      const int e = ids[j];
+      const bool ok = e >= 0 && e < E;
+      uint64_t match = __ballot(ok);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = ok && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      if (ok) {
+        const int rank = __popcll(match & lt_mask);
+        const int cur = counts[wave * E + e];
+        sorted_ids[seg_start[e] + cur + rank] = i;
+        // the highest lane of the group advances the cursor
+        if ((match >> lane) == 1ull) counts[wave * E + e] = cur + __popcll(match);
+      }
     }
   }
 
@@ -124,7 +155,7 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
                         int64_t max_padded, hipStream_t stream) {
-  const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E + (E + 1) + kAlignThreads);
+  const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E + (E + 1) + 2 * kAlignWaves);
   if (lds > 65536) {
     const hipError_t st = hipFuncSetAttribute(
         (const void*)align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -31,7 +31,7 @@ int check_route_shape(int64_t T, int32_t E, int32_t topk, int32_t G, int32_t Kg,
   return MOE_OK;
 }
 
-bool valid_block_m(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+bool valid_block_m(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
 
 int64_t align_max_padded(int64_t P, int32_t E, int32_t B) {
   const int64_t nonempty = P < E ? P : E;
@@ -49,6 +49,7 @@ int check_gemm(const moe::MoeGemmArgs& a) {
   if (a.a_rows != MOE_ROWS_PAIR && a.a_rows != MOE_ROWS_SORTED) return MOE_ERR_CONFIG;
   if (a.c_rows != MOE_ROWS_PAIR && a.c_rows != MOE_ROWS_SORTED) return MOE_ERR_CONFIG;
   if (!valid_block_m(a.block_m)) return MOE_ERR_CONFIG;
+  if (a.block_m == 256 && a.a_dtype == MOE_DTYPE_F32) return MOE_ERR_CONFIG;
   if (a.a_rows == MOE_ROWS_PAIR && a.a_row_div < 1) return MOE_ERR_CONFIG;
   if (a.E < 1 || a.N < 16 || a.K < 8 || a.K % 8 != 0) return MOE_ERR_SHAPE;
   const int64_t nout = a.epilogue == MOE_EPILOGUE_SILU_MUL ? a.N / 2 : a.N;
@@ -72,12 +73,13 @@ int enqueue_gemm(const moe::MoeGemmArgs& a, hipStream_t s) {
   return hip_status(err);
 }
 
-int choose_block_m(int64_t T, int32_t E, int32_t topk) {
+int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype) {
   const double avg = (double)T * topk / (double)E;   // pairs per expert
   if (avg < 8.0) return 16;
   if (avg < 24.0) return 32;
   if (avg < 96.0) return 64;
-  return 128;
+  if (avg < 192.0 || x_dtype == MOE_DTYPE_F32) return 128;
+  return 256;
 }
 
 struct ForwardLayout {
@@ -87,9 +89,9 @@ struct ForwardLayout {
 };
 
 ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
-                             int32_t block_m) {
+                             int32_t block_m, int32_t x_dtype) {
   ForwardLayout L{};
-  L.block_m = block_m ? block_m : choose_block_m(T, E, topk);
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype);
   const int64_t P = T * topk;
   L.max_padded = align_max_padded(P, E, L.block_m);
   size_t off = 0;
@@ -100,7 +102,7 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
-  L.y = take(sizeof(float) * (size_t)P * (size_t)H);
+  L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.bytes = off;
   return L;
 }
@@ -177,11 +179,20 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   return enqueue_gemm(a, as_stream(stream));
 }
 
+int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype) {
+  if (T < 0 || E < 1 || topk < 1) return -1;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return -1;
+  return choose_block_m(T, E, topk, x_dtype);
+}
+
 size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                   int32_t block_m) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
   if (block_m != 0 && !valid_block_m(block_m)) return 0;
-  return forward_layout(T, H, I, E, topk, block_m).bytes;
+  // the automatic block size can depend on x's dtype: cover both
+  const size_t a = forward_layout(T, H, I, E, topk, block_m, MOE_DTYPE_BF16).bytes;
+  const size_t b = forward_layout(T, H, I, E, topk, block_m, MOE_DTYPE_F32).bytes;
+  return a > b ? a : b;
 }
 
 int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void* w1, const void* w2,
@@ -198,7 +209,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   if (T == 0) return MOE_OK;
   if (!x || !gating || !w1 || !w2 || !out) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_SHAPE;
-  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m);
+  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype);
   if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
   if (L.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
@@ -210,7 +221,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   int32_t* eids = reinterpret_cast<int32_t*>(base + L.eids);
   int32_t* total = reinterpret_cast<int32_t*>(base + L.total);
   void* h = base + L.h;
-  float* y = reinterpret_cast<float*>(base + L.y);
+  void* y = base + L.y;   // per-pair down-projection rows, in x's dtype
   hipStream_t s = as_stream(stream);
   const int64_t P = T * topk;
 
@@ -233,7 +244,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   moe::MoeGemmArgs g2 = g1;
   g2.A = h; g2.a_dtype = MOE_DTYPE_BF16; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1;
   g2.B = w2; g2.N = H; g2.K = I; g2.topk_weights = w; g2.epilogue = MOE_EPILOGUE_NONE;
-  g2.C = y; g2.c_dtype = MOE_DTYPE_F32; g2.ldc = H; g2.c_rows = MOE_ROWS_PAIR;
+  g2.C = y; g2.c_dtype = x_dtype; g2.ldc = H; g2.c_rows = MOE_ROWS_PAIR;
   st = check_gemm(g2);
   if (st != MOE_OK) return st;
 
@@ -241,7 +252,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   if (st != MOE_OK) return st;
   st = enqueue_gemm(g2, s);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_topk_reduce(y, T, topk, H, out, x_dtype, s));
+  return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }
 
 int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,

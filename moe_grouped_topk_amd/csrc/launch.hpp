@@ -43,8 +43,9 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream);
 // Weight-streaming kernel, block_m 16 or 32.
 hipError_t launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t stream);
 
-// out[t, :] = sum_k y[t * topk + k, :]   (fixed order k = 0 .. topk-1)
-hipError_t launch_topk_reduce(const float* y, int64_t T, int topk, int64_t H,
+// out[t, :] = sum_k y[t * topk + k, :]   (fp32 sum in the order k = 0 .. topk-1)
+// y_dtype / out_dtype: 0 f32, 1 bf16 (out also 2 f16).
+hipError_t launch_topk_reduce(const void* y, int y_dtype, int64_t T, int topk, int64_t H,
                               void* out, int out_dtype, hipStream_t stream);
 
 struct GmmI8Args {

@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunkBytes = 512;    // bf16 bytes of K per chunk (256 elements)
+constexpr int kMaxTopkUnroll = 8;   // y rows loaded together by the reduce
 
 template <int TG, bool TF32>
 struct Regs {
@@ -215,19 +216,42 @@ hipError_t launch_tg(const MoeGemmArgs& a, hipStream_t s) {
   return tf32 ? launch_c<TG, 0, true>(a, s) : launch_c<TG, 0, false>(a, s);
 }
 
-// out[t, :] = sum_k y[t * topk + k, :], summed in the order k = 0 .. topk-1.
-template <int CDT>
-__global__ void __launch_bounds__(256) topk_reduce_kernel(const float* __restrict__ y, int64_t T,
+// out[t, :] = sum_k y[t * topk + k, :], summed in fp32 in the order
+// k = 0 .. topk-1 (YDT: y is f32 (0) or bf16 (1)).
+template <int YDT>
+__device__ __forceinline__ f32x4_t load4(const uint8_t* p) {
+  if constexpr (YDT == 0) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+  }
+}
+
+template <int YDT, int CDT>
+__global__ void __launch_bounds__(256) topk_reduce_kernel(const void* __restrict__ y, int64_t T,
                                                           int topk, int64_t H, void* out) {
+  constexpr int ye = YDT == 0 ? 4 : 2;
   const int64_t q = H / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * q) return;
   const int64_t t = idx / q, c = (idx % q) * 4;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(y) + ((t * topk) * H + c) * ye;
+  f32x4_t v[kMaxTopkUnroll];
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  const float* src = y + (t * topk) * H + c;
-  for (int k = 0; k < topk; ++k) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + (int64_t)k * H);
-    s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+  int k = 0;
+  for (; k + kMaxTopkUnroll <= topk; k += kMaxTopkUnroll) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopkUnroll; ++j) v[j] = load4<YDT>(src + (int64_t)(k + j) * H * ye);
+#pragma unroll
+    for (int j = 0; j < kMaxTopkUnroll; ++j) {
+      s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
+    }
+  }
+  for (; k < topk; ++k) {
+    const f32x4_t w = load4<YDT>(src + (int64_t)k * H * ye);
+    s[0] += w[0]; s[1] += w[1]; s[2] += w[2]; s[3] += w[3];
   }
   store4<CDT>(reinterpret_cast<uint8_t*>(out) + (t * H + c) * ElemBytes<CDT>::value,
               s[0], s[1], s[2], s[3]);
@@ -239,16 +263,23 @@ hipError_t launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t stream) {
   return a.block_m == 16 ? launch_tg<1>(a, stream) : launch_tg<2>(a, stream);
 }
 
-hipError_t launch_topk_reduce(const float* y, int64_t T, int topk, int64_t H, void* out,
-                              int out_dtype, hipStream_t stream) {
+hipError_t launch_topk_reduce(const void* y, int y_dtype, int64_t T, int topk, int64_t H,
+                              void* out, int out_dtype, hipStream_t stream) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  switch (out_dtype) {
-    case 0: hipLaunchKernelGGL(topk_reduce_kernel<0>, grid, block, 0, stream, y, T, topk, H, out); break;
-    case 1: hipLaunchKernelGGL(topk_reduce_kernel<1>, grid, block, 0, stream, y, T, topk, H, out); break;
-    default: hipLaunchKernelGGL(topk_reduce_kernel<2>, grid, block, 0, stream, y, T, topk, H, out); break;
+#define MOE_REDUCE(YD, CD) \
+  hipLaunchKernelGGL((topk_reduce_kernel<YD, CD>), grid, block, 0, stream, y, T, topk, H, out)
+  if (y_dtype == 0) {
+    if (out_dtype == 0) MOE_REDUCE(0, 0);
+    else if (out_dtype == 1) MOE_REDUCE(0, 1);
+    else MOE_REDUCE(0, 2);
+  } else {
+    if (out_dtype == 0) MOE_REDUCE(1, 0);
+    else if (out_dtype == 1) MOE_REDUCE(1, 1);
+    else MOE_REDUCE(1, 2);
   }
+#undef MOE_REDUCE
   return hipGetLastError();
 }
 

@@ -9,25 +9,29 @@
 // per-row and per-channel scales, int32 accumulation per section 5.3).
 //
 // gfx950 design (not the pages' Triton tiling):
-//  * 256 threads = 4 wave64s in a 2 (weight rows) x 2 (token rows) grid.
-//    A tile is 128 weight rows x BM token rows; each wave owns 64 x BM/2.
-//  * Operands are swapped relative to the usual C = A.B^T picture: the
-//    weight rows occupy the 16-row slot of v_mfma_*_16x16x32_bf16 /
-//    v_mfma_i32_16x16x64_i8 and the tokens the 16-column slot.  Each lane
-//    then ends up with 4 consecutive OUTPUT FEATURES of one token, which
-//    gives packed 8/16-byte stores and keeps gate and up (or a scale) in the
-//    same lane for the epilogue.
-//  * K advances 128 bytes per stage (64 bf16 or 128 int8 = 2 MFMA steps).
-//    Global -> registers -> LDS with two LDS stages; the next stage's global
-//    loads are in flight while the current stage's MFMAs run.  LDS rows are
-//    padded to 144 bytes so each group of 8 lanes reading 16 bytes hits 8
-//    distinct bank quads.
+//  * 256 threads = 4 wave64s in a 2 (weight rows) x 2 (tokens) grid.  A tile
+//    is BN weight rows x BM tokens (BN 128/256, BM 64/128/256); a wave owns
+//    BN/2 x BM/2 and computes it with v_mfma_f32_32x32x16_bf16 (or
+//    v_mfma_i32_32x32x32_i8) blocks.  At BN = BM = 256 a wave holds a
+//    128 x 128 fp32 accumulator (256 registers, kept in AGPRs), which halves
+//    the LDS operand traffic per FLOP of a 64 x 64 wave tile.
+//  * Operands are swapped relative to the usual C = A.B^T picture: weight
+//    rows sit in the MFMA's row slot and tokens in its column slot, so each
+//    lane ends up with runs of 4 consecutive OUTPUT FEATURES of one token:
+//    packed stores, and gate and up (or a channel scale) in the same lane.
+//  * K advances 128 bytes per stage (64 bf16 or 128 int8 = 4 MFMA k-steps).
+//    Global -> registers -> LDS with two LDS stages and two register
+//    buffers: the loads of stage k+2 are issued before the MFMAs of stage k,
+//    so two stages of loads are in flight while the matrix cores run.  LDS
+//    rows are padded to 144 bytes, which makes every group of 8 lanes reading
+//    16 bytes hit 8 distinct bank quads.
 //  * Token rows are gathered straight from x into LDS by pair index; the
 //    gathered tensor never exists in HBM.  Placeholder rows load nothing
-//    (zeros) and 16-token column blocks with no valid row skip their MFMAs.
-//  * Tiles are numbered so that all tiles of one expert are consecutive,
-//    and xcd_remap gives each XCD one contiguous run of tiles, so an
-//    expert's weight slab and gathered rows are shared in one L2.
+//    (zeros) and 32-token column blocks with no valid row skip their MFMAs.
+//  * Tiles are numbered block-major (all n-tiles of a block adjacent, the
+//    blocks of one expert adjacent), and xcd_remap gives each XCD one
+//    contiguous run of tiles, so an expert's weight slab and its gathered
+//    rows are shared in one XCD's L2.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -37,30 +41,35 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 128;              // weight rows per tile
 constexpr int kBKB = 128;             // K bytes per stage
 constexpr int kLdsRow = kBKB + 16;    // padded LDS row, bytes
 constexpr int kMaxGmmExperts = 1024;
 
-template <int BM>
-struct Smem {
-  static constexpr int kStage = (kBN + BM) * kLdsRow;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16_t;
+
+template <int BN, int BM>
+struct Shape {
+  static constexpr int RB = BN / 64;   // 32-row weight blocks per wave
+  static constexpr int CB = BM / 64;   // 32-token blocks per wave
+  static constexpr int WR = BN / 32;   // weight rows staged per thread per stage
+  static constexpr int TR = BM / 32;   // token rows staged per thread per stage
+  static constexpr int kStage = (BN + BM) * kLdsRow;
   static constexpr int kBytes = 2 * kStage;
 };
 
-// MFMA on 16-byte operand fragments.
 template <int KIND> struct Mma;
-template <> struct Mma<0> {   // bf16 -> f32
-  typedef f32x4_t acc_t;
+template <> struct Mma<0> {   // bf16 x bf16 -> f32
+  typedef f32x16_t acc_t;
   static __device__ __forceinline__ acc_t run(const u32x4_t& a, const u32x4_t& b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
 };
-template <> struct Mma<1> {   // int8 -> int32 (exact)
-  typedef i32x4_t acc_t;
+template <> struct Mma<1> {   // int8 x int8 -> int32 (exact)
+  typedef i32x16_t acc_t;
   static __device__ __forceinline__ acc_t run(const u32x4_t& a, const u32x4_t& b, acc_t c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
                                                  __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
   }
 };
@@ -74,101 +83,125 @@ __device__ __forceinline__ u32x4_t cvt_f32x8_bf16(const u32x4_t& lo, const u32x4
   return r;
 }
 
+// Where this thread's staged rows come from.
+//   weight row i (local row lrow + 32 i): (i < WR/2 ? w0 : w1) + (i % (WR/2)) * wstep,
+//     loaded only if bit i of wmask is set;
+//   token row i (local row lrow + 32 i): abase + trow[i] * arow_bytes, if trow[i] >= 0.
+template <int BN, int BM>
+struct Src {
+  const uint8_t* w0;
+  const uint8_t* w1;
+  int64_t wstep;
+  uint32_t wmask;
+  const uint8_t* abase;
+  int64_t arow_bytes;
+  int trow[Shape<BN, BM>::TR];
+};
+
+template <int BN, int BM, bool TF32>
+struct Stage {
+  u32x4_t w[Shape<BN, BM>::WR];
+  u32x4_t t[Shape<BN, BM>::TR][TF32 ? 2 : 1];
+};
+
 // The K loop shared by both kernels.
-//   wp[i]   : weight row base of local weight row (tid>>3) + 32 i, or null.
-//   tp[i]   : token row base of local token row (tid>>3) + 32 i, or null.
-//   kbytes  : bytes of K in a weight row (token rows: same, or twice that
-//             for float32 tokens, TF32 = true).
-//   wrow[rb]: first local weight row of this wave's row block rb.
-//   active  : bit cb set if token column block cb of this wave has a valid row.
-template <int BM, int KIND, bool TF32>
-__device__ __forceinline__ void mainloop(uint8_t* smem, const uint8_t* const (&wp)[4],
-                                         const uint8_t* const (&tp)[BM / 32], int64_t kbytes,
-                                         const int (&wrow)[4], int tcol0, uint32_t active,
-                                         typename Mma<KIND>::acc_t (&acc)[4][BM / 32]) {
-  constexpr int NCB = BM / 32;     // token column blocks per wave (BM/2 tokens)
-  constexpr int TR = BM / 32;      // token rows staged per thread
+//   kbytes  : bytes of K in a weight row (float32 token rows hold twice that).
+//   wrow[rb]: first local weight row of this wave's 32-row block rb.
+//   tcol0   : first local token row of this wave.
+//   active  : bit cb set if token block cb of this wave holds a valid row.
+template <int BN, int BM, int KIND, bool TF32>
+__device__ __forceinline__ void mainloop(uint8_t* smem, const Src<BN, BM>& src, int64_t kbytes,
+                                         const int (&wrow)[Shape<BN, BM>::RB], int tcol0,
+                                         uint32_t active,
+                                         typename Mma<KIND>::acc_t (&acc)[Shape<BN, BM>::RB]
+                                                                          [Shape<BN, BM>::CB]) {
+  typedef Shape<BN, BM> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int ch = tid & 7;
   const int lrow = tid >> 3;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  constexpr int HALF = S::WR / 2;
 
-  u32x4_t wreg[4];
-  u32x4_t treg[TR][TF32 ? 2 : 1];
-
-  auto gload = [&](int kt) {
+  auto gload = [&](Stage<BN, BM, TF32>& r, int kt) {
     const int64_t off = (int64_t)kt * kBKB + ch * 16;
     const bool kin = off < kbytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wreg[i] = (wp[i] && kin) ? *reinterpret_cast<const u32x4_t*>(wp[i] + off) : zero;
+    for (int i = 0; i < S::WR; ++i) {
+      const uint8_t* p = (i < HALF ? src.w0 : src.w1) + (int64_t)(i % HALF) * src.wstep + off;
+      r.w[i] = (kin && ((src.wmask >> i) & 1u)) ? *reinterpret_cast<const u32x4_t*>(p) : zero;
+    }
 #pragma unroll
-    for (int i = 0; i < TR; ++i) {
+    for (int i = 0; i < S::TR; ++i) {
+      const bool ok = kin && src.trow[i] >= 0;
+      const uint8_t* p = src.abase + (int64_t)src.trow[i] * src.arow_bytes;
       if constexpr (TF32) {
-        const bool ok = tp[i] && kin;
-        treg[i][0] = ok ? *reinterpret_cast<const u32x4_t*>(tp[i] + 2 * off) : zero;
-        treg[i][1] = ok ? *reinterpret_cast<const u32x4_t*>(tp[i] + 2 * off + 16) : zero;
+        r.t[i][0] = ok ? *reinterpret_cast<const u32x4_t*>(p + 2 * off) : zero;
+        r.t[i][1] = ok ? *reinterpret_cast<const u32x4_t*>(p + 2 * off + 16) : zero;
       } else {
-        treg[i][0] = (tp[i] && kin) ? *reinterpret_cast<const u32x4_t*>(tp[i] + off) : zero;
+        r.t[i][0] = ok ? *reinterpret_cast<const u32x4_t*>(p + off) : zero;
       }
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* base = smem + buf * Smem<BM>::kStage;
+  auto sstore = [&](const Stage<BN, BM, TF32>& r, int buf) {
+    uint8_t* base = smem + buf * S::kStage + lrow * kLdsRow + ch * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4_t*>(base + (lrow + 32 * i) * kLdsRow + ch * 16) = wreg[i];
+    for (int i = 0; i < S::WR; ++i)
+      *reinterpret_cast<u32x4_t*>(base + 32 * i * kLdsRow) = r.w[i];
 #pragma unroll
-    for (int i = 0; i < TR; ++i) {
+    for (int i = 0; i < S::TR; ++i) {
       u32x4_t v;
-      if constexpr (TF32) v = cvt_f32x8_bf16(treg[i][0], treg[i][1]);
-      else v = treg[i][0];
-      *reinterpret_cast<u32x4_t*>(base + (kBN + lrow + 32 * i) * kLdsRow + ch * 16) = v;
+      if constexpr (TF32) v = cvt_f32x8_bf16(r.t[i][0], r.t[i][1]);
+      else v = r.t[i][0];
+      *reinterpret_cast<u32x4_t*>(base + (BN + 32 * i) * kLdsRow) = v;
     }
   };
   auto mma = [&](int buf) {
-    const uint8_t* base = smem + buf * Smem<BM>::kStage;
-    const int fo = (lane >> 4) * 16;
+    const uint8_t* base = smem + buf * S::kStage + (lane & 31) * kLdsRow + (lane >> 5) * 16;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t af[4];
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4_t af[S::RB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        af[rb] = *reinterpret_cast<const u32x4_t*>(base + (wrow[rb] + (lane & 15)) * kLdsRow +
-                                                   ks * 64 + fo);
+      for (int rb = 0; rb < S::RB; ++rb)
+        af[rb] = *reinterpret_cast<const u32x4_t*>(base + wrow[rb] * kLdsRow + ks * 32);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < S::CB; ++cb) {
         if (!((active >> cb) & 1u)) continue;
-        const int trow = tcol0 + cb * 16 + (lane & 15);
-        const u32x4_t bf =
-            *reinterpret_cast<const u32x4_t*>(base + (kBN + trow) * kLdsRow + ks * 64 + fo);
+        const u32x4_t bf = *reinterpret_cast<const u32x4_t*>(
+            base + (BN + tcol0 + cb * 32) * kLdsRow + ks * 32);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf, acc[rb][cb]);
+        for (int rb = 0; rb < S::RB; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf, acc[rb][cb]);
       }
     }
   };
 
   const int nk = (int)((kbytes + kBKB - 1) / kBKB);
-  gload(0);
-  sstore(0);
+  Stage<BN, BM, TF32> r0, r1;
+  gload(r0, 0);
+  if (nk > 1) gload(r1, 1);
+  sstore(r0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    mma(cur);
-    if (more) sstore(cur ^ 1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    // stage kt is in LDS buffer 0, stage kt+1 is landing in r1
+    if (kt + 2 < nk) gload(r0, kt + 2);
+    mma(0);
+    if (kt + 1 < nk) sstore(r1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    // stage kt+1 is in LDS buffer 1, stage kt+2 is landing in r0
+    if (kt + 3 < nk) gload(r1, kt + 3);
+    mma(1);
+    if (kt + 2 < nk) sstore(r0, 0);
     __syncthreads();
   }
 }
 
-template <int BM>
+template <int CB>
 __device__ __forceinline__ uint32_t active_blocks(const int* rowinfo, int tcol0) {
   const int lane = threadIdx.x & 63;
   uint32_t active = 0u;
 #pragma unroll
-  for (int cb = 0; cb < BM / 32; ++cb) {
-    const bool v = rowinfo[tcol0 + cb * 16 + (lane & 15)] >= 0;
+  for (int cb = 0; cb < CB; ++cb) {
+    const bool v = rowinfo[tcol0 + cb * 32 + (lane & 31)] >= 0;
     if (__ballot(v) != 0ull) active |= 1u << cb;
   }
   return active;
@@ -178,16 +211,17 @@ __device__ __forceinline__ uint32_t active_blocks(const int* rowinfo, int tcol0)
 // Fused-MoE grouped GEMM (bf16 weights, MFMA bf16 -> f32).
 //   EPI 0: C = acc;  EPI 1: C[:, j] = silu(acc_gate_j) * acc_up_j.
 //   TF32: tokens are float32 rows (rounded to bf16 on the way to LDS).
-template <int BM, int EPI, bool TF32, int CDT>
-__global__ void __launch_bounds__(kThreads, 2) moe_gemm_tile_kernel(MoeGemmArgs a) {
-  constexpr int TR = BM / 32;
+template <int BN, int BM, int EPI, bool TF32, int CDT>
+__global__ void __launch_bounds__(kThreads) moe_gemm_tile_kernel(MoeGemmArgs a) {
+  typedef Shape<BN, BM> S;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t Nout = EPI ? a.N / 2 : a.N;
-  const int ntile = EPI ? (int)((Nout + 63) / 64) : (int)((a.N + kBN - 1) / kBN);
+  const int64_t ncols = EPI ? BN / 2 : BN;            // output columns per tile
+  const int ntile = (int)((Nout + ncols - 1) / ncols);
   const int nblk = *a.total / BM;
   const int live = nblk * ntile;
   if ((int)blockIdx.x >= live) return;
@@ -196,6 +230,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gemm_tile_kernel(MoeGemmArgs 
   const int e = a.expert_ids[blk];
   if (e < 0) return;
   const int64_t s0 = (int64_t)blk * BM;
+  const int64_t c0 = (int64_t)nt * ncols;
 
   if (tid < BM) {
     const int p = a.sorted_ids[s0 + tid];
@@ -203,84 +238,92 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gemm_tile_kernel(MoeGemmArgs 
   }
   __syncthreads();
 
-  const int ch = tid & 7;
-  (void)ch;
   const int lrow = tid >> 3;
-  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B);
   const int64_t wrow_bytes = a.K * 2;
-  const uint8_t* wp[4];
+  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)e * a.N * wrow_bytes;
+  Src<BN, BM> src;
+  constexpr int HALF = S::WR / 2;
+  src.wstep = 32 * wrow_bytes;
+  src.wmask = 0u;
+  if (EPI) {
+    src.w0 = Bw + (c0 + lrow) * wrow_bytes;            // gate row c0 + lrow
+    src.w1 = Bw + (Nout + c0 + lrow) * wrow_bytes;     // up row
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 32 * i;
-    int64_t grow;
-    bool ok;
-    if (EPI) {
-      const int64_t hcol = (int64_t)nt * 64 + (r & 63);
-      ok = hcol < Nout;
-      grow = (r < 64) ? hcol : Nout + hcol;
-    } else {
-      grow = (int64_t)nt * kBN + r;
-      ok = grow < a.N;
-    }
-    wp[i] = ok ? Bw + ((int64_t)e * a.N + grow) * wrow_bytes : nullptr;
+    for (int i = 0; i < S::WR; ++i)
+      if (c0 + lrow + 32 * (i % HALF) < Nout) src.wmask |= 1u << i;
+  } else {
+    src.w0 = Bw + (c0 + lrow) * wrow_bytes;
+    src.w1 = src.w0 + HALF * src.wstep;
+#pragma unroll
+    for (int i = 0; i < S::WR; ++i)
+      if (c0 + lrow + 32 * i < a.N) src.wmask |= 1u << i;
   }
-  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
-  const int64_t a_row_bytes = a.lda * (TF32 ? 4 : 2);
-  const uint8_t* tp[TR];
+  src.abase = reinterpret_cast<const uint8_t*>(a.A);
+  src.arow_bytes = a.lda * (TF32 ? 4 : 2);
 #pragma unroll
-  for (int i = 0; i < TR; ++i) {
+  for (int i = 0; i < S::TR; ++i) {
     const int r = lrow + 32 * i;
     const int p = rowinfo[r];
-    const int64_t src = (a.a_rows == 0) ? (int64_t)(p / a.a_row_div) : s0 + r;
-    tp[i] = (p >= 0) ? Ab + src * a_row_bytes : nullptr;
+    src.trow[i] = p < 0 ? -1 : (a.a_rows == 0 ? p / a.a_row_div : (int)(s0 + r));
   }
 
-  int wrow[4];
+  int wrow[S::RB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-    wrow[rb] = EPI ? ((rb < 2) ? wn * 32 + rb * 16 : 64 + wn * 32 + (rb - 2) * 16)
-                   : wn * 64 + rb * 16;
+  for (int rb = 0; rb < S::RB; ++rb)
+    wrow[rb] = EPI ? ((rb < S::RB / 2) ? wn * (BN / 4) + rb * 32
+                                       : BN / 2 + wn * (BN / 4) + (rb - S::RB / 2) * 32)
+                   : wn * (BN / 2) + rb * 32;
   const int tcol0 = wm * (BM / 2);
-  const uint32_t active = active_blocks<BM>(rowinfo, tcol0);
+  const uint32_t active = active_blocks<S::CB>(rowinfo, tcol0);
 
-  f32x4_t acc[4][TR];
+  f32x16_t acc[S::RB][S::CB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < S::RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < TR; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  mainloop<BM, 0, TF32>(smem, wp, tp, wrow_bytes, wrow, tcol0, active, acc);
+  mainloop<BN, BM, 0, TF32>(smem, src, wrow_bytes, wrow, tcol0, active, acc);
 
-  // Epilogue: lane holds features 4*(lane>>4) + [0,4) of its row block for
-  // token column (lane & 15) of each column block.
+  // Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and,
+  // for g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
   constexpr int ce = ElemBytes<CDT>::value;
+  const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int cb = 0; cb < TR; ++cb) {
+  for (int cb = 0; cb < S::CB; ++cb) {
     if (!((active >> cb) & 1u)) continue;
-    const int trow = tcol0 + cb * 16 + (lane & 15);
+    const int trow = tcol0 + cb * 32 + (lane & 31);
     const int p = rowinfo[trow];
     if (p < 0) continue;
     const int64_t crow = (a.c_rows == 0) ? (int64_t)p : s0 + trow;
     const float w = a.topk_weights ? a.topk_weights[p] : 1.0f;
-    uint8_t* crow_ptr = Cb + crow * a.ldc * ce;
+    uint8_t* rowp = Cb + crow * a.ldc * ce;
     if (EPI) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = (int64_t)nt * 64 + wn * 32 + j * 16 + 4 * (lane >> 4);
-        if (col < Nout) {
-          const f32x4_t g = acc[j][cb], u = acc[j + 2][cb];
-          store4<CDT>(crow_ptr + col * ce, silu_f32(g[0]) * u[0] * w, silu_f32(g[1]) * u[1] * w,
-                      silu_f32(g[2]) * u[2] * w, silu_f32(g[3]) * u[3] * w);
+      for (int j = 0; j < S::RB / 2; ++j) {
+        const f32x16_t gt = acc[j][cb], up = acc[j + S::RB / 2][cb];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = c0 + wn * (BN / 4) + j * 32 + 8 * g + rsub;
+          if (col < Nout)
+            store4<CDT>(rowp + col * ce, silu_f32(gt[4 * g]) * up[4 * g] * w,
+                        silu_f32(gt[4 * g + 1]) * up[4 * g + 1] * w,
+                        silu_f32(gt[4 * g + 2]) * up[4 * g + 2] * w,
+                        silu_f32(gt[4 * g + 3]) * up[4 * g + 3] * w);
         }
       }
     } else {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int64_t col = (int64_t)nt * kBN + wn * 64 + rb * 16 + 4 * (lane >> 4);
-        if (col < a.N) {
-          const f32x4_t v = acc[rb][cb];
-          store4<CDT>(crow_ptr + col * ce, v[0] * w, v[1] * w, v[2] * w, v[3] * w);
+      for (int rb = 0; rb < S::RB; ++rb) {
+        const f32x16_t v = acc[rb][cb];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = c0 + wrow[rb] + 8 * g + rsub;
+          if (col < a.N)
+            store4<CDT>(rowp + col * ce, v[4 * g] * w, v[4 * g + 1] * w, v[4 * g + 2] * w,
+                        v[4 * g + 3] * w);
         }
       }
     }
@@ -289,11 +332,12 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gemm_tile_kernel(MoeGemmArgs 
 
 // ---------------------------------------------------------------------------
 // INT8 GMM: rows [off[e], off[e+1]) of X use W[e]; fp16 output.
+constexpr int kGmmBN = 256;
 constexpr int kGmmBM = 128;
 
-__global__ void __launch_bounds__(kThreads, 2) gmm_i8_tile_kernel(GmmI8Args a) {
-  constexpr int BM = kGmmBM;
-  constexpr int TR = BM / 32;
+__global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
+  constexpr int BN = kGmmBN, BM = kGmmBM;
+  typedef Shape<BN, BM> S;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int tprefix[kMaxGmmExperts + 1];   // m-tiles before expert e
   __shared__ int scan_buf[kThreads];
@@ -303,7 +347,7 @@ __global__ void __launch_bounds__(kThreads, 2) gmm_i8_tile_kernel(GmmI8Args a) {
   const int wn = wave & 1, wm = wave >> 1;
   const int E = a.E;
   const int M = (int)a.M;
-  const int ntile = (int)((a.N + kBN - 1) / kBN);
+  const int ntile = (int)((a.N + BN - 1) / BN);
 
   // m-tile counts per expert from the (clamped) offsets, then a scan.
   auto lo_of = [&](int e) {
@@ -349,7 +393,7 @@ __global__ void __launch_bounds__(kThreads, 2) gmm_i8_tile_kernel(GmmI8Args a) {
   const int live = total_mt * ntile;
   if ((int)blockIdx.x >= live) return;
   const int L = xcd_remap((int)blockIdx.x, live);
-  // Find the expert: largest e with tprefix[e] * ntile <= L.
+  // Expert: largest e with tprefix[e] * ntile <= L.
   int lo = 0, hi = E;   // invariant: tprefix[lo]*ntile <= L < tprefix[hi]*ntile
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -363,52 +407,62 @@ __global__ void __launch_bounds__(kThreads, 2) gmm_i8_tile_kernel(GmmI8Args a) {
   int row_hi = lo_of(e + 1);
   row_hi = row_hi < row_lo ? row_lo : row_hi;
   const int row0 = row_lo + mt * BM;
+  const int64_t n0 = (int64_t)nt * BN;
 
   if (tid < BM) rowinfo[tid] = (row0 + tid < row_hi) ? row0 + tid : -1;
   __syncthreads();
 
   const int lrow = tid >> 3;
-  const uint8_t* wp[4];
+  Src<BN, BM> src;
+  constexpr int HALF = S::WR / 2;
+  src.wstep = 32 * a.K;
+  src.w0 = reinterpret_cast<const uint8_t*>(a.W) + ((int64_t)e * a.N + n0 + lrow) * a.K;
+  src.w1 = src.w0 + HALF * src.wstep;
+  src.wmask = 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t n = (int64_t)nt * kBN + lrow + 32 * i;
-    wp[i] = n < a.N ? reinterpret_cast<const uint8_t*>(a.W) + ((int64_t)e * a.N + n) * a.K : nullptr;
-  }
-  const uint8_t* tp[TR];
+  for (int i = 0; i < S::WR; ++i)
+    if (n0 + lrow + 32 * i < a.N) src.wmask |= 1u << i;
+  src.abase = reinterpret_cast<const uint8_t*>(a.X);
+  src.arow_bytes = a.K;
 #pragma unroll
-  for (int i = 0; i < TR; ++i) {
-    const int m = rowinfo[lrow + 32 * i];
-    tp[i] = m >= 0 ? reinterpret_cast<const uint8_t*>(a.X) + (int64_t)m * a.K : nullptr;
-  }
-  int wrow[4];
+  for (int i = 0; i < S::TR; ++i) src.trow[i] = rowinfo[lrow + 32 * i];
+
+  int wrow[S::RB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) wrow[rb] = wn * 64 + rb * 16;
+  for (int rb = 0; rb < S::RB; ++rb) wrow[rb] = wn * (BN / 2) + rb * 32;
   const int tcol0 = wm * (BM / 2);
-  const uint32_t active = active_blocks<BM>(rowinfo, tcol0);
+  const uint32_t active = active_blocks<S::CB>(rowinfo, tcol0);
 
-  i32x4_t acc[4][TR];
+  i32x16_t acc[S::RB][S::CB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < S::RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < TR; ++cb) acc[rb][cb] = i32x4_t{0, 0, 0, 0};
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
 
-  mainloop<BM, 1, false>(smem, wp, tp, a.K, wrow, tcol0, active, acc);
+  mainloop<BN, BM, 1, false>(smem, src, a.K, wrow, tcol0, active, acc);
 
   uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
+  const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int cb = 0; cb < TR; ++cb) {
+  for (int cb = 0; cb < S::CB; ++cb) {
     if (!((active >> cb) & 1u)) continue;
-    const int m = rowinfo[tcol0 + cb * 16 + (lane & 15)];
+    const int m = rowinfo[tcol0 + cb * 32 + (lane & 31)];
     if (m < 0) continue;
     const float sx = a.sx[m];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int64_t n = (int64_t)nt * kBN + wn * 64 + rb * 16 + 4 * (lane >> 4);
-      if (n < a.N) {
-        const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(a.sw + (int64_t)e * a.N + n);
-        const i32x4_t v = acc[rb][cb];
-        store4<2>(Yb + ((int64_t)m * a.N + n) * 2, (float)v[0] * sx * sw[0],
-                  (float)v[1] * sx * sw[1], (float)v[2] * sx * sw[2], (float)v[3] * sx * sw[3]);
+    for (int rb = 0; rb < S::RB; ++rb) {
+      const i32x16_t v = acc[rb][cb];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wrow[rb] + 8 * g + rsub;
+        if (n < a.N) {
+          const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(a.sw + (int64_t)e * a.N + n);
+          store4<2>(Yb + ((int64_t)m * a.N + n) * 2, (float)v[4 * g] * sx * sw[0],
+                    (float)v[4 * g + 1] * sx * sw[1], (float)v[4 * g + 2] * sx * sw[2],
+                    (float)v[4 * g + 3] * sx * sw[3]);
+        }
       }
     }
   }
@@ -422,51 +476,65 @@ hipError_t ensure_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int BM, int EPI, bool TF32, int CDT>
+template <int BN, int BM, int EPI, bool TF32, int CDT>
 hipError_t launch_tile_t(const MoeGemmArgs& a, hipStream_t stream) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
-  const int ntile = EPI ? (int)((Nout + 63) / 64) : (int)((a.N + kBN - 1) / kBN);
+  const int64_t ncols = EPI ? BN / 2 : BN;
+  const int64_t ntile = (Nout + ncols - 1) / ncols;
   const int64_t grid = (a.max_padded / BM) * ntile;
   if (grid == 0) return hipSuccess;
-  auto k = moe_gemm_tile_kernel<BM, EPI, TF32, CDT>;
-  const hipError_t st = ensure_lds(k, Smem<BM>::kBytes);
+  auto k = moe_gemm_tile_kernel<BN, BM, EPI, TF32, CDT>;
+  constexpr size_t lds = Shape<BN, BM>::kBytes;
+  const hipError_t st = ensure_lds(k, lds);
   if (st != hipSuccess) return st;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), Smem<BM>::kBytes, stream, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int BM, int EPI, bool TF32>
+template <int BN, int BM, int EPI, bool TF32>
 hipError_t launch_tile_c(const MoeGemmArgs& a, hipStream_t s) {
   switch (a.c_dtype) {
-    case 0: return launch_tile_t<BM, EPI, TF32, 0>(a, s);
-    case 1: return launch_tile_t<BM, EPI, TF32, 1>(a, s);
-    default: return launch_tile_t<BM, EPI, TF32, 2>(a, s);
+    case 0: return launch_tile_t<BN, BM, EPI, TF32, 0>(a, s);
+    case 1: return launch_tile_t<BN, BM, EPI, TF32, 1>(a, s);
+    default: return launch_tile_t<BN, BM, EPI, TF32, 2>(a, s);
   }
 }
 
 template <int BM>
 hipError_t launch_tile_bm(const MoeGemmArgs& a, hipStream_t s) {
+  constexpr int BN = 256;
   const bool tf32 = a.a_dtype == 0;
-  if (a.epilogue) return tf32 ? launch_tile_c<BM, 1, true>(a, s) : launch_tile_c<BM, 1, false>(a, s);
-  return tf32 ? launch_tile_c<BM, 0, true>(a, s) : launch_tile_c<BM, 0, false>(a, s);
+  if constexpr (BM > 128) {
+    if (tf32) return hipErrorInvalidValue;   // rejected by the ABI layer beforehand
+    return a.epilogue ? launch_tile_c<BN, BM, 1, false>(a, s) : launch_tile_c<BN, BM, 0, false>(a, s);
+  } else {
+    if (a.epilogue)
+      return tf32 ? launch_tile_c<BN, BM, 1, true>(a, s) : launch_tile_c<BN, BM, 1, false>(a, s);
+    return tf32 ? launch_tile_c<BN, BM, 0, true>(a, s) : launch_tile_c<BN, BM, 0, false>(a, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
-  return a.block_m == 64 ? launch_tile_bm<64>(a, stream) : launch_tile_bm<128>(a, stream);
+  switch (a.block_m) {
+    case 64: return launch_tile_bm<64>(a, stream);
+    case 128: return launch_tile_bm<128>(a, stream);
+    default: return launch_tile_bm<256>(a, stream);
+  }
 }
 
 hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream) {
-  const int ntile = (int)((a.N + kBN - 1) / kBN);
+  const int ntile = (int)((a.N + kGmmBN - 1) / kGmmBN);
   // Upper bound of m-tiles: every non-empty expert adds at most one partial tile.
   const int64_t mt_max = (a.M + kGmmBM - 1) / kGmmBM + a.E;
   const int64_t grid = mt_max * ntile;
   if (grid == 0 || a.M == 0) return hipSuccess;
-  const hipError_t st = ensure_lds(gmm_i8_tile_kernel, Smem<kGmmBM>::kBytes);
+  typedef Shape<kGmmBN, kGmmBM> S;
+  const hipError_t st = ensure_lds(gmm_i8_tile_kernel, S::kBytes);
   if (st != hipSuccess) return st;
-  hipLaunchKernelGGL(gmm_i8_tile_kernel, dim3((unsigned)grid), dim3(kThreads),
-                     Smem<kGmmBM>::kBytes, stream, a);
+  hipLaunchKernelGGL(gmm_i8_tile_kernel, dim3((unsigned)grid), dim3(kThreads), S::kBytes, stream,
+                     a);
   return hipGetLastError();
 }
 

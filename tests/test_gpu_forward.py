@@ -70,7 +70,7 @@ def test_tiny_layer(moe, dev, block_m):
     assert err <= BAR_BF16
 
 
-@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("block_m", [16, 128, 256])
 def test_tiny_layer_bf16_x(moe, dev, block_m):
     cfg = synth.CONFIGS["tiny"]
     d = layer_inputs(cfg, dev, x_dtype="bf16")
@@ -86,7 +86,7 @@ def test_single_expert_is_dense(moe, dev):
     from synth.configs import Config
     cfg = Config(11, "dense", T=37, H=64, I=96, E=1, topk=1, x_dtype="bf16", w_std=0.1)
     d = layer_inputs(cfg, dev)
-    for bm in (16, 64):
+    for bm in (16, 64, 256):
         out, w, ids = _run(moe, cfg, d, bm, dev)
         assert (ids == 0).all() and np.allclose(w, 1.0)
         ref = oracle.dense_swiglu(d["x_host"], d["w1_host"][0], d["w2_host"][0])

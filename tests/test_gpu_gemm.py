@@ -16,7 +16,7 @@ from parity import max_abs_rel
 
 pytestmark = pytest.mark.gpu
 
-BLOCKS = [16, 32, 64, 128]
+BLOCKS = [16, 32, 64, 128, 256]
 
 
 @pytest.fixture(scope="module")
@@ -106,7 +106,7 @@ def test_gemm_pair_rows(moe, dev, B, epilogue, c_dtype):
     assert max_abs_rel(got, ref) <= _tol(c_dtype)
 
 
-@pytest.mark.parametrize("B", BLOCKS)
+@pytest.mark.parametrize("B", [b for b in BLOCKS if b != 256])
 def test_gemm_sorted_rows_and_f32_input(moe, dev, B):
     """A rows by sorted position (how the layer feeds its second GEMM), C rows
     by sorted position; float32 A rounded to bf16 on load."""
@@ -151,3 +151,12 @@ def test_gemm_skewed_experts(moe, dev, B):
     ref, _ = oracle.grouped_gemm_sorted(oracle.bf16_bits_to_f64(Ab), oracle.bf16_bits_to_f64(Bb),
                                         s, e, B, T, 1)
     assert max_abs_rel(C.cpu().numpy(), ref) <= 1e-5
+
+
+def test_gemm_f32_input_rejected_at_256(moe, dev):
+    ids = np.zeros((8, 1), np.int64)
+    sb, eb, tot, *_ = _meta(moe, ids, 1, 256, dev)
+    A = torch.zeros((8, 64), dtype=torch.float32, device=dev)
+    Bw = torch.zeros((1, 32, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.moe_grouped_gemm(A, Bw, sb, eb, tot, 256, 8)

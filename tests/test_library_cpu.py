@@ -182,3 +182,11 @@ def test_gmm_validation(mod):
     assert L.gmm_int8(f, None, f, f, f, None, f, 2048, 4096, 4096, 32, None) == d["MOE_ERR_NULL"]
     assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 1 << 20, 4096, 32, None) == d["MOE_ERR_SHAPE"]
     assert L.gmm_int8(None, f, None, f, f, None, None, 0, 4096, 4096, 32, None) == 0   # M = 0
+
+
+def test_forward_block_m_choice(mod):
+    assert mod.moe_forward_block_m(4096, 128, 8) == 256          # prefill shape, bf16 x
+    assert mod.moe_forward_block_m(4096, 128, 8, "f32") == 128   # f32 x caps at 128
+    assert mod.moe_forward_block_m(16, 256, 8) == 16             # decode shape
+    assert mod.moe_forward_block_m(64, 8, 2, "f32") == 32        # tiny layer
+    assert mod.lib.moe_forward_block_m(16, 0, 8, 1) == -1

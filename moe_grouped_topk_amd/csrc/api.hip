@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"   // include/ is on the include path
 #include "launch.hpp"
 
 namespace {

@@ -69,7 +69,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) {
-  return z / (1.0f + __expf(-z));
+  return __fdividef(z, 1.0f + __expf(-z));
 }
 
 // Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).

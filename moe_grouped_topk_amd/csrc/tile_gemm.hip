@@ -20,14 +20,15 @@
 //    lane ends up with runs of 4 consecutive OUTPUT FEATURES of one token:
 //    packed stores, and gate and up (or a channel scale) in the same lane.
 //  * K advances 128 bytes per stage (64 bf16 or 128 int8 = 4 MFMA k-steps).
-//    Global -> registers -> LDS with two LDS stages and two register
-//    buffers: the loads of stage k+2 are issued before the MFMAs of stage k,
-//    so two stages of loads are in flight while the matrix cores run.  LDS
+//    Global -> registers -> LDS with two LDS stages and (for BM <= 128) two
+//    register buffers: the loads of stage k+2 are issued before the MFMAs of
+//    stage k, so two stages of loads are in flight while the matrix cores
+//    run (BM = 256 keeps one stage in flight to stay within 512 registers).  LDS
 //    rows are padded to 144 bytes, which makes every group of 8 lanes reading
 //    16 bytes hit 8 distinct bank quads.
 //  * Token rows are gathered straight from x into LDS by pair index; the
-//    gathered tensor never exists in HBM.  Placeholder rows load nothing
-//    (zeros) and 32-token column blocks with no valid row skip their MFMAs.
+//    gathered tensor never exists in HBM.  Placeholder rows are masked at
+//    the store; loads and MFMAs are branch-free.
 //  * Tiles are numbered block-major (all n-tiles of a block adjacent, the
 //    blocks of one expert adjacent), and xcd_remap gives each XCD one
 //    contiguous run of tiles, so an expert's weight slab and its gathered
@@ -40,22 +41,36 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBKB = 128;             // K bytes per stage
 constexpr int kLdsRow = kBKB + 16;    // padded LDS row, bytes
 constexpr int kMaxGmmExperts = 1024;
 
+#ifndef MOE_TILE_NBUF
+#define MOE_TILE_NBUF 1   // register prefetch buffers (loads one stage ahead)
+#endif
+#ifndef MOE_T256_WN
+#define MOE_T256_WN 2     // 256 x 256 tile: 2 x 4 waves of 128 x 64
+#define MOE_T256_WM 4
+#endif
+
+
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16_t;
 
-template <int BN, int BM>
-struct Shape {
-  static constexpr int RB = BN / 64;   // 32-row weight blocks per wave
-  static constexpr int CB = BM / 64;   // 32-token blocks per wave
-  static constexpr int WR = BN / 32;   // weight rows staged per thread per stage
-  static constexpr int TR = BM / 32;   // token rows staged per thread per stage
+// Tile shape: BN weight rows x BM tokens, WN x WM waves (WN along the
+// weight rows), NBUF register buffers for the global -> LDS staging.
+template <int BN_, int BM_, int WN_, int WM_, int NBUF_>
+struct Cfg {
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, NBUF = NBUF_;
+  static constexpr int THREADS = 64 * WN * WM;
+  static constexpr int STEP = THREADS / 8;      // staged rows per pass (8 x 16 B per row)
+  static constexpr int RB = BN / WN / 32;       // 32-row weight blocks per wave
+  static constexpr int CB = BM / WM / 32;       // 32-token blocks per wave
+  static constexpr int WR = BN / STEP;          // weight rows staged per thread per stage
+  static constexpr int TR = BM / STEP;          // token rows staged per thread per stage
   static constexpr int kStage = (BN + BM) * kLdsRow;
   static constexpr int kBytes = 2 * kStage;
+  static_assert(WR % 2 == 0 && TR >= 1 && RB >= 1 && CB >= 1, "tile shape");
 };
 
 template <int KIND> struct Mma;
@@ -83,76 +98,86 @@ __device__ __forceinline__ u32x4_t cvt_f32x8_bf16(const u32x4_t& lo, const u32x4
   return r;
 }
 
-// Where this thread's staged rows come from.
-//   weight row i (local row lrow + 32 i): (i < WR/2 ? w0 : w1) + (i % (WR/2)) * wstep,
-//     loaded only if bit i of wmask is set;
-//   token row i (local row lrow + 32 i): abase + trow[i] * arow_bytes, if trow[i] >= 0.
-template <int BN, int BM>
+// Where this thread's staged rows come from.  Every row address is
+// dereferenceable: rows past the weight matrix and placeholder token rows
+// read a valid row instead.  What they load only reaches output elements
+// that the epilogue masks (an MFMA output element depends on one weight row
+// and one token column only).  Loads are therefore unconditional, which
+// keeps them out of branches and lets several stages stay in flight.
+//   weight row i (local row lrow + STEP i) = w[i < WR/2 ? 0 : 1] + j * wstep with
+//     j = min(i % (WR/2), wlast[...]); wlast < 0 means no valid row: w[0] is
+//     then already a valid fallback row and j = 0;
+//   token row i (local row lrow + STEP i) = abase + trow[i] * arow_bytes.
+template <class C>
 struct Src {
-  const uint8_t* w0;
-  const uint8_t* w1;
+  const uint8_t* w[2];
   int64_t wstep;
-  uint32_t wmask;
+  int wlast[2];
   const uint8_t* abase;
   int64_t arow_bytes;
-  int trow[Shape<BN, BM>::TR];
+  int trow[C::TR];
 };
 
-template <int BN, int BM, bool TF32>
+template <class C, bool TF32>
 struct Stage {
-  u32x4_t w[Shape<BN, BM>::WR];
-  u32x4_t t[Shape<BN, BM>::TR][TF32 ? 2 : 1];
+  u32x4_t w[C::WR];
+  u32x4_t t[C::TR][TF32 ? 2 : 1];
 };
 
 // The K loop shared by both kernels.
 //   kbytes  : bytes of K in a weight row (float32 token rows hold twice that).
 //   wrow[rb]: first local weight row of this wave's 32-row block rb.
 //   tcol0   : first local token row of this wave.
-//   active  : bit cb set if token block cb of this wave holds a valid row.
-template <int BN, int BM, int KIND, bool TF32>
-__device__ __forceinline__ void mainloop(uint8_t* smem, const Src<BN, BM>& src, int64_t kbytes,
-                                         const int (&wrow)[Shape<BN, BM>::RB], int tcol0,
-                                         uint32_t active,
-                                         typename Mma<KIND>::acc_t (&acc)[Shape<BN, BM>::RB]
-                                                                          [Shape<BN, BM>::CB]) {
-  typedef Shape<BN, BM> S;
+// All MFMAs run, also on placeholder token columns (their outputs are never
+// stored): a branch per column block would serialise the LDS reads with the
+// MFMAs, and tiles that are mostly padding are bound by weight streaming.
+template <class C, int KIND, bool TF32>
+__device__ __forceinline__ void mainloop(uint8_t* smem, const Src<C>& src, int64_t kbytes,
+                                         const int (&wrow)[C::RB], int tcol0,
+                                         typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
+  typedef C S;
+  constexpr int BN = C::BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int ch = tid & 7;
   const int lrow = tid >> 3;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   constexpr int HALF = S::WR / 2;
 
-  auto gload = [&](Stage<BN, BM, TF32>& r, int kt) {
-    const int64_t off = (int64_t)kt * kBKB + ch * 16;
-    const bool kin = off < kbytes;
+  // K tail: a chunk past K loads from offset 0 of its row; it is zeroed when
+  // written to LDS (a select at store time, when the data has arrived anyway).
+  auto gload = [&](Stage<C, TF32>& r, int kt) {
+    const int64_t off0 = (int64_t)kt * kBKB + ch * 16;
+    const int64_t off = off0 < kbytes ? off0 : 0;
 #pragma unroll
     for (int i = 0; i < S::WR; ++i) {
-      const uint8_t* p = (i < HALF ? src.w0 : src.w1) + (int64_t)(i % HALF) * src.wstep + off;
-      r.w[i] = (kin && ((src.wmask >> i) & 1u)) ? *reinterpret_cast<const u32x4_t*>(p) : zero;
+      const int h = i < HALF ? 0 : 1;
+      const int j = i % HALF;
+      const int jj = j < src.wlast[h] ? j : (src.wlast[h] < 0 ? 0 : src.wlast[h]);
+      r.w[i] = *reinterpret_cast<const u32x4_t*>(src.w[h] + jj * src.wstep + off);
     }
 #pragma unroll
     for (int i = 0; i < S::TR; ++i) {
-      const bool ok = kin && src.trow[i] >= 0;
-      const uint8_t* p = src.abase + (int64_t)src.trow[i] * src.arow_bytes;
+      const uint8_t* t = src.abase + (int64_t)src.trow[i] * src.arow_bytes;
       if constexpr (TF32) {
-        r.t[i][0] = ok ? *reinterpret_cast<const u32x4_t*>(p + 2 * off) : zero;
-        r.t[i][1] = ok ? *reinterpret_cast<const u32x4_t*>(p + 2 * off + 16) : zero;
+        r.t[i][0] = *reinterpret_cast<const u32x4_t*>(t + 2 * off);
+        r.t[i][1] = *reinterpret_cast<const u32x4_t*>(t + 2 * off + 16);
       } else {
-        r.t[i][0] = ok ? *reinterpret_cast<const u32x4_t*>(p + off) : zero;
+        r.t[i][0] = *reinterpret_cast<const u32x4_t*>(t + off);
       }
     }
   };
-  auto sstore = [&](const Stage<BN, BM, TF32>& r, int buf) {
+  auto sstore = [&](const Stage<C, TF32>& r, int buf, int kt) {
+    const bool kin = (int64_t)kt * kBKB + ch * 16 < kbytes;
     uint8_t* base = smem + buf * S::kStage + lrow * kLdsRow + ch * 16;
 #pragma unroll
     for (int i = 0; i < S::WR; ++i)
-      *reinterpret_cast<u32x4_t*>(base + 32 * i * kLdsRow) = r.w[i];
+      *reinterpret_cast<u32x4_t*>(base + S::STEP * i * kLdsRow) = kin ? r.w[i] : zero;
 #pragma unroll
     for (int i = 0; i < S::TR; ++i) {
       u32x4_t v;
       if constexpr (TF32) v = cvt_f32x8_bf16(r.t[i][0], r.t[i][1]);
       else v = r.t[i][0];
-      *reinterpret_cast<u32x4_t*>(base + (BN + 32 * i) * kLdsRow) = v;
+      *reinterpret_cast<u32x4_t*>(base + (BN + S::STEP * i) * kLdsRow) = kin ? v : zero;
     }
   };
   auto mma = [&](int buf) {
@@ -163,150 +188,323 @@ __device__ __forceinline__ void mainloop(uint8_t* smem, const Src<BN, BM>& src, 
 #pragma unroll
       for (int rb = 0; rb < S::RB; ++rb)
         af[rb] = *reinterpret_cast<const u32x4_t*>(base + wrow[rb] * kLdsRow + ks * 32);
+      u32x4_t bfr[S::CB];
 #pragma unroll
-      for (int cb = 0; cb < S::CB; ++cb) {
-        if (!((active >> cb) & 1u)) continue;
-        const u32x4_t bf = *reinterpret_cast<const u32x4_t*>(
-            base + (BN + tcol0 + cb * 32) * kLdsRow + ks * 32);
+      for (int cb = 0; cb < S::CB; ++cb)
+        bfr[cb] = *reinterpret_cast<const u32x4_t*>(base + (BN + tcol0 + cb * 32) * kLdsRow +
+                                                    ks * 32);
 #pragma unroll
-        for (int rb = 0; rb < S::RB; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf, acc[rb][cb]);
-      }
+      for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < S::RB; ++rb)
+          acc[rb][cb] = Mma<KIND>::run(af[rb], bfr[cb], acc[rb][cb]);
     }
   };
 
   const int nk = (int)((kbytes + kBKB - 1) / kBKB);
-  Stage<BN, BM, TF32> r0, r1;
+  if constexpr (S::NBUF == 1) {
+    // one register buffer: the loads of stage k+1 fly during the MFMAs of k
+    Stage<C, TF32> r;
+    gload(r, 0);
+    sstore(r, 0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) gload(r, kt + 1);
+      mma(kt & 1);
+      if (more) sstore(r, (kt + 1) & 1, kt + 1);
+      __syncthreads();
+    }
+    return;
+  }
+  Stage<C, TF32> r0, r1;
   gload(r0, 0);
   if (nk > 1) gload(r1, 1);
-  sstore(r0, 0);
+  sstore(r0, 0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     // stage kt is in LDS buffer 0, stage kt+1 is landing in r1
     if (kt + 2 < nk) gload(r0, kt + 2);
     mma(0);
-    if (kt + 1 < nk) sstore(r1, 1);
+    if (kt + 1 < nk) sstore(r1, 1, kt + 1);
     __syncthreads();
     if (kt + 1 >= nk) break;
     // stage kt+1 is in LDS buffer 1, stage kt+2 is landing in r0
     if (kt + 3 < nk) gload(r1, kt + 3);
     mma(1);
-    if (kt + 2 < nk) sstore(r0, 0);
+    if (kt + 2 < nk) sstore(r0, 0, kt + 2);
     __syncthreads();
   }
 }
 
-template <int CB>
-__device__ __forceinline__ uint32_t active_blocks(const int* rowinfo, int tcol0) {
-  const int lane = threadIdx.x & 63;
-  uint32_t active = 0u;
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const bool v = rowinfo[tcol0 + cb * 32 + (lane & 31)] >= 0;
-    if (__ballot(v) != 0ull) active |= 1u << cb;
+// ---------------------------------------------------------------------------
+// Direct-to-LDS K loop (bf16 / int8 operands).
+//
+// gfx950's global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at
+// M0 + 16 l, so the loads need no staging registers and NSTAGE-1 stages of
+// them can be in flight.  A stage holds 64 bytes of K for each of the BN + BM
+// rows (row-major, 64 B per row).  Inside a row the four 16-byte chunks are
+// stored XOR-swizzled, chunk c of row r at position c ^ ((r >> 2) & 3): the
+// DMA lane that owns position p fetches chunk p ^ ((r >> 2) & 3).  gfx950's
+// LDS serves a 16-byte read for 16 lanes per cycle across 64 banks (256 B);
+// an MFMA operand read of chunk c by 16 consecutive rows then lands on 16
+// distinct 16-byte slots of that 256-byte window (measured: without the
+// swizzle every other LDS cycle was a bank conflict).
+//
+// The loads are issued from inline assembly, so the compiler does not insert
+// its conservative waits on them; the loop waits itself (vmcnt), and each
+// wait is followed by a workgroup barrier so that every wave's loads of the
+// stage have landed before any wave reads it.  The barrier's "memory" clobber
+// keeps the compiler from moving LDS reads across it.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_u8*)(void*)p;
+}
+
+__device__ __forceinline__ void dma16(uint32_t m0, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(g) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+
+template <int NI>
+__device__ __forceinline__ void wait_stage_nobar(int n_after) {
+  switch (n_after) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<NI>(); break;
+    case 2: wait_vm<2 * NI>(); break;
+    default: wait_vm<3 * NI>(); break;
   }
-  return active;
+}
+
+template <int NI>
+__device__ __forceinline__ void wait_stage(int n_after) {
+  // wait until only n_after stages (NI loads each) of this wave are pending
+  switch (n_after) {
+    case 0: wait_vm_barrier<0>(); break;
+    case 1: wait_vm_barrier<NI>(); break;
+    case 2: wait_vm_barrier<2 * NI>(); break;
+    default: wait_vm_barrier<3 * NI>(); break;
+  }
+}
+
+template <int BN_, int BM_, int NSTAGE_, int WN_ = 2, int WM_ = 2>
+struct DmaCfg {
+  static constexpr int BN = BN_, BM = BM_, NSTAGE = NSTAGE_;
+  static constexpr int WN = WN_, WM = WM_, THREADS = 64 * WN * WM;
+  static constexpr int ROWB = 64;                            // LDS bytes per row per stage
+  static constexpr int RB = BN / WN / 32, CB = BM / WM / 32;
+  static constexpr int NI = (BN + BM) / 16 / (WN * WM);      // DMA instructions per wave per stage
+  static constexpr int kStage = (BN + BM) * ROWB;
+  static constexpr int kBytes = NSTAGE * kStage;
+  static_assert((BN + BM) % (16 * WN * WM) == 0 && NSTAGE >= 2 && NSTAGE <= 4, "dma tile shape");
+};
+
+// rowp[j]: global address of the start of this lane's j-th DMA row (local
+// row (wave * NI + j) * 16 + lane / 4); every row is at least 16 bytes long.
+// kbytes: bytes of K per row.  A partial last stage is handled by loading a
+// valid chunk and zeroing it in LDS afterwards.
+template <class C, int KIND>
+__device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
+                                             int64_t kbytes, const int (&wrow)[C::RB], int tcol0,
+                                             typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t sbase = lds_addr(smem);
+  const int chunk_pos = lane & 3;
+  const int nk = (int)((kbytes + C::ROWB - 1) / C::ROWB);
+
+  auto issue = [&](int kt) {
+    const uint32_t st = sbase + (uint32_t)((kt % C::NSTAGE) * C::kStage);
+    const int64_t koff = (int64_t)kt * C::ROWB;
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+      const int row = (wave * C::NI + j) * 16 + (lane >> 2);
+      const int c = chunk_pos ^ ((row >> 2) & 3);            // chunk this lane fetches
+      const int64_t off = koff + c * 16 < kbytes ? koff + c * 16 : 0;   // past K: row start
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (uint32_t)((wave * C::NI + j) * 1024));
+      dma16(m0, rowp[j] + off);
+    }
+  };
+  // zero the chunks of a partial stage that lie past K (after its loads landed)
+  auto zero_tail = [&](int kt) {
+    uint8_t* st = smem + (kt % C::NSTAGE) * C::kStage;
+    const int64_t koff = (int64_t)kt * C::ROWB;
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+      const int row = (wave * C::NI + j) * 16 + (lane >> 2);
+      const int c = chunk_pos ^ ((row >> 2) & 3);
+      if (koff + c * 16 >= kbytes)
+        *reinterpret_cast<u32x4_t*>(st + (wave * C::NI + j) * 1024 + lane * 16) =
+            u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // MFMA operand fragments are double-buffered in registers: the LDS reads
+  // of the next k-step (32 elements of K) are in flight while the MFMAs of
+  // the current one run; the first k-step of the next stage is read right
+  // after the barrier that publishes it.
+  const int swz = ((lane & 31) >> 2) & 3;
+  auto load_frags = [&](int kt, int ks, u32x4_t (&af)[C::RB], u32x4_t (&bf)[C::CB]) {
+    const uint8_t* st = smem + (kt % C::NSTAGE) * C::kStage + (lane & 31) * C::ROWB;
+    const int pos = ((ks * 2 + (lane >> 5)) ^ swz) * 16;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+      af[rb] = *reinterpret_cast<const u32x4_t*>(st + wrow[rb] * C::ROWB + pos);
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+      bf[cb] = *reinterpret_cast<const u32x4_t*>(st + (C::BN + tcol0 + cb * 32) * C::ROWB + pos);
+  };
+  auto mfmas = [&](const u32x4_t (&af)[C::RB], const u32x4_t (&bf)[C::CB]) {
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf[cb], acc[rb][cb]);
+  };
+  const bool partial = (kbytes % C::ROWB) != 0;
+  // Publish stage s: this wave's loads of it have landed (n_after later
+  // stages may still be pending), then all waves meet at the barrier.
+  auto publish = [&](int s, int n_after) {
+    if (partial && s == nk - 1) {
+      wait_stage_nobar<C::NI>(0);
+      zero_tail(s);
+      __syncthreads();
+    } else {
+      wait_stage<C::NI>(n_after);
+    }
+  };
+
+  // Stage s goes to LDS buffer s % NSTAGE; all NSTAGE buffers start loading.
+  const int pre = nk < C::NSTAGE ? nk : C::NSTAGE;
+  for (int kt = 0; kt < pre; ++kt) issue(kt);
+  u32x4_t a0[C::RB], b0[C::CB], a1[C::RB], b1[C::CB];
+  publish(0, pre - 1);
+  load_frags(0, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    load_frags(kt, 1, a1, b1);
+    mfmas(a0, b0);
+    if (kt + 1 < nk) {
+      const int last = (kt + C::NSTAGE - 1 < nk - 1) ? kt + C::NSTAGE - 1 : nk - 1;
+      publish(kt + 1, last - (kt + 1));
+      // every wave has finished reading stage kt: refill its buffer
+      if (kt + C::NSTAGE < nk) issue(kt + C::NSTAGE);
+      load_frags(kt + 1, 0, a0, b0);
+    }
+    mfmas(a1, b1);
+  }
 }
 
 // ---------------------------------------------------------------------------
+// Weight-row sources of a thread: local rows lrow + STEP i, i < WR; rows of
+// the second half (i >= WR/2) come from w[1].  `first` is the global row of
+// local row lrow in the first half, `second` that of the second half, and
+// `limit` bounds both halves' rows counted from `first` / `second`.
+template <class C>
+__device__ __forceinline__ void weight_src(Src<C>& src, const uint8_t* base, int64_t row_bytes,
+                                           int64_t first, int64_t second, int64_t limit0,
+                                           int64_t limit1) {
+  constexpr int HALF = C::WR / 2;
+  src.wstep = (int64_t)C::STEP * row_bytes;
+  const int64_t n0 = limit0 > 0 ? (limit0 + C::STEP - 1) / C::STEP : 0;
+  const int64_t n1 = limit1 > 0 ? (limit1 + C::STEP - 1) / C::STEP : 0;
+  const int last0 = (int)(n0 < HALF ? n0 : HALF) - 1;
+  const int last1 = (int)(n1 < HALF ? n1 : HALF) - 1;
+  src.w[0] = last0 >= 0 ? base + first * row_bytes : base;
+  src.w[1] = last1 >= 0 ? base + second * row_bytes : base;
+  src.wlast[0] = last0;
+  src.wlast[1] = last1;
+}
+
 // Fused-MoE grouped GEMM (bf16 weights, MFMA bf16 -> f32).
 //   EPI 0: C = acc;  EPI 1: C[:, j] = silu(acc_gate_j) * acc_up_j.
-//   TF32: tokens are float32 rows (rounded to bf16 on the way to LDS).
-template <int BN, int BM, int EPI, bool TF32, int CDT>
-__global__ void __launch_bounds__(kThreads) moe_gemm_tile_kernel(MoeGemmArgs a) {
-  typedef Shape<BN, BM> S;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int rowinfo[BM];
+//   TF32: tokens are float32 rows (rounded to bf16 on the way to LDS; these
+//   tiles use the register-staged loop, the others the direct-to-LDS loop).
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+// Tile of the sorted list handled by this workgroup; false if none.
+struct MoeTile {
+  int blk, nt, e;
+  int64_t s0, c0;
+};
+
+template <int BN, int BM, int EPI>
+__device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   const int64_t ncols = EPI ? BN / 2 : BN;            // output columns per tile
   const int ntile = (int)((Nout + ncols - 1) / ncols);
   const int nblk = *a.total / BM;
   const int live = nblk * ntile;
-  if ((int)blockIdx.x >= live) return;
+  if ((int)blockIdx.x >= live) return false;
   const int L = xcd_remap((int)blockIdx.x, live);
-  const int blk = L / ntile, nt = L % ntile;
-  const int e = a.expert_ids[blk];
-  if (e < 0) return;
-  const int64_t s0 = (int64_t)blk * BM;
-  const int64_t c0 = (int64_t)nt * ncols;
+  t.blk = L / ntile;
+  t.nt = L % ntile;
+  t.e = a.expert_ids[t.blk];
+  t.s0 = (int64_t)t.blk * BM;
+  t.c0 = (int64_t)t.nt * ncols;
+  return t.e >= 0;
+}
 
-  if (tid < BM) {
-    const int p = a.sorted_ids[s0 + tid];
-    rowinfo[tid] = (p >= 0 && p < a.num_valid) ? p : -1;
-  }
-  __syncthreads();
-
-  const int lrow = tid >> 3;
-  const int64_t wrow_bytes = a.K * 2;
-  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)e * a.N * wrow_bytes;
-  Src<BN, BM> src;
-  constexpr int HALF = S::WR / 2;
-  src.wstep = 32 * wrow_bytes;
-  src.wmask = 0u;
+// Local weight row of tile row r (0 <= r < BN) -> global row of expert e,
+// or -1 past the matrix.  With the SiLU epilogue rows [0, BN/2) are gate
+// rows c0 + r and rows [BN/2, BN) the up rows of the same columns.
+template <int BN, int EPI>
+__device__ __forceinline__ int64_t moe_weight_row(const MoeGemmArgs& a, int64_t c0, int r) {
   if (EPI) {
-    src.w0 = Bw + (c0 + lrow) * wrow_bytes;            // gate row c0 + lrow
-    src.w1 = Bw + (Nout + c0 + lrow) * wrow_bytes;     // up row
-#pragma unroll
-    for (int i = 0; i < S::WR; ++i)
-      if (c0 + lrow + 32 * (i % HALF) < Nout) src.wmask |= 1u << i;
-  } else {
-    src.w0 = Bw + (c0 + lrow) * wrow_bytes;
-    src.w1 = src.w0 + HALF * src.wstep;
-#pragma unroll
-    for (int i = 0; i < S::WR; ++i)
-      if (c0 + lrow + 32 * i < a.N) src.wmask |= 1u << i;
+    const int64_t Nout = a.N / 2;
+    const int64_t hcol = c0 + (r < BN / 2 ? r : r - BN / 2);
+    if (hcol >= Nout) return -1;
+    return r < BN / 2 ? hcol : Nout + hcol;
   }
-  src.abase = reinterpret_cast<const uint8_t*>(a.A);
-  src.arow_bytes = a.lda * (TF32 ? 4 : 2);
-#pragma unroll
-  for (int i = 0; i < S::TR; ++i) {
-    const int r = lrow + 32 * i;
-    const int p = rowinfo[r];
-    src.trow[i] = p < 0 ? -1 : (a.a_rows == 0 ? p / a.a_row_div : (int)(s0 + r));
-  }
+  const int64_t n = c0 + r;
+  return n < a.N ? n : -1;
+}
 
-  int wrow[S::RB];
+// First local weight row of each of this wave's 32-row blocks; with the SiLU
+// epilogue block rb < RB/2 holds gate rows, block rb + RB/2 the matching up rows.
+template <int BN, int WN, int RB, int EPI>
+__device__ __forceinline__ void wave_rows(int wn, int (&wrow)[RB]) {
+  constexpr int WROWS = BN / WN;
 #pragma unroll
-  for (int rb = 0; rb < S::RB; ++rb)
-    wrow[rb] = EPI ? ((rb < S::RB / 2) ? wn * (BN / 4) + rb * 32
-                                       : BN / 2 + wn * (BN / 4) + (rb - S::RB / 2) * 32)
-                   : wn * (BN / 2) + rb * 32;
-  const int tcol0 = wm * (BM / 2);
-  const uint32_t active = active_blocks<S::CB>(rowinfo, tcol0);
+  for (int rb = 0; rb < RB; ++rb)
+    wrow[rb] = EPI ? ((rb < RB / 2) ? wn * (WROWS / 2) + rb * 32
+                                    : BN / 2 + wn * (WROWS / 2) + (rb - RB / 2) * 32)
+                   : wn * WROWS + rb * 32;
+}
 
-  f32x16_t acc[S::RB][S::CB];
-#pragma unroll
-  for (int rb = 0; rb < S::RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < S::CB; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
-
-  mainloop<BN, BM, 0, TF32>(smem, src, wrow_bytes, wrow, tcol0, active, acc);
-
-  // Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and,
-  // for g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
+// Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and, for
+// g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
+template <int RB, int CB, int EPI, int CDT>
+__device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile& t,
+                                             const int* rowinfo, const int (&wrow)[RB],
+                                             int tcol0, const f32x16_t (&acc)[RB][CB]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t Nout = EPI ? a.N / 2 : a.N;
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
   constexpr int ce = ElemBytes<CDT>::value;
   const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int cb = 0; cb < S::CB; ++cb) {
-    if (!((active >> cb) & 1u)) continue;
+  for (int cb = 0; cb < CB; ++cb) {
     const int trow = tcol0 + cb * 32 + (lane & 31);
     const int p = rowinfo[trow];
     if (p < 0) continue;
-    const int64_t crow = (a.c_rows == 0) ? (int64_t)p : s0 + trow;
+    const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + trow;
     const float w = a.topk_weights ? a.topk_weights[p] : 1.0f;
     uint8_t* rowp = Cb + crow * a.ldc * ce;
     if (EPI) {
 #pragma unroll
-      for (int j = 0; j < S::RB / 2; ++j) {
-        const f32x16_t gt = acc[j][cb], up = acc[j + S::RB / 2][cb];
+      for (int j = 0; j < RB / 2; ++j) {
+        const f32x16_t gt = acc[j][cb], up = acc[j + RB / 2][cb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t col = c0 + wn * (BN / 4) + j * 32 + 8 * g + rsub;
+          const int64_t col = t.c0 + wrow[j] + 8 * g + rsub;
           if (col < Nout)
             store4<CDT>(rowp + col * ce, silu_f32(gt[4 * g]) * up[4 * g] * w,
                         silu_f32(gt[4 * g + 1]) * up[4 * g + 1] * w,
@@ -316,11 +514,11 @@ __global__ void __launch_bounds__(kThreads) moe_gemm_tile_kernel(MoeGemmArgs a) 
       }
     } else {
 #pragma unroll
-      for (int rb = 0; rb < S::RB; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         const f32x16_t v = acc[rb][cb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t col = c0 + wrow[rb] + 8 * g + rsub;
+          const int64_t col = t.c0 + wrow[rb] + 8 * g + rsub;
           if (col < a.N)
             store4<CDT>(rowp + col * ce, v[4 * g] * w, v[4 * g + 1] * w, v[4 * g + 2] * w,
                         v[4 * g + 3] * w);
@@ -330,21 +528,126 @@ __global__ void __launch_bounds__(kThreads) moe_gemm_tile_kernel(MoeGemmArgs a) 
   }
 }
 
+template <int BM>
+__device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile& t, int* rowinfo) {
+  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+    const int p = a.sorted_ids[t.s0 + r];
+    rowinfo[r] = (p >= 0 && p < a.num_valid) ? p : -1;
+  }
+  __syncthreads();
+}
+
+// A row feeding tile token row r; placeholder rows read the tile's first row
+// (valid whenever row 0 is), which only reaches masked outputs.
+__device__ __forceinline__ int moe_token_row(const MoeGemmArgs& a, const MoeTile& t,
+                                             const int* rowinfo, int r) {
+  const int p = rowinfo[r];
+  if (p < 0) {
+    const int p0 = rowinfo[0];
+    return p0 < 0 ? 0 : (a.a_rows == 0 ? p0 / a.a_row_div : (int)t.s0);
+  }
+  return a.a_rows == 0 ? p / a.a_row_div : (int)(t.s0 + r);
+}
+
+// Register-staged variant (float32 tokens).
+template <class C, int EPI, int CDT>
+__global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a) {
+  typedef C S;
+  constexpr int BN = C::BN, BM = C::BM;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[BM];
+  MoeTile t;
+  if (!moe_tile<BN, BM, EPI>(a, t)) return;
+  load_rowinfo<BM>(a, t, rowinfo);
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const int lrow = tid >> 3;
+  const int64_t Nout = EPI ? a.N / 2 : a.N;
+  const int64_t wrow_bytes = a.K * 2;
+  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)t.e * a.N * wrow_bytes;
+  Src<C> src;
+  if (EPI)   // first half: gate rows c0 + ..., second half: the matching up rows
+    weight_src<C>(src, Bw, wrow_bytes, t.c0 + lrow, Nout + t.c0 + lrow, Nout - t.c0 - lrow,
+                  Nout - t.c0 - lrow);
+  else
+    weight_src<C>(src, Bw, wrow_bytes, t.c0 + lrow, t.c0 + BN / 2 + lrow, a.N - t.c0 - lrow,
+                  a.N - t.c0 - BN / 2 - lrow);
+  src.abase = reinterpret_cast<const uint8_t*>(a.A);
+  src.arow_bytes = a.lda * 4;
+#pragma unroll
+  for (int i = 0; i < S::TR; ++i) src.trow[i] = moe_token_row(a, t, rowinfo, lrow + S::STEP * i);
+
+  int wrow[S::RB];
+  wave_rows<BN, C::WN, S::RB, EPI>(wn, wrow);
+  const int tcol0 = wm * (BM / C::WM);
+  f32x16_t acc[S::RB][S::CB];
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+  mainloop<C, 0, true>(smem, src, wrow_bytes, wrow, tcol0, acc);
+  moe_epilogue<S::RB, S::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
+}
+
+// Direct-to-LDS variant (bf16 tokens).
+template <class C, int EPI, int CDT>
+__global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a) {
+  constexpr int BN = C::BN, BM = C::BM;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[BM];
+  MoeTile t;
+  if (!moe_tile<BN, BM, EPI>(a, t)) return;
+  load_rowinfo<BM>(a, t, rowinfo);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const int64_t wrow_bytes = a.K * 2;
+  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)t.e * a.N * wrow_bytes;
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
+  const int64_t arow_bytes = a.lda * 2;
+  const uint8_t* rowp[C::NI];
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    const int r = (wave * C::NI + j) * 16 + (lane >> 2);
+    if (r < BN) {
+      const int64_t g = moe_weight_row<BN, EPI>(a, t.c0, r);
+      rowp[j] = Bw + (g < 0 ? 0 : g) * wrow_bytes;        // past the matrix: row 0
+    } else {
+      rowp[j] = Ab + (int64_t)moe_token_row(a, t, rowinfo, r - BN) * arow_bytes;
+    }
+  }
+  int wrow[C::RB];
+  wave_rows<BN, C::WN, C::RB, EPI>(wn, wrow);
+  const int tcol0 = wm * (BM / C::WM);
+  f32x16_t acc[C::RB][C::CB];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+  mainloop_dma<C, 0>(smem, rowp, wrow_bytes, wrow, tcol0, acc);
+  moe_epilogue<C::RB, C::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
+}
+
 // ---------------------------------------------------------------------------
 // INT8 GMM: rows [off[e], off[e+1]) of X use W[e]; fp16 output.
-constexpr int kGmmBN = 256;
-constexpr int kGmmBM = 128;
+typedef DmaCfg<256, 128, 4> GmmCfg;
 
-__global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
-  constexpr int BN = kGmmBN, BM = kGmmBM;
-  typedef Shape<BN, BM> S;
+__global__ void __launch_bounds__(GmmCfg::THREADS) gmm_i8_tile_kernel(GmmI8Args a) {
+  typedef GmmCfg C;
+  typedef C S;
+  constexpr int BN = C::BN, BM = C::BM, NT = C::THREADS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int tprefix[kMaxGmmExperts + 1];   // m-tiles before expert e
-  __shared__ int scan_buf[kThreads];
+  __shared__ int scan_buf[NT];
   __shared__ int rowinfo[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % C::WN, wm = wave / C::WN;
   const int E = a.E;
   const int M = (int)a.M;
   const int ntile = (int)((a.N + BN - 1) / BN);
@@ -354,7 +657,7 @@ __global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
     int v = a.offsets[e];
     return v < 0 ? 0 : (v > M ? M : v);
   };
-  const int per = (E + kThreads - 1) / kThreads;   // <= 4
+  const int per = (E + NT - 1) / NT;   // <= 4
   int cnt[4] = {0, 0, 0, 0};
   int local = 0;
 #pragma unroll
@@ -370,7 +673,7 @@ __global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
   }
   scan_buf[tid] = local;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     const int add = tid >= off ? scan_buf[tid - off] : 0;
     __syncthreads();
     scan_buf[tid] += add;
@@ -386,7 +689,7 @@ __global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
         run += cnt[j];
       }
     }
-    if (tid == kThreads - 1) tprefix[E] = scan_buf[tid];
+    if (tid == NT - 1) tprefix[E] = scan_buf[tid];
   }
   __syncthreads();
   const int total_mt = tprefix[E];
@@ -412,26 +715,25 @@ __global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
   if (tid < BM) rowinfo[tid] = (row0 + tid < row_hi) ? row0 + tid : -1;
   __syncthreads();
 
-  const int lrow = tid >> 3;
-  Src<BN, BM> src;
-  constexpr int HALF = S::WR / 2;
-  src.wstep = 32 * a.K;
-  src.w0 = reinterpret_cast<const uint8_t*>(a.W) + ((int64_t)e * a.N + n0 + lrow) * a.K;
-  src.w1 = src.w0 + HALF * src.wstep;
-  src.wmask = 0u;
+  const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W) + (int64_t)e * a.N * a.K;
+  const uint8_t* rowp[C::NI];
 #pragma unroll
-  for (int i = 0; i < S::WR; ++i)
-    if (n0 + lrow + 32 * i < a.N) src.wmask |= 1u << i;
-  src.abase = reinterpret_cast<const uint8_t*>(a.X);
-  src.arow_bytes = a.K;
-#pragma unroll
-  for (int i = 0; i < S::TR; ++i) src.trow[i] = rowinfo[lrow + 32 * i];
+  for (int j = 0; j < C::NI; ++j) {
+    const int r = (wave * C::NI + j) * 16 + (lane >> 2);
+    if (r < BN) {
+      const int64_t n = n0 + r;
+      rowp[j] = Wb + (n < a.N ? n : 0) * a.K;
+    } else {
+      const int m = rowinfo[r - BN];
+      rowp[j] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)(m < 0 ? row_lo : m) * a.K;
+    }
+  }
 
+  constexpr int WROWS = BN / C::WN;
   int wrow[S::RB];
 #pragma unroll
-  for (int rb = 0; rb < S::RB; ++rb) wrow[rb] = wn * (BN / 2) + rb * 32;
-  const int tcol0 = wm * (BM / 2);
-  const uint32_t active = active_blocks<S::CB>(rowinfo, tcol0);
+  for (int rb = 0; rb < S::RB; ++rb) wrow[rb] = wn * WROWS + rb * 32;
+  const int tcol0 = wm * (BM / C::WM);
 
   i32x16_t acc[S::RB][S::CB];
 #pragma unroll
@@ -441,13 +743,12 @@ __global__ void __launch_bounds__(kThreads) gmm_i8_tile_kernel(GmmI8Args a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
 
-  mainloop<BN, BM, 1, false>(smem, src, a.K, wrow, tcol0, active, acc);
+  mainloop_dma<C, 1>(smem, rowp, a.K, wrow, tcol0, acc);
 
   uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
   const int rsub = 4 * (lane >> 5);
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) {
-    if (!((active >> cb) & 1u)) continue;
     const int m = rowinfo[tcol0 + cb * 32 + (lane & 31)];
     if (m < 0) continue;
     const float sx = a.sx[m];
@@ -476,41 +777,57 @@ hipError_t ensure_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int BN, int BM, int EPI, bool TF32, int CDT>
+template <class C, int EPI, bool TF32, int CDT>
 hipError_t launch_tile_t(const MoeGemmArgs& a, hipStream_t stream) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
-  const int64_t ncols = EPI ? BN / 2 : BN;
+  const int64_t ncols = EPI ? C::BN / 2 : C::BN;
   const int64_t ntile = (Nout + ncols - 1) / ncols;
-  const int64_t grid = (a.max_padded / BM) * ntile;
+  const int64_t grid = (a.max_padded / C::BM) * ntile;
   if (grid == 0) return hipSuccess;
-  auto k = moe_gemm_tile_kernel<BN, BM, EPI, TF32, CDT>;
-  constexpr size_t lds = Shape<BN, BM>::kBytes;
+  void (*k)(MoeGemmArgs);
+  if constexpr (TF32) k = moe_gemm_tile_kernel<C, EPI, CDT>;
+  else k = moe_gemm_dma_kernel<C, EPI, CDT>;
+  constexpr size_t lds = C::kBytes;
   const hipError_t st = ensure_lds(k, lds);
   if (st != hipSuccess) return st;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int BN, int BM, int EPI, bool TF32>
+template <class C, int EPI, bool TF32>
 hipError_t launch_tile_c(const MoeGemmArgs& a, hipStream_t s) {
   switch (a.c_dtype) {
-    case 0: return launch_tile_t<BN, BM, EPI, TF32, 0>(a, s);
-    case 1: return launch_tile_t<BN, BM, EPI, TF32, 1>(a, s);
-    default: return launch_tile_t<BN, BM, EPI, TF32, 2>(a, s);
+    case 0: return launch_tile_t<C, EPI, TF32, 0>(a, s);
+    case 1: return launch_tile_t<C, EPI, TF32, 1>(a, s);
+    default: return launch_tile_t<C, EPI, TF32, 2>(a, s);
   }
 }
 
+// Tile configurations per block size.  bf16 tokens: direct-to-LDS loop,
+// BN x BM with NSTAGE LDS stages; float32 tokens: register-staged loop.
+template <int BM> struct TileFor;
+template <> struct TileFor<64> {
+  typedef DmaCfg<256, 64, 4> Dma;
+  typedef Cfg<256, 64, 2, 2, MOE_TILE_NBUF> Regs;
+};
+template <> struct TileFor<128> {
+  typedef DmaCfg<256, 128, 4> Dma;
+  typedef Cfg<256, 128, 2, 2, MOE_TILE_NBUF> Regs;
+};
+template <> struct TileFor<256> {
+  typedef DmaCfg<256, 256, 4, MOE_T256_WN, MOE_T256_WM> Dma;   // 2 waves per SIMD
+};
+
 template <int BM>
 hipError_t launch_tile_bm(const MoeGemmArgs& a, hipStream_t s) {
-  constexpr int BN = 256;
-  const bool tf32 = a.a_dtype == 0;
+  typedef typename TileFor<BM>::Dma D;
+  if (a.a_dtype != 0)
+    return a.epilogue ? launch_tile_c<D, 1, false>(a, s) : launch_tile_c<D, 0, false>(a, s);
   if constexpr (BM > 128) {
-    if (tf32) return hipErrorInvalidValue;   // rejected by the ABI layer beforehand
-    return a.epilogue ? launch_tile_c<BN, BM, 1, false>(a, s) : launch_tile_c<BN, BM, 0, false>(a, s);
+    return hipErrorInvalidValue;   // rejected by the ABI layer beforehand
   } else {
-    if (a.epilogue)
-      return tf32 ? launch_tile_c<BN, BM, 1, true>(a, s) : launch_tile_c<BN, BM, 1, false>(a, s);
-    return tf32 ? launch_tile_c<BN, BM, 0, true>(a, s) : launch_tile_c<BN, BM, 0, false>(a, s);
+    typedef typename TileFor<BM>::Regs R;
+    return a.epilogue ? launch_tile_c<R, 1, true>(a, s) : launch_tile_c<R, 0, true>(a, s);
   }
 }
 
@@ -525,16 +842,16 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream) {
-  const int ntile = (int)((a.N + kGmmBN - 1) / kGmmBN);
+  typedef GmmCfg C;
+  const int ntile = (int)((a.N + C::BN - 1) / C::BN);
   // Upper bound of m-tiles: every non-empty expert adds at most one partial tile.
-  const int64_t mt_max = (a.M + kGmmBM - 1) / kGmmBM + a.E;
+  const int64_t mt_max = (a.M + C::BM - 1) / C::BM + a.E;
   const int64_t grid = mt_max * ntile;
   if (grid == 0 || a.M == 0) return hipSuccess;
-  typedef Shape<kGmmBN, kGmmBM> S;
-  const hipError_t st = ensure_lds(gmm_i8_tile_kernel, S::kBytes);
+  constexpr size_t lds = C::kBytes;
+  const hipError_t st = ensure_lds(gmm_i8_tile_kernel, lds);
   if (st != hipSuccess) return st;
-  hipLaunchKernelGGL(gmm_i8_tile_kernel, dim3((unsigned)grid), dim3(kThreads), S::kBytes, stream,
-                     a);
+  hipLaunchKernelGGL(gmm_i8_tile_kernel, dim3((unsigned)grid), dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -216,6 +216,25 @@ def test_quantizer_closed_form():
     assert q.tolist() == [[64, -127, 32]]
 
 
+def test_per_token_quantizer_closed_form():
+    """[GMM] §3.2 activation side: one scale per row, amax maps to +-127,
+    halves round to even, an all-zero row gets scale 1 and codes 0, and the
+    reconstruction error of every element is at most half a step."""
+    x = np.array([[254.0, 5.0, -3.0, 1.0],        # scale 2: 127, 2.5->2, -1.5->-2, 0.5->0
+                  [0.0, 0.0, 0.0, 0.0],
+                  [-0.5, 0.25, 0.125, 0.0]])      # scale 0.5/127
+    q, s = oracle.quantize_per_token(x)
+    assert s.tolist()[:2] == [2.0, 1.0]
+    np.testing.assert_allclose(s[2], 0.5 / 127.0)
+    assert q.tolist() == [[127, 2, -2, 0], [0, 0, 0, 0], [-127, 64, 32, 0]]
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((16, 40))
+    q, s = oracle.quantize_per_token(x)
+    assert q.dtype == np.int8 and s.shape == (16,)
+    assert (np.abs(q).max(axis=1) == 127).all()
+    assert (np.abs(q.astype(np.float64) * s[:, None] - x) <= 0.5 * s[:, None] + 1e-15).all()
+
+
 def test_gmm_int8_exactly_representable():
     """Weights and activations that are exactly q * scale: the int8 GMM
     equals the float GMM of the dequantised tensors."""

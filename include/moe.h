@@ -68,6 +68,9 @@ extern "C" {
 #define MOE_ROWS_PAIR   0   /* row index = pair index (token*topk + k)      */
 #define MOE_ROWS_SORTED 1   /* row index = position in sorted_token_ids     */
 
+#define MOE_WEIGHTS_PLAIN  0   /* [E, N, K], K contiguous                    */
+#define MOE_WEIGHTS_PACKED 1   /* written by moe_pack_weights (see there)    */
+
 /* Largest supported sizes (validated; MOE_ERR_SHAPE beyond them). */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK    64
@@ -139,6 +142,36 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
                          int32_t* expert_ids, int32_t* num_tokens_post_padded,
                          int64_t max_padded, void* stream);
 
+/* ---- packed expert weights --------------------------------------------
+ * moe_pack_weights: one-time re-layout of bf16 expert weights [E, N, K] for
+ * the MFMA tile kernels (block_m 64, 128, 256).  The weights and every
+ * result computed from them are unchanged; only the byte order differs.
+ * In the plain layout each K step of a tile reads 64 bytes from each of 256
+ * rows that lie K*2 bytes apart; packed, the same step is one contiguous
+ * 16 KiB block, which HBM serves far faster.
+ *
+ * Layout.  Each expert's rows are cut into tiles of 256 rows:
+ *   epilogue MOE_EPILOGUE_NONE:     tile t holds rows 256t .. 256t+255;
+ *   epilogue MOE_EPILOGUE_SILU_MUL: tile t holds gate rows 128t .. 128t+127
+ *                                   and then the up rows N/2 + 128t ..
+ *                                   (the pairs the SiLU*up epilogue joins).
+ * K is cut into stages of 32 elements (64 bytes).  Block (e, t, s) is 16 KiB
+ * at byte offset ((e * NT + t) * KS + s) * 16384 with NT tiles per expert
+ * and KS = ceil(K / 32).  Inside a block, the 16-byte chunk c (elements
+ * 8c .. 8c+7 of the stage) of tile row r is at r * 64 + 16 * (c ^ ((r >> 2) & 3)).
+ * Rows past the matrix and elements past K are zero.
+ *
+ *   w         [E, N, K] bf16 (read only).
+ *   epilogue  the epilogue of the GEMM that will use the packed weights.
+ *   packed    output, at least moe_packed_weights_size(E, N, K, epilogue) bytes.
+ * Requirements: as moe_grouped_gemm for N and K; w and packed 16-byte aligned.
+ * Errors: NULLs, bad sizes or epilogue, packed_bytes too small.
+ */
+MOE_API size_t moe_packed_weights_size(int32_t E, int64_t N, int64_t K, int32_t epilogue);
+
+MOE_API int moe_pack_weights(const void* w, int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                     void* packed, size_t packed_bytes, void* stream);
+
 /* ---- grouped GEMM ------------------------------------------------------
  * moe_grouped_gemm: [MSG] fused MoE, fused_moe_kernel, with the gathered
  * weight never materialised ([P1] 01): for every block b of block_m entries
@@ -156,7 +189,9 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
  *
  *   A        rows of K elements, row stride lda elements; a_dtype BF16 or
  *            F32 (F32 rows are rounded to bf16 on load).
- *   B        [E, N, K] bf16, K contiguous.
+ *   B        [E, N, K] bf16, K contiguous (b_layout MOE_WEIGHTS_PLAIN), or
+ *            written by moe_pack_weights with the same E, N, K and epilogue
+ *            (MOE_WEIGHTS_PACKED; block_m 64, 128 or 256 and bf16 A only).
  *   C        row stride ldc elements; c_dtype F32, BF16 or F16.
  *   sorted_token_ids / expert_ids / num_tokens_post_padded: as written by
  *            moe_align_block_size with the same block_m; max_padded is the
@@ -169,7 +204,7 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
  * 16-byte aligned.
  */
 MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows,
-                     int32_t a_row_div, const void* B, int32_t E, int64_t N,
+                     int32_t a_row_div, const void* B, int32_t b_layout, int32_t E, int64_t N,
                      int64_t K, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids,
                      const int32_t* num_tokens_post_padded, int64_t max_padded,
@@ -188,24 +223,30 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
  *   gating   [T, E] f32 logits.
  *   w1       [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)).
  *   w2       [E, H, I] bf16.
+ *   w_layout MOE_WEIGHTS_PLAIN, or MOE_WEIGHTS_PACKED: w1 packed with
+ *            MOE_EPILOGUE_SILU_MUL and w2 with MOE_EPILOGUE_NONE by
+ *            moe_pack_weights (needs bf16 x; block_m 64, 128 or 256).
  *   topk_weights_out [T, topk] f32, topk_ids_out [T, topk] int32: optional
  *            (NULL = kept in the workspace only).
  *   block_m  0 = chosen from the average pairs per expert (16, 32, 64, 128,
- *            or 256 for bf16 x with at least 192 pairs per expert);
- *            otherwise one of the moe_grouped_gemm block sizes.
+ *            or 256 for bf16 x with at least 192 pairs per expert; at
+ *            least 64 with packed weights); otherwise one of the
+ *            moe_grouped_gemm block sizes.
  *   ws       device workspace of at least moe_forward_workspace_size(...)
  *            bytes for the same arguments (256-byte aligned).
  * Requirements: H % 16 == 0, I % 16 == 0, plus moe_route's.
  */
 /* Block size moe_forward uses when called with block_m = 0 (the choice is a
- * pure function of the shape and x's dtype); -1 on invalid arguments. */
-MOE_API int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype);
+ * pure function of the shape, x's dtype and the weight layout); -1 on
+ * invalid arguments. */
+MOE_API int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype,
+                                    int32_t w_layout);
 
 MOE_API size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
                                   int32_t topk, int32_t block_m);
 
 MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
-                const void* w1, const void* w2, int64_t T, int32_t H, int32_t I,
+                const void* w1, const void* w2, int32_t w_layout, int64_t T, int32_t H, int32_t I,
                 int32_t E, int32_t topk, int32_t num_expert_group,
                 int32_t topk_group, int32_t scoring, int32_t renormalize,
                 float routed_scaling_factor, int32_t block_m, void* out,

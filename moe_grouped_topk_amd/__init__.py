@@ -16,6 +16,7 @@ __all__ = [
     "MoeError", "LIB_PATH", "lib", "moe_status_string", "moe_route",
     "moe_align_max_padded", "moe_align_block_size", "moe_grouped_gemm",
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
+    "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -25,6 +26,7 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 SCORING = {"softmax": 0, "sigmoid": 1}
 EPILOGUE = {"none": 0, "silu_mul": 1}
 ROWS = {"pair": 0, "sorted": 1}
+WEIGHTS = {"plain": 0, "packed": 1}
 
 
 class MoeError(RuntimeError):
@@ -37,7 +39,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libmoe.so is not built (%s); build it with "
-            "`python -m moe_grouped_topk_amd.build` or __graft_entry__.build()" % LIB_PATH)
+            "`python moe_grouped_topk_amd/build.py` or __graft_entry__.build()" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                              ctypes.c_float, ctypes.c_size_t)
@@ -49,15 +51,19 @@ def _load():
     L.moe_align_max_padded.restype = i64
     L.moe_align_block_size.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, vp]
     L.moe_align_block_size.restype = ctypes.c_int
-    L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i64, i64, vp, vp, vp, i64,
+    L.moe_packed_weights_size.argtypes = [i32, i64, i64, i32]
+    L.moe_packed_weights_size.restype = sz
+    L.moe_pack_weights.argtypes = [vp, i32, i64, i64, i32, vp, sz, vp]
+    L.moe_pack_weights.restype = ctypes.c_int
+    L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
                                    i32, i64, vp, i32, vp, i32, i64, i32, vp]
     L.moe_grouped_gemm.restype = ctypes.c_int
-    L.moe_forward_block_m.argtypes = [i64, i32, i32, i32]
+    L.moe_forward_block_m.argtypes = [i64, i32, i32, i32, i32]
     L.moe_forward_block_m.restype = i32
     L.moe_forward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     L.moe_forward_workspace_size.restype = sz
-    L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32,
-                              f32, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+                              i32, f32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
     L.gmm_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.gmm_int8.restype = ctypes.c_int
@@ -156,15 +162,59 @@ def moe_align_block_size(topk_ids, num_experts, block_m, sorted_token_ids=None,
     return sorted_token_ids, expert_ids, num_tokens_post_padded
 
 
+def moe_packed_weights_size(E, N, K, epilogue="none"):
+    return int(lib.moe_packed_weights_size(E, N, K, EPILOGUE[epilogue]))
+
+
+def moe_pack_weights(w, epilogue="none", packed=None, stream=None):
+    """Re-layout bf16 expert weights w [E, N, K] for the tile kernels (see
+    moe_pack_weights in include/moe.h).  Returns a PackedWeights holding the
+    packed bytes and the logical shape."""
+    torch = _torch()
+    E, N, K = w.shape
+    need = moe_packed_weights_size(E, N, K, epilogue)
+    if need == 0:
+        raise MoeError("moe_packed_weights_size", -2)
+    if packed is None:
+        packed = torch.empty(need, dtype=torch.uint8, device=w.device)
+    _check("moe_pack_weights", lib.moe_pack_weights(
+        _ptr(w, torch.bfloat16, "w"), E, N, K, EPILOGUE[epilogue],
+        _ptr(packed, torch.uint8, "packed"), packed.numel(), _stream(stream)))
+    return PackedWeights(packed, (E, N, K), epilogue)
+
+
+class PackedWeights:
+    """Packed expert weights: `data` (uint8 device tensor) plus the logical
+    [E, N, K] shape and the epilogue they were packed for."""
+
+    def __init__(self, data, shape, epilogue):
+        self.data, self.shape, self.epilogue = data, tuple(shape), epilogue
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def _weights(B, epilogue, name):
+    """(pointer, layout code, (E, N, K)) of plain or packed weights."""
+    torch = _torch()
+    if isinstance(B, PackedWeights):
+        if B.epilogue != epilogue:
+            raise ValueError("%s was packed for epilogue %r, used with %r" % (name, B.epilogue, epilogue))
+        return _ptr(B.data, torch.uint8, name), WEIGHTS["packed"], B.shape
+    return _ptr(B, torch.bfloat16, name), WEIGHTS["plain"], tuple(B.shape)
+
+
 def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded, block_m,
                      num_valid_pairs, a_rows="pair", a_row_div=1, topk_weights=None,
                      epilogue="none", C=None, c_dtype=None, c_rows="pair", c_num_rows=None,
                      stream=None):
-    """Sorted grouped GEMM.  A [rows, K] (bf16 or f32), B [E, N, K] bf16.
-    C is allocated as [c_num_rows or (num_valid_pairs if c_rows == 'pair'
-    else len(sorted_token_ids)), N or N/2] of c_dtype (default A's dtype)."""
+    """Sorted grouped GEMM.  A [rows, K] (bf16 or f32), B [E, N, K] bf16 or
+    PackedWeights (packed for the same epilogue).  C is allocated as
+    [c_num_rows or (num_valid_pairs if c_rows == 'pair' else
+    len(sorted_token_ids)), N or N/2] of c_dtype (default A's dtype)."""
     torch = _torch()
-    E, N, K = B.shape
+    b_ptr, b_layout, (E, N, K) = _weights(B, epilogue, "B")
     nout = N // 2 if epilogue == "silu_mul" else N
     if C is None:
         rows = c_num_rows if c_num_rows is not None else (
@@ -174,7 +224,7 @@ def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded,
         raise ValueError("expert_ids is smaller than sorted_token_ids / block_m")
     _check("moe_grouped_gemm", lib.moe_grouped_gemm(
         _ptr(A, None, "A"), _dtype_code(A), A.shape[-1], ROWS[a_rows], a_row_div,
-        _ptr(B, torch.bfloat16, "B"), E, N, K,
+        b_ptr, b_layout, E, N, K,
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
         _ptr(expert_ids, torch.int32, "expert_ids"),
         _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
@@ -184,9 +234,9 @@ def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded,
     return C
 
 
-def moe_forward_block_m(T, E, topk, x_dtype="bf16"):
+def moe_forward_block_m(T, E, topk, x_dtype="bf16", weights="plain"):
     """Block size moe_forward picks for block_m=0."""
-    return int(lib.moe_forward_block_m(T, E, topk, DTYPE[x_dtype]))
+    return int(lib.moe_forward_block_m(T, E, topk, DTYPE[x_dtype], WEIGHTS[weights]))
 
 
 def moe_forward_workspace_size(T, H, I, E, topk, block_m=0):
@@ -198,10 +248,14 @@ def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,
                 block_m=0, out=None, topk_weights_out=None, topk_ids_out=None,
                 workspace=None, stream=None):
     """Whole fused-MoE layer: x [T, H] (bf16 or f32), gating [T, E] f32,
-    w1 [E, 2I, H] bf16, w2 [E, H, I] bf16.  Returns out [T, H] in x's dtype."""
+    w1 [E, 2I, H] bf16, w2 [E, H, I] bf16, both plain or both PackedWeights
+    (w1 packed for 'silu_mul', w2 for 'none').  Returns out [T, H] in x's dtype."""
     torch = _torch()
     T, H = x.shape
-    E, twoI, _ = w1.shape
+    w1_ptr, l1, (E, twoI, _) = _weights(w1, "silu_mul", "w1")
+    w2_ptr, l2, _ = _weights(w2, "none", "w2")
+    if l1 != l2:
+        raise ValueError("w1 and w2 must both be plain or both packed")
     I = twoI // 2
     if out is None:
         out = torch.empty_like(x)
@@ -210,7 +264,7 @@ def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check("moe_forward", lib.moe_forward(
         _ptr(x, None, "x"), _dtype_code(x), _ptr(gating, torch.float32, "gating"),
-        _ptr(w1, torch.bfloat16, "w1"), _ptr(w2, torch.bfloat16, "w2"), T, H, I, E, topk,
+        w1_ptr, w2_ptr, l1, T, H, I, E, topk,
         num_expert_group, topk_group, SCORING[scoring], int(bool(renormalize)),
         float(routed_scaling_factor), block_m, _ptr(out, x.dtype, "out"),
         _ptr(topk_weights_out, torch.float32, "topk_weights_out"),

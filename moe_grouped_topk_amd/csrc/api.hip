@@ -51,6 +51,7 @@ int check_gemm(const moe::MoeGemmArgs& a) {
   if (!valid_block_m(a.block_m)) return MOE_ERR_CONFIG;
   if (a.block_m == 256 && a.a_dtype == MOE_DTYPE_F32) return MOE_ERR_CONFIG;
   if (a.a_rows == MOE_ROWS_PAIR && a.a_row_div < 1) return MOE_ERR_CONFIG;
+  if (a.b_packed && (a.block_m < 64 || a.a_dtype != MOE_DTYPE_BF16)) return MOE_ERR_CONFIG;
   if (a.E < 1 || a.N < 16 || a.K < 8 || a.K % 8 != 0) return MOE_ERR_SHAPE;
   const int64_t nout = a.epilogue == MOE_EPILOGUE_SILU_MUL ? a.N / 2 : a.N;
   if (a.epilogue == MOE_EPILOGUE_SILU_MUL ? (a.N % 32 != 0) : (a.N % 16 != 0)) return MOE_ERR_SHAPE;
@@ -73,14 +74,19 @@ int enqueue_gemm(const moe::MoeGemmArgs& a, hipStream_t s) {
   return hip_status(err);
 }
 
-int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype) {
+// Packed weights run on the tile kernels only (block_m >= 64); with few rows
+// per expert those skip the MFMAs of empty token columns and stream weights.
+int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
   const double avg = (double)T * topk / (double)E;   // pairs per expert
-  if (avg < 8.0) return 16;
-  if (avg < 24.0) return 32;
+  const bool packed = w_layout == MOE_WEIGHTS_PACKED;
+  if (avg < 8.0 && !packed) return 16;
+  if (avg < 24.0 && !packed) return 32;
   if (avg < 96.0) return 64;
   if (avg < 192.0 || x_dtype == MOE_DTYPE_F32) return 128;
   return 256;
 }
+
+bool valid_layout(int32_t l) { return l == MOE_WEIGHTS_PLAIN || l == MOE_WEIGHTS_PACKED; }
 
 struct ForwardLayout {
   size_t w, ids, sorted, eids, total, h, y, bytes;
@@ -89,9 +95,9 @@ struct ForwardLayout {
 };
 
 ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
-                             int32_t block_m, int32_t x_dtype) {
+                             int32_t block_m, int32_t x_dtype, int32_t w_layout) {
   ForwardLayout L{};
-  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype);
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, w_layout);
   const int64_t P = T * topk;
   L.max_padded = align_max_padded(P, E, L.block_m);
   size_t off = 0;
@@ -159,8 +165,29 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, 
                                       as_stream(stream)));
 }
 
+size_t moe_packed_weights_size(int32_t E, int64_t N, int64_t K, int32_t epilogue) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || N < 16 || K < 8 || K % 8 != 0) return 0;
+  if (epilogue != MOE_EPILOGUE_NONE && epilogue != MOE_EPILOGUE_SILU_MUL) return 0;
+  if (epilogue == MOE_EPILOGUE_SILU_MUL ? (N % 32 != 0) : (N % 16 != 0)) return 0;
+  const int silu = epilogue == MOE_EPILOGUE_SILU_MUL;
+  return (size_t)E * (size_t)moe::packed_tiles(N, silu) * (size_t)moe::packed_kstages(K, 2) *
+         (size_t)moe::kPackBlockBytes;
+}
+
+int moe_pack_weights(const void* w, int32_t E, int64_t N, int64_t K, int32_t epilogue, void* packed,
+                     size_t packed_bytes, void* stream) {
+  if (epilogue != MOE_EPILOGUE_NONE && epilogue != MOE_EPILOGUE_SILU_MUL) return MOE_ERR_CONFIG;
+  const size_t need = moe_packed_weights_size(E, N, K, epilogue);
+  if (need == 0) return MOE_ERR_SHAPE;
+  if (!w || !packed) return MOE_ERR_NULL;
+  if (packed_bytes < need) return MOE_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_pack_weights(w, E, N, K, epilogue == MOE_EPILOGUE_SILU_MUL, packed,
+                                             as_stream(stream)));
+}
+
 int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows, int32_t a_row_div,
-                     const void* B, int32_t E, int64_t N, int64_t K,
+                     const void* B, int32_t b_layout, int32_t E, int64_t N, int64_t K,
                      const int32_t* sorted_token_ids, const int32_t* expert_ids,
                      const int32_t* num_tokens_post_padded, int64_t max_padded, int32_t block_m,
                      int64_t num_valid_pairs, const float* topk_weights, int32_t epilogue, void* C,
@@ -169,7 +196,8 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   a.A = A; a.a_dtype = a_dtype; a.lda = lda; a.a_rows = a_rows;
   a.a_row_div = a_row_div < 1 ? 1 : a_row_div;
   if (a_rows == MOE_ROWS_PAIR && a_row_div < 1) return MOE_ERR_CONFIG;
-  a.B = B; a.E = E; a.N = N; a.K = K;
+  if (!valid_layout(b_layout)) return MOE_ERR_CONFIG;
+  a.B = B; a.b_packed = b_layout == MOE_WEIGHTS_PACKED; a.E = E; a.N = N; a.K = K;
   a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.total = num_tokens_post_padded;
   a.max_padded = max_padded; a.block_m = block_m; a.num_valid = num_valid_pairs;
   a.topk_weights = topk_weights; a.epilogue = epilogue;
@@ -179,37 +207,45 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   return enqueue_gemm(a, as_stream(stream));
 }
 
-int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype) {
+int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
   if (T < 0 || E < 1 || topk < 1) return -1;
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return -1;
-  return choose_block_m(T, E, topk, x_dtype);
+  if (!valid_layout(w_layout)) return -1;
+  return choose_block_m(T, E, topk, x_dtype, w_layout);
 }
 
 size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                   int32_t block_m) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
   if (block_m != 0 && !valid_block_m(block_m)) return 0;
-  // the automatic block size can depend on x's dtype: cover both
-  const size_t a = forward_layout(T, H, I, E, topk, block_m, MOE_DTYPE_BF16).bytes;
-  const size_t b = forward_layout(T, H, I, E, topk, block_m, MOE_DTYPE_F32).bytes;
-  return a > b ? a : b;
+  // the automatic block size can depend on x's dtype and the weight layout: cover all
+  size_t most = 0;
+  for (int32_t dt : {MOE_DTYPE_BF16, MOE_DTYPE_F32})
+    for (int32_t wl : {MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED}) {
+      const size_t b = forward_layout(T, H, I, E, topk, block_m, dt, wl).bytes;
+      most = b > most ? b : most;
+    }
+  return most;
 }
 
 int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void* w1, const void* w2,
-                int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                int32_t w_layout, int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                 int32_t num_expert_group, int32_t topk_group, int32_t scoring,
                 int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
                 float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
                 void* stream) {
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
+  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
+  const bool packed = w_layout == MOE_WEIGHTS_PACKED;
+  if (packed && (x_dtype != MOE_DTYPE_BF16 || (block_m != 0 && block_m < 64))) return MOE_ERR_CONFIG;
   if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0) return MOE_ERR_SHAPE;
   int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x || !gating || !w1 || !w2 || !out) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_SHAPE;
-  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype);
+  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype, w_layout);
   if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
   if (L.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
@@ -233,7 +269,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
 
   moe::MoeGemmArgs g1{};
   g1.A = x; g1.a_dtype = x_dtype; g1.lda = H; g1.a_rows = MOE_ROWS_PAIR; g1.a_row_div = topk;
-  g1.B = w1; g1.E = E; g1.N = 2 * (int64_t)I; g1.K = H;
+  g1.B = w1; g1.b_packed = packed; g1.E = E; g1.N = 2 * (int64_t)I; g1.K = H;
   g1.sorted_ids = sorted; g1.expert_ids = eids; g1.total = total; g1.max_padded = L.max_padded;
   g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
   g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I;

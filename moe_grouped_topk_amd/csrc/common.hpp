@@ -68,8 +68,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
+// z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each);
+// for z -> -inf the reciprocal of +inf gives 0, for z -> +inf it gives z.
 __device__ __forceinline__ float silu_f32(float z) {
-  return __fdividef(z, 1.0f + __expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 // Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).

@@ -15,13 +15,30 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
                         int64_t max_padded, hipStream_t stream);
 
+// Packed expert weights (see moe_pack_weights in moe.h): tiles of 256 rows,
+// K stages of 64 bytes, one 16 KiB block per (expert, tile, stage).
+constexpr int kPackRows = 256;
+constexpr int kPackStageBytes = 64;
+constexpr int kPackBlockBytes = kPackRows * kPackStageBytes;
+
+__host__ __device__ inline int64_t packed_tiles(int64_t N, int silu) {
+  return silu ? (N / 2 + kPackRows / 2 - 1) / (kPackRows / 2) : (N + kPackRows - 1) / kPackRows;
+}
+__host__ __device__ inline int64_t packed_kstages(int64_t K_elems, int elem_bytes) {
+  return (K_elems * elem_bytes + kPackStageBytes - 1) / kPackStageBytes;
+}
+
+hipError_t launch_pack_weights(const void* w, int E, int64_t N, int64_t K, int silu, void* packed,
+                               hipStream_t stream);
+
 struct MoeGemmArgs {
   const void* A;
   int a_dtype;            // 0 f32, 1 bf16
   int64_t lda;
   int a_rows;             // 0 pair, 1 sorted
   int a_row_div;
-  const void* B;          // [E, N, K] bf16
+  const void* B;          // [E, N, K] bf16, or packed (b_packed)
+  int b_packed;
   int E;
   int64_t N, K;
   const int32_t* sorted_ids;

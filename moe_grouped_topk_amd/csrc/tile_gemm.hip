@@ -314,9 +314,17 @@ struct DmaCfg {
 // row (wave * NI + j) * 16 + lane / 4); every row is at least 16 bytes long.
 // kbytes: bytes of K per row.  A partial last stage is handled by loading a
 // valid chunk and zeroing it in LDS afterwards.
-template <class C, int KIND>
+// Bit j of pk_mask (wave-uniform) marks rows held in the packed weight
+// layout: there rowp[j] already points at this lane's 16 bytes of stage 0 and
+// stage kt lies kt * kPackBlockBytes further (contiguous, pre-swizzled).
+//   NCB: this wave's token column blocks that hold at least one valid row
+//   (the valid rows of a tile come first); the others are neither read from
+//   LDS nor multiplied.  Every wave still issues its loads and meets every
+//   barrier.
+template <class C, int KIND, int NCB>
 __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
-                                             int64_t kbytes, const int (&wrow)[C::RB], int tcol0,
+                                             uint32_t pk_mask, int64_t kbytes,
+                                             const int (&wrow)[C::RB], int tcol0,
                                              typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t sbase = lds_addr(smem);
@@ -330,7 +338,9 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
     for (int j = 0; j < C::NI; ++j) {
       const int row = (wave * C::NI + j) * 16 + (lane >> 2);
       const int c = chunk_pos ^ ((row >> 2) & 3);            // chunk this lane fetches
-      const int64_t off = koff + c * 16 < kbytes ? koff + c * 16 : 0;   // past K: row start
+      const int64_t off = ((pk_mask >> j) & 1u)
+                              ? (int64_t)kt * kPackBlockBytes
+                              : (koff + c * 16 < kbytes ? koff + c * 16 : 0);   // past K: row start
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (uint32_t)((wave * C::NI + j) * 1024));
       dma16(m0, rowp[j] + off);
     }
@@ -357,16 +367,18 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
   auto load_frags = [&](int kt, int ks, u32x4_t (&af)[C::RB], u32x4_t (&bf)[C::CB]) {
     const uint8_t* st = smem + (kt % C::NSTAGE) * C::kStage + (lane & 31) * C::ROWB;
     const int pos = ((ks * 2 + (lane >> 5)) ^ swz) * 16;
+    if constexpr (NCB > 0) {
 #pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb)
-      af[rb] = *reinterpret_cast<const u32x4_t*>(st + wrow[rb] * C::ROWB + pos);
+      for (int rb = 0; rb < C::RB; ++rb)
+        af[rb] = *reinterpret_cast<const u32x4_t*>(st + wrow[rb] * C::ROWB + pos);
+    }
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
       bf[cb] = *reinterpret_cast<const u32x4_t*>(st + (C::BN + tcol0 + cb * 32) * C::ROWB + pos);
   };
   auto mfmas = [&](const u32x4_t (&af)[C::RB], const u32x4_t (&bf)[C::CB]) {
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf[cb], acc[rb][cb]);
   };
@@ -401,6 +413,28 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
     }
     mfmas(a1, b1);
   }
+}
+
+// Runs the K loop specialised for this wave's number of live column blocks
+// (wave-uniform), so the loop itself has no per-block branches.
+template <class C, int KIND>
+__device__ __forceinline__ void mainloop_dma_live(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
+                                                  uint32_t pk_mask, int64_t kbytes,
+                                                  const int (&wrow)[C::RB], int tcol0,
+                                                  int valid_rows,
+                                                  typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
+  int ncb = (valid_rows - tcol0 + 31) / 32;
+  ncb = __builtin_amdgcn_readfirstlane(ncb < 0 ? 0 : (ncb > C::CB ? C::CB : ncb));
+  pk_mask = __builtin_amdgcn_readfirstlane(pk_mask);
+  if constexpr (C::CB >= 4) {
+    if (ncb == 4) return mainloop_dma<C, KIND, 4>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 3) return mainloop_dma<C, KIND, 3>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  }
+  if constexpr (C::CB >= 2) {
+    if (ncb == 2) return mainloop_dma<C, KIND, 2>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  }
+  if (ncb == 1) return mainloop_dma<C, KIND, 1>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  mainloop_dma<C, KIND, 0>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -537,6 +571,17 @@ __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile
   __syncthreads();
 }
 
+// 1 + the last tile row holding a valid pair (0 if none); wave-uniform.
+template <int BM>
+__device__ __forceinline__ int live_rows(const int* rowinfo) {
+  const int lane = threadIdx.x & 63;
+  uint32_t last = 0;
+#pragma unroll
+  for (int r = lane; r < BM; r += 64)
+    if (rowinfo[r] >= 0) last = (uint32_t)(r + 1);
+  return (int)wave_max_u32(last);
+}
+
 // A row feeding tile token row r; placeholder rows read the tile's first row
 // (valid whenever row 0 is), which only reaches masked outputs.
 __device__ __forceinline__ int moe_token_row(const MoeGemmArgs& a, const MoeTile& t,
@@ -608,13 +653,25 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a)
   const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)t.e * a.N * wrow_bytes;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const int64_t arow_bytes = a.lda * 2;
+  // packed weights: this tile's blocks; BN == kPackRows and the tile's
+  // columns are the packed tile's (checked by the launcher)
+  const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
+                      ((int64_t)t.e * packed_tiles(a.N, EPI) + t.nt) *
+                          packed_kstages(a.K, 2) * kPackBlockBytes;
   const uint8_t* rowp[C::NI];
+  uint32_t pk_mask = 0;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
-    const int r = (wave * C::NI + j) * 16 + (lane >> 2);
-    if (r < BN) {
-      const int64_t g = moe_weight_row<BN, EPI>(a, t.c0, r);
-      rowp[j] = Bw + (g < 0 ? 0 : g) * wrow_bytes;        // past the matrix: row 0
+    const int q = wave * C::NI + j;            // 1 KiB piece of the stage: rows 16q .. 16q+15
+    const int r = q * 16 + (lane >> 2);
+    if (q < BN / 16) {
+      if (a.b_packed) {
+        rowp[j] = Bp + q * 1024 + lane * 16;
+        pk_mask |= 1u << j;
+      } else {
+        const int64_t g = moe_weight_row<BN, EPI>(a, t.c0, r);
+        rowp[j] = Bw + (g < 0 ? 0 : g) * wrow_bytes;      // past the matrix: row 0
+      }
     } else {
       rowp[j] = Ab + (int64_t)moe_token_row(a, t, rowinfo, r - BN) * arow_bytes;
     }
@@ -629,7 +686,8 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a)
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
-  mainloop_dma<C, 0>(smem, rowp, wrow_bytes, wrow, tcol0, acc);
+  mainloop_dma_live<C, 0>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0, live_rows<BM>(rowinfo),
+                          acc);
   moe_epilogue<C::RB, C::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
@@ -743,7 +801,8 @@ __global__ void __launch_bounds__(GmmCfg::THREADS) gmm_i8_tile_kernel(GmmI8Args 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
 
-  mainloop_dma<C, 1>(smem, rowp, a.K, wrow, tcol0, acc);
+  const int live_m = row_hi - row0 < BM ? row_hi - row0 : BM;
+  mainloop_dma_live<C, 1>(smem, rowp, 0u, a.K, wrow, tcol0, live_m, acc);
 
   uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
   const int rsub = 4 * (lane >> 5);
@@ -821,6 +880,8 @@ template <> struct TileFor<256> {
 template <int BM>
 hipError_t launch_tile_bm(const MoeGemmArgs& a, hipStream_t s) {
   typedef typename TileFor<BM>::Dma D;
+  static_assert(D::BN == kPackRows, "packed weights are cut into tiles of the kernel's BN rows");
+  if (a.b_packed && a.a_dtype == 0) return hipErrorInvalidValue;   // rejected by the ABI layer
   if (a.a_dtype != 0)
     return a.epilogue ? launch_tile_c<D, 1, false>(a, s) : launch_tile_c<D, 0, false>(a, s);
   if constexpr (BM > 128) {

@@ -25,11 +25,20 @@ def moe(dev):
     return m
 
 
-def _run(moe, cfg, d, block_m=0, dev=None):
+def _packed(moe, d):
+    """The layer's weights in the packed layout (cached in the input dict)."""
+    if "w1_packed" not in d:
+        d["w1_packed"] = moe.moe_pack_weights(d["w1"], "silu_mul")
+        d["w2_packed"] = moe.moe_pack_weights(d["w2"], "none")
+    return d["w1_packed"], d["w2_packed"]
+
+
+def _run(moe, cfg, d, block_m=0, dev=None, layout="plain"):
     T, E, K = cfg.T, cfg.E, cfg.topk
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
-    out = moe.moe_forward(d["x"], d["gating"], d["w1"], d["w2"], K, cfg.groups,
+    w1, w2 = _packed(moe, d) if layout == "packed" else (d["w1"], d["w2"])
+    out = moe.moe_forward(d["x"], d["gating"], w1, w2, K, cfg.groups,
                           cfg.topk_group, "softmax", cfg.renormalize, cfg.scale,
                           block_m=block_m, topk_weights_out=w, topk_ids_out=ids)
     torch.cuda.synchronize()
@@ -70,11 +79,13 @@ def test_tiny_layer(moe, dev, block_m):
     assert err <= BAR_BF16
 
 
-@pytest.mark.parametrize("block_m", [16, 128, 256])
-def test_tiny_layer_bf16_x(moe, dev, block_m):
+@pytest.mark.parametrize("block_m,layout", [(16, "plain"), (128, "plain"), (256, "plain"),
+                                            (0, "packed"), (64, "packed"), (128, "packed"),
+                                            (256, "packed")])
+def test_tiny_layer_bf16_x(moe, dev, block_m, layout):
     cfg = synth.CONFIGS["tiny"]
     d = layer_inputs(cfg, dev, x_dtype="bf16")
-    out, w, ids = _run(moe, cfg, d, block_m, dev)
+    out, w, ids = _run(moe, cfg, d, block_m, dev, layout)
     assert out.dtype == torch.bfloat16
     ref = oracle.moe_layer_expert_loop(d["x_host"], d["w1_host"], d["w2_host"],
                                        *oracle.grouped_topk(d["gating_host"], cfg.topk))
@@ -93,10 +104,16 @@ def test_single_expert_is_dense(moe, dev):
         assert max_abs_rel(_out_host(out), ref) <= BAR_BF16
 
 
-def test_prefill_layer_sampled(moe, dev):
+@pytest.fixture(scope="module")
+def prefill_inputs(dev):
+    return layer_inputs(synth.CONFIGS["prefill"], dev)
+
+
+@pytest.mark.parametrize("layout", ["plain", "packed"])
+def test_prefill_layer_sampled(moe, dev, prefill_inputs, layout):
     cfg = synth.CONFIGS["prefill"]
-    d = layer_inputs(cfg, dev)
-    out, w, ids = _run(moe, cfg, d, 0, dev)
+    d = prefill_inputs
+    out, w, ids = _run(moe, cfg, d, 0, dev, layout)
     check_routing(w, ids, d["gating_host"], cfg.topk, True, 1, 1, "softmax", 1.0)
     o = _out_host(out)
     assert np.isfinite(o).all()
@@ -123,6 +140,10 @@ def test_decode_layer_sampled(moe, dev, name):
     err = max_abs_rel(o[rows], ref)
     print("%s sampled err=%.3e" % (name, err))
     assert err <= BAR_BF16
-    # both weight-streaming and tile kernels agree on the same inputs
+    # both weight-streaming and tile kernels, plain and packed weights, agree
     out_t, _, _ = _run(moe, cfg, d, 64, dev)
     assert max_abs_rel(_out_host(out_t)[rows], ref) <= BAR_BF16
+    out_p, _, ids_p = _run(moe, cfg, d, 0, dev, "packed")
+    assert (ids_p == ids).all()
+    assert max_abs_rel(_out_host(out_p)[rows], ref) <= BAR_BF16
+    del d["w1_packed"], d["w2_packed"]

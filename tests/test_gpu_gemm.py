@@ -1,6 +1,7 @@
 """GPU parity of moe_grouped_gemm (both kernels: weight-streaming for
-block_m 16/32, MFMA tile for 64/128) against the oracle's sorted grouped
-GEMM.  The sorted metadata handed to both sides comes from the oracle."""
+block_m 16/32, MFMA tile for 64/128/256, plain and packed weights) against
+the oracle's sorted grouped GEMM.  The sorted metadata handed to both sides
+comes from the oracle."""
 
 import json
 import os
@@ -47,6 +48,56 @@ def _tol(c_dtype):
     return 1e-5 if c_dtype == torch.float32 else 8e-3
 
 
+def _weights(moe, Bb, dev, layout, epilogue):
+    """bf16 bits [E, N, K] -> device weights in the requested layout."""
+    w = bf16_dev(Bb, dev)
+    return moe.moe_pack_weights(w, epilogue) if layout == "packed" else w
+
+
+def _packed_reference(Wbits, silu):
+    """The packed layout of moe_pack_weights (include/moe.h), written out
+    element by element from its description: uint16 array of the packed size."""
+    E, N, K = Wbits.shape
+    NT = -(-(N // 2) // 128) if silu else -(-N // 256)
+    KS = -(-K // 32)
+    out = np.zeros((E, NT, KS, 256, 32), np.uint16)
+    for t in range(NT):
+        for r in range(256):
+            if silu:
+                col = t * 128 + (r % 128)
+                if col >= N // 2:
+                    continue
+                row = col if r < 128 else N // 2 + col
+            else:
+                row = t * 256 + r
+                if row >= N:
+                    continue
+            for ks in range(KS):
+                for c in range(4):
+                    k0 = ks * 32 + 8 * c
+                    if k0 >= K:
+                        continue
+                    pos = c ^ ((r >> 2) & 3)
+                    out[:, t, ks, r, 8 * pos:8 * pos + 8] = Wbits[:, row, k0:k0 + 8]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("silu,N,K", [(False, 80, 40), (False, 512, 64), (True, 96, 40),
+                                      (True, 288, 72)])
+def test_pack_layout(moe, dev, silu, N, K):
+    """Packed bytes equal the documented layout exactly (ragged N and K
+    included: padding is zero)."""
+    E = 3
+    rng = np.random.default_rng(N + K)
+    Wbits = rng.integers(0, 1 << 16, size=(E, N, K), dtype=np.uint16)
+    pw = moe.moe_pack_weights(bf16_dev(Wbits, dev), "silu_mul" if silu else "none")
+    torch.cuda.synchronize()
+    got = pw.data.cpu().numpy().view(np.uint16)
+    ref = _packed_reference(Wbits, silu)
+    assert got.shape == ref.shape
+    assert (got == ref).all()
+
+
 def test_p1_worked_example(moe, dev, golden_dir):
     """[P1] 03.3 example embedded in the kernel's alignment: K padded from 3
     to 8 and N from 2 to 16 with zeros (the extra columns stay zero)."""
@@ -58,14 +109,16 @@ def test_p1_worked_example(moe, dev, golden_dir):
     for e, v in enumerate(g["expert_fill"]):
         W[e, :2, :3] = v
     ids = np.array(g["topk_ids"])
-    for B in BLOCKS:
+    cases = [(B, "plain") for B in BLOCKS] + [(B, "packed") for B in BLOCKS if B >= 64]
+    for B, layout in cases:
         sb, eb, tot, *_ = _meta(moe, ids, 4, B, dev)
         C = moe.moe_grouped_gemm(
-            bf16_dev(synth.f32_to_bf16_bits(x), dev), bf16_dev(synth.f32_to_bf16_bits(W), dev),
+            bf16_dev(synth.f32_to_bf16_bits(x), dev),
+            _weights(moe, synth.f32_to_bf16_bits(W), dev, layout, "none"),
             sb, eb, tot, B, 4, a_rows="pair", a_row_div=2, c_dtype=torch.float32)
         torch.cuda.synchronize()
         out = C.cpu().numpy()
-        assert out[:, :2].reshape(2, 2, 2).tolist() == g["output"], B
+        assert out[:, :2].reshape(2, 2, 2).tolist() == g["output"], (B, layout)
         assert (out[:, 2:] == 0).all()
 
 
@@ -78,10 +131,13 @@ def _rand_case(seed, T, E, K_top, H, N, a_f32=False):
     return ids, A, Bw, wts
 
 
-@pytest.mark.parametrize("B", BLOCKS)
+CASES = [(B, "plain") for B in BLOCKS] + [(B, "packed") for B in BLOCKS if B >= 64]
+
+
+@pytest.mark.parametrize("B,layout", CASES)
 @pytest.mark.parametrize("epilogue", ["none", "silu_mul"])
 @pytest.mark.parametrize("c_dtype", [torch.float32, torch.bfloat16])
-def test_gemm_pair_rows(moe, dev, B, epilogue, c_dtype):
+def test_gemm_pair_rows(moe, dev, B, layout, epilogue, c_dtype):
     T, E, Kt, H, N = 97, 7, 3, 136, 96        # K tail (136 = 2 stages + 8), N not /128
     ids, A, Bw, wts = _rand_case(B + (epilogue == "none"), T, E, Kt, H, N)
     Ab, Bb = synth.f32_to_bf16_bits(A), synth.f32_to_bf16_bits(Bw)
@@ -90,8 +146,8 @@ def test_gemm_pair_rows(moe, dev, B, epilogue, c_dtype):
     w_dev = torch.from_numpy(wts).to(dev)
     C = torch.full((P, N // 2 if epilogue == "silu_mul" else N), float("nan"),
                    dtype=c_dtype, device=dev)
-    moe.moe_grouped_gemm(bf16_dev(Ab, dev), bf16_dev(Bb, dev), sb, eb, tot, B, P,
-                         a_rows="pair", a_row_div=Kt, topk_weights=w_dev, epilogue=epilogue,
+    moe.moe_grouped_gemm(bf16_dev(Ab, dev), _weights(moe, Bb, dev, layout, epilogue), sb, eb, tot,
+                         B, P, a_rows="pair", a_row_div=Kt, topk_weights=w_dev, epilogue=epilogue,
                          C=C, c_rows="pair")
     torch.cuda.synchronize()
     A64, B64 = oracle.bf16_bits_to_f64(Ab), oracle.bf16_bits_to_f64(Bb)
@@ -133,8 +189,8 @@ def test_gemm_sorted_rows_and_f32_input(moe, dev, B):
     assert np.isnan(got[total:]).all()
 
 
-@pytest.mark.parametrize("B", BLOCKS)
-def test_gemm_skewed_experts(moe, dev, B):
+@pytest.mark.parametrize("B,layout", CASES)
+def test_gemm_skewed_experts(moe, dev, B, layout):
     """One expert holds most pairs (many full blocks), others one pair or
     none: exercises full, partial and single-row blocks."""
     T, E, Kt, H, N = 300, 16, 1, 256, 128
@@ -145,12 +201,26 @@ def test_gemm_skewed_experts(moe, dev, B):
     Bw = synth.normal_f32((E, N, H), 9, 8, 0, 0.05)
     Ab, Bb = synth.f32_to_bf16_bits(A), synth.f32_to_bf16_bits(Bw)
     sb, eb, tot, s, e, total = _meta(moe, ids, E, B, dev)
-    C = moe.moe_grouped_gemm(bf16_dev(Ab, dev), bf16_dev(Bb, dev), sb, eb, tot, B, T,
-                             c_dtype=torch.float32)
+    C = moe.moe_grouped_gemm(bf16_dev(Ab, dev), _weights(moe, Bb, dev, layout, "none"), sb, eb,
+                             tot, B, T, c_dtype=torch.float32)
     torch.cuda.synchronize()
     ref, _ = oracle.grouped_gemm_sorted(oracle.bf16_bits_to_f64(Ab), oracle.bf16_bits_to_f64(Bb),
                                         s, e, B, T, 1)
     assert max_abs_rel(C.cpu().numpy(), ref) <= 1e-5
+
+
+def test_gemm_packed_rejects_f32_input_and_small_blocks(moe, dev):
+    ids = np.zeros((8, 1), np.int64)
+    A = torch.zeros((8, 64), dtype=torch.float32, device=dev)
+    pw = moe.moe_pack_weights(torch.zeros((1, 32, 64), dtype=torch.bfloat16, device=dev))
+    sb, eb, tot, *_ = _meta(moe, ids, 1, 64, dev)
+    with pytest.raises(moe.MoeError):
+        moe.moe_grouped_gemm(A, pw, sb, eb, tot, 64, 8)
+    sb, eb, tot, *_ = _meta(moe, ids, 1, 32, dev)
+    with pytest.raises(moe.MoeError):
+        moe.moe_grouped_gemm(A.to(torch.bfloat16), pw, sb, eb, tot, 32, 8)
+    with pytest.raises(ValueError):                       # packed for another epilogue
+        moe.moe_grouped_gemm(A.to(torch.bfloat16), pw, sb, eb, tot, 64, 8, epilogue="silu_mul")
 
 
 def test_gemm_f32_input_rejected_at_256(moe, dev):

@@ -96,6 +96,10 @@ def test_workspace_size(mod):
     assert ws >= 4 * P * 2 + 4 * maxp + 2 * maxp * 768 + 4 * P * 2048
     assert ws % 256 == 0
     assert mod.lib.moe_forward_workspace_size(16, 7168, 2048, 256, 8, 48) == 0   # bad block_m
+    # covers the packed-weight choice of block size (at least 64) too
+    P = 16 * 8
+    assert mod.moe_forward_workspace_size(16, 7168, 2048, 256, 8) >= \
+        2 * mod.moe_align_max_padded(P, 256, 64) * 2048
 
 
 # ---- validation error paths (no HIP call is reached) -----------------------
@@ -133,16 +137,16 @@ def test_align_validation(mod):
 def test_gemm_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)
-    base = dict(A=f, a_dtype=1, lda=128, a_rows=0, a_row_div=2, B=f, E=8, N=256, K=128,
+    base = dict(A=f, a_dtype=1, lda=128, a_rows=0, a_row_div=2, B=f, bl=0, E=8, N=256, K=128,
                 s=f, e=f, tot=f, maxp=512, bm=64, nv=128, w=None, epi=1, C=f, c_dtype=1,
                 ldc=128, c_rows=1)
 
     def call(**kw):
         a = dict(base, **kw)
         return L.moe_grouped_gemm(a["A"], a["a_dtype"], a["lda"], a["a_rows"], a["a_row_div"],
-                                  a["B"], a["E"], a["N"], a["K"], a["s"], a["e"], a["tot"],
-                                  a["maxp"], a["bm"], a["nv"], a["w"], a["epi"], a["C"],
-                                  a["c_dtype"], a["ldc"], a["c_rows"], None)
+                                  a["B"], a["bl"], a["E"], a["N"], a["K"], a["s"], a["e"],
+                                  a["tot"], a["maxp"], a["bm"], a["nv"], a["w"], a["epi"],
+                                  a["C"], a["c_dtype"], a["ldc"], a["c_rows"], None)
     assert call(A=None) == d["MOE_ERR_NULL"]
     assert call(a_dtype=2) == d["MOE_ERR_DTYPE"]
     assert call(c_dtype=9) == d["MOE_ERR_DTYPE"]
@@ -154,23 +158,51 @@ def test_gemm_validation(mod):
     assert call(lda=64) == d["MOE_ERR_SHAPE"]
     assert call(ldc=64) == d["MOE_ERR_SHAPE"]
     assert call(A=ctypes.c_void_p(264)) == d["MOE_ERR_SHAPE"]   # misaligned
+    assert call(bl=2) == d["MOE_ERR_CONFIG"]                     # unknown weight layout
+    assert call(bl=1, bm=32) == d["MOE_ERR_CONFIG"]              # packed needs a tile kernel
+    assert call(bl=1, a_dtype=0) == d["MOE_ERR_CONFIG"]          # packed needs bf16 A
 
 
 def test_forward_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)
-    args = [f, 1, f, f, f, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, f, 1 << 30, None]
+    args = [f, 1, f, f, f, 0, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, f, 1 << 30,
+            None]
     assert L.moe_forward(*args[:1], 5, *args[2:]) == d["MOE_ERR_DTYPE"]
-    a = list(args); a[19] = None
+    a = list(args); a[20] = None
     assert L.moe_forward(*a) == d["MOE_ERR_WORKSPACE"]
-    a = list(args); a[20] = 1024
+    a = list(args); a[21] = 1024
     assert L.moe_forward(*a) == d["MOE_ERR_WORKSPACE"]
-    a = list(args); a[6] = 100      # H % 16
+    a = list(args); a[7] = 100      # H % 16
     assert L.moe_forward(*a) == d["MOE_ERR_SHAPE"]
-    a = list(args); a[15] = 24      # block_m
+    a = list(args); a[16] = 24      # block_m
     assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
     a = list(args); a[0] = None
     assert L.moe_forward(*a) == d["MOE_ERR_NULL"]
+    a = list(args); a[5] = 3        # weight layout
+    assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[5] = 1; a[1] = 0      # packed weights with f32 x
+    assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[5] = 1; a[16] = 32    # packed weights with the streaming block size
+    assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
+
+
+def test_packed_weights_size_and_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    # gate_up of the prefill layer: 6 tiles of 128 gate + 128 up rows, 64 K stages
+    assert mod.moe_packed_weights_size(128, 1536, 2048, "silu_mul") == 128 * 6 * 64 * 16384
+    assert mod.moe_packed_weights_size(128, 2048, 768, "none") == 128 * 8 * 24 * 16384
+    # ragged: N and K rounded up to whole tiles and stages (zero padded)
+    assert mod.moe_packed_weights_size(3, 80, 40, "none") == 3 * 1 * 2 * 16384
+    assert mod.moe_packed_weights_size(3, 96, 40, "silu_mul") == 3 * 1 * 2 * 16384
+    assert L.moe_packed_weights_size(3, 80, 44, 0) == 0                 # K % 8
+    assert L.moe_packed_weights_size(3, 48, 40, 1) == 0                 # silu: (N/2) % 16
+    assert L.moe_pack_weights(f, 3, 80, 40, 0, None, 1 << 20, None) == d["MOE_ERR_NULL"]
+    assert L.moe_pack_weights(f, 3, 80, 40, 0, f, 16384, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_pack_weights(f, 3, 80, 40, 7, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_pack_weights(ctypes.c_void_p(264), 3, 80, 40, 0, f, 1 << 20,
+                              None) == d["MOE_ERR_SHAPE"]
 
 
 def test_gmm_validation(mod):
@@ -189,4 +221,7 @@ def test_forward_block_m_choice(mod):
     assert mod.moe_forward_block_m(4096, 128, 8, "f32") == 128   # f32 x caps at 128
     assert mod.moe_forward_block_m(16, 256, 8) == 16             # decode shape
     assert mod.moe_forward_block_m(64, 8, 2, "f32") == 32        # tiny layer
-    assert mod.lib.moe_forward_block_m(16, 0, 8, 1) == -1
+    assert mod.moe_forward_block_m(16, 256, 8, weights="packed") == 64    # tile kernels only
+    assert mod.moe_forward_block_m(4096, 128, 8, weights="packed") == 256
+    assert mod.lib.moe_forward_block_m(16, 0, 8, 1, 0) == -1
+    assert mod.lib.moe_forward_block_m(16, 256, 8, 1, 5) == -1

@@ -4,11 +4,14 @@ A step is one moe_forward of the prefill-shaped layer (T=4096, H=2048,
 I=768, E=128, top-8 softmax with renormalisation): routing, alignment, the
 gate_up GEMM with SiLU*up, the down GEMM with the routing weight and the
 top-k reduce, on seeded synthetic inputs already resident in HBM.  The
-headline value is that step's throughput in TFLOP/s (6*T*topk*H*I
-algorithmic FLOPs, padding excluded).  The same run measures the
-decode-shaped layers (HBM GB/s over the touched experts' weights), the int8
-grouped GEMM, the routing workload and the tiny layer, and times the oracle
-on a bounded sample of the prefill workload on the host cores.
+expert weights are in the packed tile layout (moe_pack_weights, done once
+before timing, as at model load; its time is reported).  The headline value
+is that step's throughput in TFLOP/s (6*T*topk*H*I algorithmic FLOPs,
+padding excluded).  The same run measures the layer on plain [E, N, K]
+weights, the decode-shaped layers (HBM GB/s over the touched experts'
+weights), the int8 grouped GEMM, the routing workload and the tiny layer,
+and times the oracle on a bounded sample of the prefill workload on the
+host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -80,11 +83,21 @@ def layer_inputs(torch, cfg, dev):
     return x_dev, torch.from_numpy(g).to(dev), w1, w2, x, g
 
 
+def pack(torch, moe, w1, w2, timer):
+    """Packed copies of the layer's weights and the time the packing took."""
+    p1 = moe.moe_pack_weights(w1, "silu_mul")
+    p2 = moe.moe_pack_weights(w2, "none")
+    ms, _ = timer.run(lambda: (moe.moe_pack_weights(w1, "silu_mul", packed=p1.data),
+                               moe.moe_pack_weights(w2, "none", packed=p2.data)), 3)
+    return p1, p2, ms
+
+
 def bench_prefill(torch, moe, dev, steps, warmup, timer):
     import synth
     cfg = synth.CONFIGS["prefill"]
     T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
-    x, g, w1, w2, x_host, g_host = layer_inputs(torch, cfg, dev)
+    x, g, w1_plain, w2_plain, x_host, g_host = layer_inputs(torch, cfg, dev)
+    w1, w2, pack_ms = pack(torch, moe, w1_plain, w2_plain, timer)
     ws = torch.empty(moe.moe_forward_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
 
@@ -93,12 +106,18 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer):
 
     ms = wall_steps(torch, step, steps, warmup)
     flops = 6.0 * T * K * H * I
-    res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops)
+    res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops, pack_weights_ms=pack_ms)
+
+    def step_plain():
+        moe.moe_forward(x, g, w1_plain, w2_plain, K, out=out, workspace=ws)
+
+    ms_plain = wall_steps(torch, step_plain, steps, warmup)
+    res["plain_weights"] = dict(ms=ms_plain, tflops=flops / ms_plain * 1e-9)
 
     # Per-kernel breakdown: the same five launches moe_forward makes, each
     # timed with HIP events on the stream they run on.
     P = T * K
-    bm = moe.moe_forward_block_m(T, E, K)     # the block size moe_forward uses here
+    bm = moe.moe_forward_block_m(T, E, K, "bf16", "packed")   # the block size used here
     w_t, ids_t = moe.moe_route(g, K)
     sorted_ids, eids, total = moe.moe_align_block_size(ids_t, E, bm)
     cap = sorted_ids.numel()
@@ -133,7 +152,7 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer):
     res["breakdown"] = br
     res["gemm1_flops"] = gemm1_flops
     res["block_m"] = bm
-    res["inputs"] = (x_host, g_host, w1, w2)
+    res["inputs"] = (x_host, g_host, w1_plain, w2_plain)
     return res
 
 
@@ -145,25 +164,30 @@ def bench_decode(torch, moe, dev, name, steps, warmup, timer):
     import synth
     cfg = synth.CONFIGS[name]
     T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
-    x, g, w1, w2, _, _ = layer_inputs(torch, cfg, dev)
+    x, g, w1_plain, w2_plain, _, _ = layer_inputs(torch, cfg, dev)
+    w1, w2, pack_ms = pack(torch, moe, w1_plain, w2_plain, timer)
     ws = torch.empty(moe.moe_forward_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
 
-    def step():
-        moe.moe_forward(x, g, w1, w2, K, cfg.groups, cfg.topk_group, "softmax", True, cfg.scale,
+    def run(a, b):
+        moe.moe_forward(x, g, a, b, K, cfg.groups, cfg.topk_group, "softmax", True, cfg.scale,
                         out=out, topk_ids_out=ids, workspace=ws)
 
-    ms = wall_steps(torch, step, steps, warmup)
+    ms = wall_steps(torch, lambda: run(w1, w2), steps, warmup)
     n_exp = touched_experts(ids.cpu().numpy())
     per_expert = (2 * I * H + H * I) * 2
     nbytes = n_exp * per_expert + 2 * T * H * 2
-    mean, med = timer.run(step, max(steps, 10))
-    del w1, w2
+    mean, med = timer.run(lambda: run(w1, w2), max(steps, 10))
+    ms_plain = wall_steps(torch, lambda: run(w1_plain, w2_plain), steps, warmup)
+    del w1, w2, w1_plain, w2_plain
     torch.cuda.empty_cache()
     return dict(ms=ms, event_mean_ms=mean, touched_experts=n_exp, bytes=nbytes,
                 gbs=nbytes / ms * 1e-6, frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
-                flops=6.0 * T * K * H * I)
+                flops=6.0 * T * K * H * I, block_m=moe.moe_forward_block_m(T, E, K, "bf16", "packed"),
+                pack_weights_ms=pack_ms,
+                plain_weights=dict(ms=ms_plain, gbs=nbytes / ms_plain * 1e-6,
+                                   block_m=moe.moe_forward_block_m(T, E, K)))
 
 
 def bench_int8(torch, moe, dev, steps, warmup, timer):
@@ -239,8 +263,9 @@ def bench_tiny(torch, moe, dev, steps, warmup, timer):
     return dict(ms_wall=ms, event_median_us=med * 1e3)
 
 
-def cpu_baseline(torch, prefill_inputs, target_s=15.0):
-    """The oracle, as it stands, on the first S tokens of the prefill batch.
+def cpu_baseline(torch, prefill_inputs, target_s=12.0):
+    """The oracle, as it stands, on the first S tokens of the prefill batch
+    (all of them, repeated, when one pass is shorter than the target).
     Weights are decoded from bf16 to float64 before the timed region."""
     import oracle
     import synth
@@ -251,22 +276,30 @@ def cpu_baseline(torch, prefill_inputs, target_s=15.0):
     w1h = oracle.bf16_bits_to_f64(w1.view(torch.int16).cpu().numpy().view(np.uint16))
     w2h = oracle.bf16_bits_to_f64(w2.view(torch.int16).cpu().numpy().view(np.uint16))
     g64 = g_host.astype(np.float64)
+    def one(S):
+        w, ids = oracle.grouped_topk(g64[:S], cfg.topk)
+        oracle.moe_layer_expert_loop(xb[:S], w1h, w2h, w, ids)
+
     S = 64
     while True:
         t0 = time.perf_counter()
-        w, ids = oracle.grouped_topk(g64[:S], cfg.topk)
-        oracle.moe_layer_expert_loop(xb[:S], w1h, w2h, w, ids)
+        one(S)
         dt = time.perf_counter() - t0
         if dt >= target_s / 3 or S >= cfg.T:
             break
         S = min(cfg.T, int(S * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+    reps = max(1, int(round(target_s / max(dt, 1e-3)))) if S >= cfg.T else 1
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one(S)
+    dt = (time.perf_counter() - t0) / reps
     flops = 6.0 * S * cfg.topk * cfg.H * cfg.I
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return dict(value=flops / dt * 1e-12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                seconds=dt,
-                sample="first %d of %d tokens of the prefill layer (route + expert-loop layer, "
-                       "float64 NumPy; weights pre-decoded)" % (S, cfg.T))
+                seconds_per_pass=dt, passes=reps,
+                sample="%d pass(es) over the first %d of %d tokens of the prefill layer (route + "
+                       "expert-loop layer, float64 NumPy; weights pre-decoded)" % (reps, S, cfg.T))
 
 
 def main():
@@ -293,10 +326,11 @@ def main():
     g1 = pre["breakdown"]["gemm1_gate_up_silu"]
     roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=g1["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
-                    kernel="moe_gemm_tile_kernel (gate_up GEMM, SiLU*up epilogue)",
+                    kernel="moe_gemm_dma_kernel (gate_up GEMM, SiLU*up epilogue, packed weights)",
                     block_m=pre["block_m"],
                     flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
-    components = {"prefill_breakdown": pre["breakdown"]}
+    components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre["plain_weights"],
+                  "prefill_pack_weights_ms": pre["pack_weights_ms"]}
     if not args.quick:
         for name in ("decode16", "decode64"):
             log(name)
@@ -313,8 +347,7 @@ def main():
         cpu = cpu_baseline(torch, pre["inputs"])
 
     line = {
-        "metric": "fused-MoE layer TFLOP/s (prefill) + decode HBM GB/s at 1 GPU, "
-                  "as % of MI355X roofline",
+        "metric": "fused-MoE layer TFLOP/s + decode HBM GB/s at 1 GPU, as % of MI355X roofline",
         "value": round(pre["tflops"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

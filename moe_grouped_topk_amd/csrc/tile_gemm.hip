@@ -49,8 +49,11 @@ constexpr int kMaxGmmExperts = 1024;
 #define MOE_TILE_NBUF 1   // register prefetch buffers (loads one stage ahead)
 #endif
 #ifndef MOE_T256_WN
-#define MOE_T256_WN 2     // 256 x 256 tile: 2 x 4 waves of 128 x 64
-#define MOE_T256_WM 4
+#define MOE_T256_WN 4     // 256 x 256 tile: 4 x 2 waves of 64 x 128
+#define MOE_T256_WM 2
+#endif
+#ifndef MOE_T256_NSTAGE
+#define MOE_T256_NSTAGE 4 // K stages in the LDS ring (4 x 32 KiB)
 #endif
 
 
@@ -283,7 +286,8 @@ __device__ __forceinline__ void wait_stage_nobar(int n_after) {
     case 0: wait_vm<0>(); break;
     case 1: wait_vm<NI>(); break;
     case 2: wait_vm<2 * NI>(); break;
-    default: wait_vm<3 * NI>(); break;
+    case 3: wait_vm<3 * NI>(); break;
+    default: wait_vm<4 * NI>(); break;
   }
 }
 
@@ -294,7 +298,8 @@ __device__ __forceinline__ void wait_stage(int n_after) {
     case 0: wait_vm_barrier<0>(); break;
     case 1: wait_vm_barrier<NI>(); break;
     case 2: wait_vm_barrier<2 * NI>(); break;
-    default: wait_vm_barrier<3 * NI>(); break;
+    case 3: wait_vm_barrier<3 * NI>(); break;
+    default: wait_vm_barrier<4 * NI>(); break;
   }
 }
 
@@ -307,7 +312,9 @@ struct DmaCfg {
   static constexpr int NI = (BN + BM) / 16 / (WN * WM);      // DMA instructions per wave per stage
   static constexpr int kStage = (BN + BM) * ROWB;
   static constexpr int kBytes = NSTAGE * kStage;
-  static_assert((BN + BM) % (16 * WN * WM) == 0 && NSTAGE >= 2 && NSTAGE <= 4, "dma tile shape");
+  static_assert((BN + BM) % (16 * WN * WM) == 0 && NSTAGE >= 2 && NSTAGE <= 5, "dma tile shape");
+  // vmcnt counts at most 63 outstanding loads per wave
+  static_assert((NSTAGE - 1) * NI <= 63, "too many loads in flight for vmcnt");
 };
 
 // rowp[j]: global address of the start of this lane's j-th DMA row (local
@@ -528,7 +535,7 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
   for (int cb = 0; cb < CB; ++cb) {
     const int trow = tcol0 + cb * 32 + (lane & 31);
     const int p = rowinfo[trow];
-    if (p < 0) continue;
+    if (p < 0 || p >= a.num_valid) continue;
     const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + trow;
     const float w = a.topk_weights ? a.topk_weights[p] : 1.0f;
     uint8_t* rowp = Cb + crow * a.ldc * ce;
@@ -572,24 +579,28 @@ __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile
 }
 
 // 1 + the last tile row holding a valid pair (0 if none); wave-uniform.
+// rowinfo: the tile's entries, -1 or a raw sorted id (>= num_valid = placeholder).
 template <int BM>
-__device__ __forceinline__ int live_rows(const int* rowinfo) {
+__device__ __forceinline__ int live_rows(const int* rowinfo, int64_t num_valid) {
   const int lane = threadIdx.x & 63;
   uint32_t last = 0;
 #pragma unroll
-  for (int r = lane; r < BM; r += 64)
-    if (rowinfo[r] >= 0) last = (uint32_t)(r + 1);
+  for (int r = lane; r < BM; r += 64) {
+    const int p = rowinfo[r];
+    if (p >= 0 && p < num_valid) last = (uint32_t)(r + 1);
+  }
   return (int)wave_max_u32(last);
 }
 
 // A row feeding tile token row r; placeholder rows read the tile's first row
-// (valid whenever row 0 is), which only reaches masked outputs.
+// (valid whenever row 0 is), which only reaches masked outputs.  rowinfo
+// entries are -1 or raw sorted ids (>= num_valid = placeholder).
 __device__ __forceinline__ int moe_token_row(const MoeGemmArgs& a, const MoeTile& t,
                                              const int* rowinfo, int r) {
   const int p = rowinfo[r];
-  if (p < 0) {
+  if (p < 0 || p >= a.num_valid) {
     const int p0 = rowinfo[0];
-    return p0 < 0 ? 0 : (a.a_rows == 0 ? p0 / a.a_row_div : (int)t.s0);
+    return (p0 < 0 || p0 >= a.num_valid) ? 0 : (a.a_rows == 0 ? p0 / a.a_row_div : (int)t.s0);
   }
   return a.a_rows == 0 ? p / a.a_row_div : (int)(t.s0 + r);
 }
@@ -645,7 +656,7 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a)
   __shared__ int rowinfo[BM];
   MoeTile t;
   if (!moe_tile<BN, BM, EPI>(a, t)) return;
-  load_rowinfo<BM>(a, t, rowinfo);
+  load_rowinfo<BM>(a, t, rowinfo);   // one global round trip, then LDS
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
@@ -686,8 +697,8 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a)
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
-  mainloop_dma_live<C, 0>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0, live_rows<BM>(rowinfo),
-                          acc);
+  mainloop_dma_live<C, 0>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
+                          live_rows<BM>(rowinfo, a.num_valid), acc);
   moe_epilogue<C::RB, C::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
@@ -874,7 +885,7 @@ template <> struct TileFor<128> {
   typedef Cfg<256, 128, 2, 2, MOE_TILE_NBUF> Regs;
 };
 template <> struct TileFor<256> {
-  typedef DmaCfg<256, 256, 4, MOE_T256_WN, MOE_T256_WM> Dma;   // 2 waves per SIMD
+  typedef DmaCfg<256, 256, MOE_T256_NSTAGE, MOE_T256_WN, MOE_T256_WM> Dma;   // 2 waves per SIMD
 };
 
 template <int BM>

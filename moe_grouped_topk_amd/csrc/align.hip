@@ -4,8 +4,10 @@
 // Semantics: mini-sglang "MoE and fused MoE", moe_align_block_size (stable
 // argsort by expert, placeholder = number of pairs, one expert id per block).
 //
-// Design: a single 1024-thread workgroup (16 waves); totals never leave the
-// device.  Wave w owns a contiguous chunk of the pairs.
+// Two kernels, both keeping every total on the device.  The expert-parallel
+// one (below) serves the usual sizes; this single 1024-thread workgroup (16
+// waves) serves very large pair counts.  Wave w owns a contiguous chunk of
+// the pairs.
 //   pass 1: per-wave histograms counts[w][e] in LDS (LDS atomics), the ids
 //           read in batches so many loads are in flight at once;
 //   scan:   per expert, exclusive prefix over waves (so wave w knows where its
@@ -152,9 +154,160 @@ align_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   if (tid == 0) *total_out = total;
 }
 
+// ---------------------------------------------------------------------------
+// Expert-parallel variant: one workgroup per expert, for the common sizes.
+//
+// Every workgroup reads all the ids (a few hundred KiB at most, served from
+// L2), builds the full per-expert histogram in LDS and scans the padded
+// sizes itself, so no workgroup waits for another and nothing has to be
+// staged in global memory.  Workgroup e then writes only expert e's segment:
+// wave w owns the w-th contiguous run of pairs, counts its pairs of expert
+// e, and a block-wide exclusive scan of those counts gives each wave where
+// its pairs go.  Runs are in pair order and each run is written in order,
+// so the segment is in ascending pair order (stable).  Placeholders, expert
+// ids per block and the unused tail of both buffers are written alongside.
+// The ids are cached in LDS as 16-bit values when they fit.
+constexpr int kAlignEThreads = 512;
+constexpr int kAlignEWaves = kAlignEThreads / kWave;
+constexpr int kAlignEBatch = 64;   // ids per thread in flight at once (one round trip for 32K pairs)
+
+// Exclusive scan of one int per thread over the workgroup; also returns the
+// total.  tmp: LDS scratch of 2 * kAlignEWaves ints.  Contains barriers.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kAlignEWaves ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kAlignEWaves; off <<= 1) {
+      const int y = __shfl_up(w, off, kWave);
+      if (lane >= off) w += y;
+    }
+    if (lane < kAlignEWaves) tmp[kAlignEWaves + lane] = w;
+  }
+  __syncthreads();
+  total = tmp[2 * kAlignEWaves - 1];
+  const int before = wave ? tmp[kAlignEWaves + wave - 1] : 0;
+  __syncthreads();   // tmp may be reused right after
+  return before + x - v;
+}
+
+template <bool CACHE>
+__global__ void __launch_bounds__(kAlignEThreads)
+align_expert_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
+                    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+                    int32_t* __restrict__ total_out, int max_padded) {
+  extern __shared__ int smem[];
+  int* hist = smem;                                  // [kAlignEWaves][E]
+  int* seg = hist + kAlignEWaves * E;                // [E + 1] segment starts
+  int* tmp = seg + (E + 1);                          // [2 * kAlignEWaves]
+  uint16_t* cache = reinterpret_cast<uint16_t*>(tmp + 2 * kAlignEWaves);   // [P] if CACHE
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int e = blockIdx.x;
+  for (int i = tid; i < kAlignEWaves * E; i += kAlignEThreads) hist[i] = 0;
+  __syncthreads();
+
+  // 1. histogram of all pairs (per-wave copies keep LDS atomics apart)
+  for (int base = 0; base < P; base += kAlignEThreads * kAlignEBatch) {
+    int ids[kAlignEBatch];
+#pragma unroll
+    for (int j = 0; j < kAlignEBatch; ++j) {
+      const int i = base + j * kAlignEThreads + tid;
+      ids[j] = i < P ? topk_ids[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kAlignEBatch; ++j) {
+      const int i = base + j * kAlignEThreads + tid;
+      const bool ok = ids[j] >= 0 && ids[j] < E;
+      if (ok) atomicAdd(&hist[wave * E + ids[j]], 1);
+      if (CACHE && i < P) cache[i] = ok ? (uint16_t)ids[j] : (uint16_t)0xFFFFu;
+    }
+  }
+  __syncthreads();
+
+  // 2. padded segment sizes and their exclusive scan (two experts per thread)
+  int cnt2[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int ee = 2 * tid + q;
+    if (ee < E)
+      for (int w = 0; w < kAlignEWaves; ++w) cnt2[q] += hist[w * E + ee];
+  }
+  const int pad0 = (cnt2[0] + B - 1) / B * B, pad1 = (cnt2[1] + B - 1) / B * B;
+  int total;
+  const int start = block_exclusive_scan(pad0 + pad1, tmp, total);
+  if (2 * tid < E) seg[2 * tid] = start;
+  if (2 * tid + 1 < E) seg[2 * tid + 1] = start + pad0;
+  if (tid == 0) seg[E] = total;
+  __syncthreads();
+
+  // 3. this expert's pairs, stable: wave w walks the w-th contiguous run of
+  //    pairs 64 at a time (consecutive lanes read consecutive ids), counts
+  //    its matches, and after a scan over the waves writes them, each lane
+  //    at the wave's cursor plus its rank among the matching lanes.
+  const int run = (P + kAlignEWaves * kWave - 1) / (kAlignEWaves * kWave) * kWave;
+  const int r0 = min(P, wave * run), r1 = min(P, r0 + run);
+  auto id_at = [&](int i) -> int { return CACHE ? (int)cache[i] : topk_ids[i]; };
+  int mine = 0;
+#pragma unroll 8
+  for (int i = r0 + lane; i < r1; i += kWave) mine += id_at(i) == e;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mine += __shfl_xor(mine, m, kWave);
+  int cnt_e;
+  int cursor = seg[e] + block_exclusive_scan(lane == 0 ? mine : 0, tmp, cnt_e);
+  cursor = __shfl(cursor, 0, kWave);
+  if (mine) {
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll 4
+    for (int base = r0; base < r1; base += kWave) {
+      const int i = base + lane;
+      const bool hit = i < r1 && id_at(i) == e;
+      const uint64_t m = __ballot(hit);
+      if (hit) sorted_ids[cursor + __popcll(m & lt_mask)] = i;
+      cursor += __popcll(m);
+    }
+  }
+
+  // 4. placeholders and expert ids of this segment
+  const int s0 = seg[e], s1 = seg[e + 1];
+  for (int s = s0 + cnt_e + tid; s < s1; s += kAlignEThreads) sorted_ids[s] = P;
+  for (int b = s0 / B + tid; b < s1 / B; b += kAlignEThreads) expert_ids[b] = e;
+
+  // 5. unused tail of both buffers, shared by all workgroups
+  const int stride = gridDim.x * kAlignEThreads, first = blockIdx.x * kAlignEThreads + tid;
+  for (int s = total + first; s < max_padded; s += stride) sorted_ids[s] = P;
+  for (int b = total / B + first; b < max_padded / B; b += stride) expert_ids[b] = -1;
+  if (blockIdx.x == 0 && tid == 0) *total_out = total;
+}
+
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
                         int64_t max_padded, hipStream_t stream) {
+  // Expert-parallel kernel while every workgroup's full read of the ids stays
+  // cheap; the single-workgroup kernel beyond that.
+  if (P * (int64_t)E <= ((int64_t)1 << 26)) {
+    const size_t base = sizeof(int) * ((size_t)kAlignEWaves * E + (E + 1) + 2 * kAlignEWaves);
+    const size_t with_cache = base + 2 * (size_t)P;
+    const bool cache = with_cache <= 160 * 1024;
+    const size_t lds = cache ? with_cache : base;
+    auto k = cache ? align_expert_kernel<true> : align_expert_kernel<false>;
+    if (lds > 65536) {
+      const hipError_t st =
+          hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (st != hipSuccess) return st;
+    }
+    hipLaunchKernelGGL(k, dim3(E), dim3(kAlignEThreads), lds, stream, topk_ids, (int)P, E, B,
+                       sorted_ids, expert_ids, total, (int)max_padded);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E + (E + 1) + 2 * kAlignWaves);
   if (lds > 65536) {
     const hipError_t st = hipFuncSetAttribute(

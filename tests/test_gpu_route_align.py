@@ -171,6 +171,18 @@ def test_align_workload_shapes(moe, dev, T, E, K, B):
     _check_align(moe, ids, E, B, dev)
 
 
+@pytest.mark.parametrize("P,E,B", [(32768, 128, 256),     # prefill pairs, block 256
+                                   (100000, 128, 64),     # ids not cached in LDS
+                                   (600000, 128, 128)])   # single-workgroup kernel
+def test_align_large(moe, dev, P, E, B):
+    """The three alignment kernels the library picks by size all agree with
+    the oracle bit for bit."""
+    rng = np.random.default_rng(P + E + B)
+    ids = rng.integers(0, E, size=P).astype(np.int32)
+    ids[: P // 7] = E // 3                     # one heavy expert
+    _check_align(moe, ids, E, B, dev)
+
+
 def test_align_skewed_and_edge(moe, dev):
     _check_align(moe, np.zeros(5000, np.int32), 64, 128, dev)          # one expert
     _check_align(moe, np.full(777, 63, np.int32), 64, 16, dev)         # last expert

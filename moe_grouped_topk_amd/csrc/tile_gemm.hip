@@ -303,9 +303,10 @@ __device__ __forceinline__ void wait_stage(int n_after) {
   }
 }
 
-template <int BN_, int BM_, int NSTAGE_, int WN_ = 2, int WM_ = 2>
+template <int BN_, int BM_, int NSTAGE_, int WN_ = 2, int WM_ = 2, int OCC_ = 1>
 struct DmaCfg {
   static constexpr int BN = BN_, BM = BM_, NSTAGE = NSTAGE_;
+  static constexpr int OCC = OCC_;                           // workgroups per CU aimed for
   static constexpr int WN = WN_, WM = WM_, THREADS = 64 * WN * WM;
   static constexpr int ROWB = 64;                            // LDS bytes per row per stage
   static constexpr int RB = BN / WN / 32, CB = BM / WM / 32;
@@ -650,7 +651,7 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
 
 // Direct-to-LDS variant (bf16 tokens).
 template <class C, int EPI, int CDT>
-__global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a) {
+__global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGemmArgs a) {
   constexpr int BN = C::BN, BM = C::BM;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[BM];
@@ -704,9 +705,15 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_dma_kernel(MoeGemmArgs a)
 
 // ---------------------------------------------------------------------------
 // INT8 GMM: rows [off[e], off[e+1]) of X use W[e]; fp16 output.
-typedef DmaCfg<256, 128, 4> GmmCfg;
+#ifndef MOE_GMM_NSTAGE
+#define MOE_GMM_NSTAGE 3
+#define MOE_GMM_OCC 2
+#define MOE_GMM_WN 4
+#define MOE_GMM_WM 2
+#endif
+typedef DmaCfg<256, 128, MOE_GMM_NSTAGE, MOE_GMM_WN, MOE_GMM_WM, MOE_GMM_OCC> GmmCfg;
 
-__global__ void __launch_bounds__(GmmCfg::THREADS) gmm_i8_tile_kernel(GmmI8Args a) {
+__global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kernel(GmmI8Args a) {
   typedef GmmCfg C;
   typedef C S;
   constexpr int BN = C::BN, BM = C::BM, NT = C::THREADS;
@@ -876,12 +883,30 @@ hipError_t launch_tile_c(const MoeGemmArgs& a, hipStream_t s) {
 // Tile configurations per block size.  bf16 tokens: direct-to-LDS loop,
 // BN x BM with NSTAGE LDS stages; float32 tokens: register-staged loop.
 template <int BM> struct TileFor;
+// 256 x 128 tiles: 8 waves of 64 x 64, a 3-stage ring (72 KiB) and two
+// workgroups per CU, so one workgroup's MFMAs run while the other waits at
+// its barrier or for its loads (measured faster than one 256 x 256 tile per
+// CU with 8 or 16 waves).
+#ifndef MOE_T128_NSTAGE
+#define MOE_T128_NSTAGE 3
+#define MOE_T128_OCC 2
+#endif
+#ifndef MOE_T128_WN
+#define MOE_T128_WN 4
+#define MOE_T128_WM 2
+#endif
+#ifndef MOE_T64_NSTAGE
+#define MOE_T64_NSTAGE 4
+#define MOE_T64_OCC 1
+#define MOE_T64_WN 2
+#define MOE_T64_WM 2
+#endif
 template <> struct TileFor<64> {
-  typedef DmaCfg<256, 64, 4> Dma;
+  typedef DmaCfg<256, 64, MOE_T64_NSTAGE, MOE_T64_WN, MOE_T64_WM, MOE_T64_OCC> Dma;
   typedef Cfg<256, 64, 2, 2, MOE_TILE_NBUF> Regs;
 };
 template <> struct TileFor<128> {
-  typedef DmaCfg<256, 128, 4> Dma;
+  typedef DmaCfg<256, 128, MOE_T128_NSTAGE, MOE_T128_WN, MOE_T128_WM, MOE_T128_OCC> Dma;
   typedef Cfg<256, 128, 2, 2, MOE_TILE_NBUF> Regs;
 };
 template <> struct TileFor<256> {

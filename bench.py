@@ -32,6 +32,11 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
+# HBM bytes per launch of the gate_up kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled
+# by a 1 GiB copy (profiles/prefill_layer_packed_bm128.md).  Only valid for that kernel
+# configuration; reported as null for any other block size.
+GATE_UP_TRAFFIC = {"block_m": 128, "bytes": 1.430e9 + 0.054e9}
+
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
@@ -92,7 +97,7 @@ def pack(torch, moe, w1, w2, timer):
     return p1, p2, ms
 
 
-def bench_prefill(torch, moe, dev, steps, warmup, timer):
+def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     import synth
     cfg = synth.CONFIGS["prefill"]
     T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
@@ -111,8 +116,9 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer):
     def step_plain():
         moe.moe_forward(x, g, w1_plain, w2_plain, K, out=out, workspace=ws)
 
-    ms_plain = wall_steps(torch, step_plain, steps, warmup)
-    res["plain_weights"] = dict(ms=ms_plain, tflops=flops / ms_plain * 1e-9)
+    if plain:
+        ms_plain = wall_steps(torch, step_plain, steps, warmup)
+        res["plain_weights"] = dict(ms=ms_plain, tflops=flops / ms_plain * 1e-9)
 
     # Per-kernel breakdown: the same five launches moe_forward makes, each
     # timed with HIP events on the stream they run on.
@@ -309,6 +315,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="prefill headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain", action="store_true",
+                    help="skip the plain-layout comparison runs (profiling the measured path only)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also copy 1 GiB device-to-device 3 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -322,15 +332,25 @@ def main():
     timer = Timer(torch)
 
     log("prefill layer")
-    pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer)
+    pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
     g1 = pre["breakdown"]["gemm1_gate_up_silu"]
     roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=g1["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                    frac=g1["tflops"] / PEAK_BF16_TFLOPS,
+                    traffic=(GATE_UP_TRAFFIC["bytes"] if pre["block_m"] == GATE_UP_TRAFFIC["block_m"]
+                             else None),
+                    traffic_unit="bytes per launch",
                     kernel="moe_gemm_dma_kernel (gate_up GEMM, SiLU*up epilogue, packed weights)",
                     block_m=pre["block_m"],
                     flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
-    components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre["plain_weights"],
+    components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_pack_weights_ms": pre["pack_weights_ms"]}
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.quick:
         for name in ("decode16", "decode64"):
             log(name)

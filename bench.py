@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the gate_up kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled
 # by a 1 GiB copy (profiles/prefill_layer_packed_bm128.md).  Only valid for that kernel
 # configuration; reported as null for any other block size.
-GATE_UP_TRAFFIC = {"block_m": 128, "bytes": 1.430e9 + 0.054e9}
+GATE_UP_TRAFFIC = {"block_m": 128, "bytes": 1.230e9 + 0.053e9}
 
 
 def log(msg):

@@ -477,8 +477,18 @@ struct MoeTile {
   int64_t s0, c0;
 };
 
+// Logical tile order.  Block-major numbering (L = blk * ntile + nt) gives
+// each expert one contiguous range of m_e * ntile tiles.  Inside that range
+// the tiles are renumbered n-tile-major (L = base + nt * m_e + mb), so the
+// m_e tiles that read the same weight slice are neighbours: they are
+// dispatched together and stream that slice through L2 once.  The workgroup
+// finds its expert's block range from one read of expert_ids around its
+// block-major block (a window of blockDim.x blocks).  Experts longer than
+// half the window keep block-major order; that choice depends only on the
+// expert, so every workgroup of an expert uses the same numbering and the
+// mapping stays a bijection.  Uses two barriers; s_win: 3 ints of LDS.
 template <int BN, int BM, int EPI>
-__device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t) {
+__device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t, int* s_win) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   const int64_t ncols = EPI ? BN / 2 : BN;            // output columns per tile
   const int ntile = (int)((Nout + ncols - 1) / ncols);
@@ -486,9 +496,29 @@ __device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t) {
   const int live = nblk * ntile;
   if ((int)blockIdx.x >= live) return false;
   const int L = xcd_remap((int)blockIdx.x, live);
-  t.blk = L / ntile;
-  t.nt = L % ntile;
-  t.e = a.expert_ids[t.blk];
+  const int bm = L / ntile;                           // block-major block
+  const int half = (int)blockDim.x / 2;
+  const int idx = bm - half + (int)threadIdx.x;       // window [bm - half, bm + half)
+  const int v = (idx >= 0 && idx < nblk) ? a.expert_ids[idx] : -2;
+  if (threadIdx.x == 0) { s_win[1] = INT32_MAX; s_win[2] = -1; }
+  if (idx == bm) s_win[0] = v;
+  __syncthreads();
+  const int e = s_win[0];
+  if (v == e) { atomicMin(&s_win[1], idx); atomicMax(&s_win[2], idx); }
+  __syncthreads();
+  const int first = s_win[1], last = s_win[2];
+  const bool first_exact = first > bm - half || first == 0;
+  const bool last_exact = last < bm + half - 1 || last == nblk - 1;
+  const int m_e = last - first + 1;
+  if (e >= 0 && first_exact && last_exact && m_e <= half - 1) {
+    const int local = L - first * ntile;
+    t.nt = local / m_e;
+    t.blk = first + local % m_e;
+  } else {
+    t.blk = bm;
+    t.nt = L % ntile;
+  }
+  t.e = e;
   t.s0 = (int64_t)t.blk * BM;
   t.c0 = (int64_t)t.nt * ncols;
   return t.e >= 0;
@@ -614,7 +644,8 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[BM];
   MoeTile t;
-  if (!moe_tile<BN, BM, EPI>(a, t)) return;
+  __shared__ int s_win[3];
+  if (!moe_tile<BN, BM, EPI>(a, t, s_win)) return;
   load_rowinfo<BM>(a, t, rowinfo);
 
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -656,7 +687,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[BM];
   MoeTile t;
-  if (!moe_tile<BN, BM, EPI>(a, t)) return;
+  __shared__ int s_win[3];
+  if (!moe_tile<BN, BM, EPI>(a, t, s_win)) return;
   load_rowinfo<BM>(a, t, rowinfo);   // one global round trip, then LDS
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -209,6 +209,31 @@ def test_gemm_skewed_experts(moe, dev, B, layout):
     assert max_abs_rel(C.cpu().numpy(), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("B,layout", [(64, "plain"), (128, "packed"), (256, "plain")])
+def test_gemm_long_and_short_experts(moe, dev, B, layout):
+    """One expert spans more token blocks than the kernels' tile-order window
+    (it keeps block-major tile order), the others span 1-3 blocks (n-tile-major
+    order inside the expert); every output row is written exactly once."""
+    E, H, N = 6, 64, 512
+    counts = [40000, 1, 130, 0, 257, 64]
+    ids = np.concatenate([np.full(c, e, np.int64) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(B).permutation(ids)[:, None]
+    T = ids.shape[0]
+    A = synth.normal_f32((T, H), 9, 11)
+    Bw = synth.normal_f32((E, N, H), 9, 12, 0, 0.05)
+    Ab, Bb = synth.f32_to_bf16_bits(A), synth.f32_to_bf16_bits(Bw)
+    sb, eb, tot, s, e, total = _meta(moe, ids, E, B, dev)
+    C = torch.full((T, N), float("nan"), dtype=torch.float32, device=dev)
+    moe.moe_grouped_gemm(bf16_dev(Ab, dev), _weights(moe, Bb, dev, layout, "none"), sb, eb, tot, B,
+                         T, C=C)
+    torch.cuda.synchronize()
+    ref, _ = oracle.grouped_gemm_sorted(oracle.bf16_bits_to_f64(Ab), oracle.bf16_bits_to_f64(Bb),
+                                        s, e, B, T, 1)
+    got = C.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert max_abs_rel(got, ref) <= 1e-5
+
+
 def test_gemm_packed_rejects_f32_input_and_small_blocks(moe, dev):
     ids = np.zeros((8, 1), np.int64)
     A = torch.zeros((8, 64), dtype=torch.float32, device=dev)

@@ -215,20 +215,24 @@ def bench_int8(torch, moe, dev, steps, warmup, timer):
     sx_d = torch.from_numpy(sx).to(dev)
     off_d = torch.from_numpy(off).to(dev)
     Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    wp = moe.moe_pack_weights(wq)           # packed once, as at model load
 
     def step():
-        moe.gmm_int8(xq_d, wq, sx_d, sw, off_d, output=Y)
+        moe.gmm_int8(xq_d, wp, sx_d, sw, off_d, output=Y)
 
     ms = wall_steps(torch, step, steps, warmup)
     mean, med = timer.run(step, max(steps, 10))
+    ms_plain = wall_steps(torch, lambda: moe.gmm_int8(xq_d, wq, sx_d, sw, off_d, output=Y),
+                          steps, warmup)
     nz = int((sizes > 0).sum())
     nbytes = nz * N * K + M * K + 2 * M * N + 4 * (E * N + M)
     ops = 2.0 * M * N * K
-    del wq
+    del wq, wp
     torch.cuda.empty_cache()
     return dict(ms=ms, event_mean_ms=mean, tops=ops / ms * 1e-9, gbs=nbytes / ms * 1e-6,
                 frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
                 frac_int8=ops / ms * 1e-9 / PEAK_INT8_TOPS, bytes=nbytes, ops=ops,
+                weights="packed", plain_weights=dict(ms=ms_plain, gbs=nbytes / ms_plain * 1e-6),
                 group_sizes_min_max=[int(sizes.min()), int(sizes.max())])
 
 

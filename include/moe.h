@@ -58,6 +58,7 @@ extern "C" {
 #define MOE_DTYPE_F32   0
 #define MOE_DTYPE_BF16  1
 #define MOE_DTYPE_F16   2
+#define MOE_DTYPE_I8    3   /* int8 weights (moe_pack_weights / gmm_int8 only) */
 
 #define MOE_SCORING_SOFTMAX 0
 #define MOE_SCORING_SIGMOID 1
@@ -143,34 +144,39 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
                          int64_t max_padded, void* stream);
 
 /* ---- packed expert weights --------------------------------------------
- * moe_pack_weights: one-time re-layout of bf16 expert weights [E, N, K] for
- * the MFMA tile kernels (block_m 64, 128, 256).  The weights and every
- * result computed from them are unchanged; only the byte order differs.
- * In the plain layout each K step of a tile reads 64 bytes from each of 256
- * rows that lie K*2 bytes apart; packed, the same step is one contiguous
- * 16 KiB block, which HBM serves far faster.
+ * moe_pack_weights: one-time re-layout of expert weights [E, N, K] (bf16 for
+ * the MoE GEMMs, int8 for gmm_int8) for the MFMA tile kernels (block_m 64,
+ * 128, 256 and the int8 GMM).  The weights and every result computed from
+ * them are unchanged; only the byte order differs.  In the plain layout each
+ * K step of a tile reads 64 bytes from each of 256 rows that lie K * element
+ * size bytes apart; packed, the same step is one contiguous 16 KiB block,
+ * which HBM serves far faster.
  *
  * Layout.  Each expert's rows are cut into tiles of 256 rows:
  *   epilogue MOE_EPILOGUE_NONE:     tile t holds rows 256t .. 256t+255;
  *   epilogue MOE_EPILOGUE_SILU_MUL: tile t holds gate rows 128t .. 128t+127
  *                                   and then the up rows N/2 + 128t ..
  *                                   (the pairs the SiLU*up epilogue joins).
- * K is cut into stages of 32 elements (64 bytes).  Block (e, t, s) is 16 KiB
- * at byte offset ((e * NT + t) * KS + s) * 16384 with NT tiles per expert
- * and KS = ceil(K / 32).  Inside a block, the 16-byte chunk c (elements
- * 8c .. 8c+7 of the stage) of tile row r is at r * 64 + 16 * (c ^ ((r >> 2) & 3)).
- * Rows past the matrix and elements past K are zero.
+ * K is cut into stages of 64 bytes (32 bf16 or 64 int8 elements).  Block
+ * (e, t, s) is 16 KiB at byte offset ((e * NT + t) * KS + s) * 16384 with NT
+ * tiles per expert and KS = ceil(K * element size / 64).  Inside a block, the
+ * 16-byte chunk c (bytes 16c .. 16c+15 of the stage) of tile row r is at
+ * r * 64 + 16 * (c ^ ((r >> 2) & 3)).  Rows past the matrix and bytes past K
+ * are zero.
  *
- *   w         [E, N, K] bf16 (read only).
+ *   w         [E, N, K] of dtype (read only).
+ *   dtype     MOE_DTYPE_BF16 or MOE_DTYPE_I8 (int8 only with epilogue NONE).
  *   epilogue  the epilogue of the GEMM that will use the packed weights.
- *   packed    output, at least moe_packed_weights_size(E, N, K, epilogue) bytes.
- * Requirements: as moe_grouped_gemm for N and K; w and packed 16-byte aligned.
- * Errors: NULLs, bad sizes or epilogue, packed_bytes too small.
+ *   packed    output, at least moe_packed_weights_size(...) bytes.
+ * Requirements: bf16 as moe_grouped_gemm for N and K; int8 as gmm_int8;
+ * w and packed 16-byte aligned.  Errors: NULLs, bad sizes, dtype or
+ * epilogue, packed_bytes too small.
  */
-MOE_API size_t moe_packed_weights_size(int32_t E, int64_t N, int64_t K, int32_t epilogue);
+MOE_API size_t moe_packed_weights_size(int32_t dtype, int32_t E, int64_t N, int64_t K,
+                                       int32_t epilogue);
 
-MOE_API int moe_pack_weights(const void* w, int32_t E, int64_t N, int64_t K, int32_t epilogue,
-                     void* packed, size_t packed_bytes, void* stream);
+MOE_API int moe_pack_weights(const void* w, int32_t dtype, int32_t E, int64_t N, int64_t K,
+                     int32_t epilogue, void* packed, size_t packed_bytes, void* stream);
 
 /* ---- grouped GEMM ------------------------------------------------------
  * moe_grouped_gemm: [MSG] fused MoE, fused_moe_kernel, with the gathered
@@ -261,7 +267,9 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
  * with the integer sum accumulated exactly in int32 ([GMM] 5.3) and the
  * scales applied in fp32.  Output rows stay in input order.
  *
- *   input          [M, K] int8.       weights   [E, N, K] int8 (K contiguous).
+ *   input          [M, K] int8.       weights   [E, N, K] int8 (K contiguous);
+ *                  with w_layout MOE_WEIGHTS_PACKED, written by
+ *                  moe_pack_weights(dtype MOE_DTYPE_I8, epilogue NONE).
  *   scales_x       [M] f32 per row.   scales_w  [E, N] f32 per output channel.
  *   expert_offsets [E + 1] int32, non-decreasing, offsets[0] = 0,
  *                  offsets[E] = M (device memory; checked on the device only
@@ -271,7 +279,7 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
  * Requirements: K % 16 == 0, N % 16 == 0, K <= 131072 (exact int32 sums),
  * E in [1, MOE_MAX_EXPERTS].
  */
-MOE_API int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
+MOE_API int gmm_int8(const int8_t* input, const int8_t* weights, int32_t w_layout, const float* scales_x,
              const float* scales_w, const int32_t* expert_offsets,
              const int32_t* expert_sizes, void* output, int64_t M, int64_t K,
              int64_t N, int32_t E, void* stream);

@@ -22,7 +22,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 # Codes of include/moe.h
-DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
+DTYPE = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3}
 SCORING = {"softmax": 0, "sigmoid": 1}
 EPILOGUE = {"none": 0, "silu_mul": 1}
 ROWS = {"pair": 0, "sorted": 1}
@@ -51,9 +51,9 @@ def _load():
     L.moe_align_max_padded.restype = i64
     L.moe_align_block_size.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, vp]
     L.moe_align_block_size.restype = ctypes.c_int
-    L.moe_packed_weights_size.argtypes = [i32, i64, i64, i32]
+    L.moe_packed_weights_size.argtypes = [i32, i32, i64, i64, i32]
     L.moe_packed_weights_size.restype = sz
-    L.moe_pack_weights.argtypes = [vp, i32, i64, i64, i32, vp, sz, vp]
+    L.moe_pack_weights.argtypes = [vp, i32, i32, i64, i64, i32, vp, sz, vp]
     L.moe_pack_weights.restype = ctypes.c_int
     L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
                                    i32, i64, vp, i32, vp, i32, i64, i32, vp]
@@ -65,7 +65,7 @@ def _load():
     L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
                               i32, f32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
-    L.gmm_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.gmm_int8.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.gmm_int8.restype = ctypes.c_int
     return L
 
@@ -162,33 +162,36 @@ def moe_align_block_size(topk_ids, num_experts, block_m, sorted_token_ids=None,
     return sorted_token_ids, expert_ids, num_tokens_post_padded
 
 
-def moe_packed_weights_size(E, N, K, epilogue="none"):
-    return int(lib.moe_packed_weights_size(E, N, K, EPILOGUE[epilogue]))
+def moe_packed_weights_size(E, N, K, epilogue="none", dtype="bf16"):
+    return int(lib.moe_packed_weights_size(DTYPE[dtype], E, N, K, EPILOGUE[epilogue]))
 
 
 def moe_pack_weights(w, epilogue="none", packed=None, stream=None):
-    """Re-layout bf16 expert weights w [E, N, K] for the tile kernels (see
-    moe_pack_weights in include/moe.h).  Returns a PackedWeights holding the
-    packed bytes and the logical shape."""
+    """Re-layout expert weights w [E, N, K] (bf16, or int8 for gmm_int8) for
+    the tile kernels (see moe_pack_weights in include/moe.h).  Returns a
+    PackedWeights holding the packed bytes and the logical shape."""
     torch = _torch()
     E, N, K = w.shape
-    need = moe_packed_weights_size(E, N, K, epilogue)
+    dtype = {torch.bfloat16: "bf16", torch.int8: "i8"}.get(w.dtype)
+    if dtype is None:
+        raise TypeError("w must be bfloat16 or int8, got %s" % w.dtype)
+    need = moe_packed_weights_size(E, N, K, epilogue, dtype)
     if need == 0:
         raise MoeError("moe_packed_weights_size", -2)
     if packed is None:
         packed = torch.empty(need, dtype=torch.uint8, device=w.device)
     _check("moe_pack_weights", lib.moe_pack_weights(
-        _ptr(w, torch.bfloat16, "w"), E, N, K, EPILOGUE[epilogue],
+        _ptr(w, None, "w"), DTYPE[dtype], E, N, K, EPILOGUE[epilogue],
         _ptr(packed, torch.uint8, "packed"), packed.numel(), _stream(stream)))
-    return PackedWeights(packed, (E, N, K), epilogue)
+    return PackedWeights(packed, (E, N, K), epilogue, dtype)
 
 
 class PackedWeights:
     """Packed expert weights: `data` (uint8 device tensor) plus the logical
     [E, N, K] shape and the epilogue they were packed for."""
 
-    def __init__(self, data, shape, epilogue):
-        self.data, self.shape, self.epilogue = data, tuple(shape), epilogue
+    def __init__(self, data, shape, epilogue, dtype="bf16"):
+        self.data, self.shape, self.epilogue, self.dtype = data, tuple(shape), epilogue, dtype
 
     @property
     def device(self):
@@ -199,6 +202,8 @@ def _weights(B, epilogue, name):
     """(pointer, layout code, (E, N, K)) of plain or packed weights."""
     torch = _torch()
     if isinstance(B, PackedWeights):
+        if B.dtype != "bf16":
+            raise TypeError("%s holds packed %s weights, bf16 needed" % (name, B.dtype))
         if B.epilogue != epilogue:
             raise ValueError("%s was packed for epilogue %r, used with %r" % (name, B.epilogue, epilogue))
         return _ptr(B.data, torch.uint8, name), WEIGHTS["packed"], B.shape
@@ -276,15 +281,22 @@ def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,
 def gmm_int8(input, weights, scales_x, scales_w, expert_offsets, expert_sizes=None,
              output=None, stream=None):
     """INT8 grouped GEMM: input [M, K] int8 sorted by expert, weights [E, N, K]
-    int8, scales_x [M] f32, scales_w [E, N] f32, expert_offsets [E+1] int32.
-    Returns output [M, N] float16."""
+    int8 (or PackedWeights packed from them), scales_x [M] f32, scales_w [E, N]
+    f32, expert_offsets [E+1] int32.  Returns output [M, N] float16."""
     torch = _torch()
     M, K = input.shape
-    E, N, _ = weights.shape
+    if isinstance(weights, PackedWeights):
+        if weights.dtype != "i8" or weights.epilogue != "none":
+            raise TypeError("weights must be int8 weights packed with epilogue 'none'")
+        E, N, _ = weights.shape
+        w_ptr, w_layout = _ptr(weights.data, torch.uint8, "weights"), WEIGHTS["packed"]
+    else:
+        E, N, _ = weights.shape
+        w_ptr, w_layout = _ptr(weights, torch.int8, "weights"), WEIGHTS["plain"]
     if output is None:
         output = torch.empty((M, N), dtype=torch.float16, device=input.device)
     _check("gmm_int8", lib.gmm_int8(
-        _ptr(input, torch.int8, "input"), _ptr(weights, torch.int8, "weights"),
+        _ptr(input, torch.int8, "input"), w_ptr, w_layout,
         _ptr(scales_x, torch.float32, "scales_x"), _ptr(scales_w, torch.float32, "scales_w"),
         _ptr(expert_offsets, torch.int32, "expert_offsets"),
         _ptr(expert_sizes, torch.int32, "expert_sizes"), _ptr(output, torch.float16, "output"),

@@ -165,24 +165,38 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, 
                                       as_stream(stream)));
 }
 
-size_t moe_packed_weights_size(int32_t E, int64_t N, int64_t K, int32_t epilogue) {
-  if (E < 1 || E > MOE_MAX_EXPERTS || N < 16 || K < 8 || K % 8 != 0) return 0;
+size_t moe_packed_weights_size(int32_t dtype, int32_t E, int64_t N, int64_t K, int32_t epilogue) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
   if (epilogue != MOE_EPILOGUE_NONE && epilogue != MOE_EPILOGUE_SILU_MUL) return 0;
-  if (epilogue == MOE_EPILOGUE_SILU_MUL ? (N % 32 != 0) : (N % 16 != 0)) return 0;
+  int elem;
+  if (dtype == MOE_DTYPE_BF16) {
+    if (N < 16 || K < 8 || K % 8 != 0) return 0;
+    if (epilogue == MOE_EPILOGUE_SILU_MUL ? (N % 32 != 0) : (N % 16 != 0)) return 0;
+    elem = 2;
+  } else if (dtype == MOE_DTYPE_I8) {
+    if (epilogue != MOE_EPILOGUE_NONE) return 0;
+    if (N < 16 || N % 16 != 0 || K < 16 || K % 16 != 0 || K > 131072) return 0;
+    elem = 1;
+  } else {
+    return 0;
+  }
   const int silu = epilogue == MOE_EPILOGUE_SILU_MUL;
-  return (size_t)E * (size_t)moe::packed_tiles(N, silu) * (size_t)moe::packed_kstages(K, 2) *
+  return (size_t)E * (size_t)moe::packed_tiles(N, silu) * (size_t)moe::packed_kstages(K, elem) *
          (size_t)moe::kPackBlockBytes;
 }
 
-int moe_pack_weights(const void* w, int32_t E, int64_t N, int64_t K, int32_t epilogue, void* packed,
-                     size_t packed_bytes, void* stream) {
+int moe_pack_weights(const void* w, int32_t dtype, int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                     void* packed, size_t packed_bytes, void* stream) {
   if (epilogue != MOE_EPILOGUE_NONE && epilogue != MOE_EPILOGUE_SILU_MUL) return MOE_ERR_CONFIG;
-  const size_t need = moe_packed_weights_size(E, N, K, epilogue);
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_I8) return MOE_ERR_DTYPE;
+  if (dtype == MOE_DTYPE_I8 && epilogue != MOE_EPILOGUE_NONE) return MOE_ERR_CONFIG;
+  const size_t need = moe_packed_weights_size(dtype, E, N, K, epilogue);
   if (need == 0) return MOE_ERR_SHAPE;
   if (!w || !packed) return MOE_ERR_NULL;
   if (packed_bytes < need) return MOE_ERR_SHAPE;
   if (!aligned16(w) || !aligned16(packed)) return MOE_ERR_SHAPE;
-  return hip_status(moe::launch_pack_weights(w, E, N, K, epilogue == MOE_EPILOGUE_SILU_MUL, packed,
+  return hip_status(moe::launch_pack_weights(w, dtype == MOE_DTYPE_I8 ? 1 : 2, E, N, K,
+                                             epilogue == MOE_EPILOGUE_SILU_MUL, packed,
                                              as_stream(stream)));
 }
 
@@ -291,7 +305,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }
 
-int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
+int gmm_int8(const int8_t* input, const int8_t* weights, int32_t w_layout, const float* scales_x,
              const float* scales_w, const int32_t* expert_offsets, const int32_t* expert_sizes,
              void* output, int64_t M, int64_t K, int64_t N, int32_t E, void* stream) {
   (void)expert_sizes;   // the offsets decide; sizes are redundant
@@ -299,6 +313,7 @@ int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
   if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
   if (K < 16 || K % 16 != 0 || K > 131072) return MOE_ERR_SHAPE;
   if (N < 16 || N % 16 != 0) return MOE_ERR_SHAPE;
+  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
   if (!weights || !scales_w || !expert_offsets) return MOE_ERR_NULL;
   if (M > 0 && (!input || !scales_x || !output)) return MOE_ERR_NULL;
   if (M == 0) return MOE_OK;
@@ -306,7 +321,8 @@ int gmm_int8(const int8_t* input, const int8_t* weights, const float* scales_x,
     return MOE_ERR_SHAPE;
   const int64_t grid = ((M + 127) / 128 + E) * ((N + 127) / 128);
   if (grid >= INT32_MAX) return MOE_ERR_SHAPE;
-  moe::GmmI8Args a{input, weights, scales_x, scales_w, expert_offsets, output, M, K, N, E};
+  moe::GmmI8Args a{input, weights, w_layout == MOE_WEIGHTS_PACKED, scales_x, scales_w, expert_offsets,
+                   output, M, K, N, E};
   return hip_status(moe::launch_gmm_int8(a, as_stream(stream)));
 }
 

@@ -28,8 +28,8 @@ __host__ __device__ inline int64_t packed_kstages(int64_t K_elems, int elem_byte
   return (K_elems * elem_bytes + kPackStageBytes - 1) / kPackStageBytes;
 }
 
-hipError_t launch_pack_weights(const void* w, int E, int64_t N, int64_t K, int silu, void* packed,
-                               hipStream_t stream);
+hipError_t launch_pack_weights(const void* w, int elem_bytes, int E, int64_t N, int64_t K, int silu,
+                               void* packed, hipStream_t stream);
 
 struct MoeGemmArgs {
   const void* A;
@@ -67,7 +67,8 @@ hipError_t launch_topk_reduce(const void* y, int y_dtype, int64_t T, int topk, i
 
 struct GmmI8Args {
   const int8_t* X;
-  const int8_t* W;
+  const int8_t* W;        // [E, N, K] int8, or packed (w_packed)
+  int w_packed;
   const float* sx;
   const float* sw;
   const int32_t* offsets;

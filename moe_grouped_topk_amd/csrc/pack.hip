@@ -43,15 +43,15 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* w, int64_t N, 
 
 }  // namespace
 
-hipError_t launch_pack_weights(const void* w, int E, int64_t N, int64_t K, int silu, void* packed,
-                               hipStream_t stream) {
-  const int64_t NT = packed_tiles(N, silu), KS = packed_kstages(K, 2);
+hipError_t launch_pack_weights(const void* w, int elem_bytes, int E, int64_t N, int64_t K, int silu,
+                               void* packed, hipStream_t stream) {
+  const int64_t NT = packed_tiles(N, silu), KS = packed_kstages(K, elem_bytes);
   const int64_t nchunks = (int64_t)E * NT * KS * (kPackBlockBytes / 16);
   if (nchunks == 0) return hipSuccess;
   const int64_t want = (nchunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, stream,
-                     reinterpret_cast<const uint8_t*>(w), N, K * 2, silu, NT, KS, nchunks,
+                     reinterpret_cast<const uint8_t*>(w), N, K * elem_bytes, silu, NT, KS, nchunks,
                      reinterpret_cast<uint8_t*>(packed));
   return hipGetLastError();
 }

@@ -744,6 +744,7 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
 #define MOE_GMM_WM 2
 #endif
 typedef DmaCfg<256, 128, MOE_GMM_NSTAGE, MOE_GMM_WN, MOE_GMM_WM, MOE_GMM_OCC> GmmCfg;
+static_assert(GmmCfg::BN == kPackRows, "packed int8 weights are cut into tiles of BN rows");
 
 __global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kernel(GmmI8Args a) {
   typedef GmmCfg C;
@@ -824,11 +825,20 @@ __global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kern
   __syncthreads();
 
   const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W) + (int64_t)e * a.N * a.K;
+  // packed weights: this n-tile's blocks (tiles of kPackRows == BN rows)
+  const uint8_t* Wp = reinterpret_cast<const uint8_t*>(a.W) +
+                      ((int64_t)e * packed_tiles(a.N, 0) + nt) * packed_kstages(a.K, 1) *
+                          kPackBlockBytes;
   const uint8_t* rowp[C::NI];
+  uint32_t pk_mask = 0;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
-    const int r = (wave * C::NI + j) * 16 + (lane >> 2);
-    if (r < BN) {
+    const int q = wave * C::NI + j;
+    const int r = q * 16 + (lane >> 2);
+    if (r < BN && a.w_packed) {
+      rowp[j] = Wp + q * 1024 + lane * 16;
+      pk_mask |= 1u << j;
+    } else if (r < BN) {
       const int64_t n = n0 + r;
       rowp[j] = Wb + (n < a.N ? n : 0) * a.K;
     } else {
@@ -852,7 +862,7 @@ __global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kern
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
 
   const int live_m = row_hi - row0 < BM ? row_hi - row0 : BM;
-  mainloop_dma_live<C, 1>(smem, rowp, 0u, a.K, wrow, tcol0, live_m, acc);
+  mainloop_dma_live<C, 1>(smem, rowp, pk_mask, a.K, wrow, tcol0, live_m, acc);
 
   uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
   const int rsub = 4 * (lane >> 5);

@@ -98,6 +98,22 @@ def test_pack_layout(moe, dev, silu, N, K):
     assert (got == ref).all()
 
 
+@pytest.mark.parametrize("N,K", [(80, 48), (272, 208)])
+def test_pack_layout_int8(moe, dev, N, K):
+    """int8 weights: the same layout in bytes (64 int8 per stage).  Two int8
+    columns are viewed as one 16-bit element, which the bf16 reference lays
+    out identically."""
+    E = 2
+    rng = np.random.default_rng(7 * N + K)
+    W = rng.integers(-128, 128, size=(E, N, K), dtype=np.int8)
+    pw = moe.moe_pack_weights(torch.from_numpy(W).to(dev))
+    torch.cuda.synchronize()
+    got = pw.data.cpu().numpy().view(np.uint16)
+    ref = _packed_reference(W.view(np.uint16), False)
+    assert got.shape == ref.shape
+    assert (got == ref).all()
+
+
 def test_p1_worked_example(moe, dev, golden_dir):
     """[P1] 03.3 example embedded in the kernel's alignment: K padded from 3
     to 8 and N from 2 to 16 with zeros (the extra columns stay zero)."""

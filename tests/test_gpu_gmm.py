@@ -25,10 +25,11 @@ def moe(dev):
     return m
 
 
-def _run_and_check(moe, dev, M, K, N, E, sizes, seed, bar=BAR_INT8):
+def _run_and_check(moe, dev, M, K, N, E, sizes, seed, bar=BAR_INT8, layout="plain"):
     h, d = gmm_inputs(M, K, N, E, sizes, seed, dev)
     Y = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
-    moe.gmm_int8(d["xq"], d["wq"], d["sx"], d["sw"], d["off"], output=Y)
+    W = moe.moe_pack_weights(d["wq"]) if layout == "packed" else d["wq"]
+    moe.gmm_int8(d["xq"], W, d["sx"], d["sw"], d["off"], output=Y)
     torch.cuda.synchronize()
     got = Y.float().cpu().numpy()
     ref = oracle.gmm_int8(h["xq"], h["wq"], h["sx"], h["sw"], h["off"])
@@ -38,12 +39,14 @@ def _run_and_check(moe, dev, M, K, N, E, sizes, seed, bar=BAR_INT8):
     return got, ref, h, err
 
 
-def test_int8_workload_zipf(moe, dev):
+@pytest.mark.parametrize("layout", ["plain", "packed"])
+def test_int8_workload_zipf(moe, dev, layout):
     cfg = synth.CONFIGS["int8gmm"]
     sizes = synth.zipf_group_sizes(cfg.T, cfg.E, cfg.extra["zipf_s"], cfg.cid, 9)
     assert (sizes == 0).any() and (sizes == 1).any()
-    got, ref, h, err = _run_and_check(moe, dev, cfg.T, cfg.H, cfg.I, cfg.E, sizes, cfg.cid)
-    print("int8 gmm workload err=%.3e" % err)
+    got, ref, h, err = _run_and_check(moe, dev, cfg.T, cfg.H, cfg.I, cfg.E, sizes, cfg.cid,
+                                      layout=layout)
+    print("int8 gmm workload (%s weights) err=%.3e" % (layout, err))
 
 
 @pytest.mark.parametrize("sizes", [
@@ -52,14 +55,17 @@ def test_int8_workload_zipf(moe, dev):
     [1] * 9,                          # one row each
     [128, 128, 0, 256],               # exact tile multiples
     [0, 0, 0, 1]])
-def test_int8_edge_groups(moe, dev, sizes):
+@pytest.mark.parametrize("layout", ["plain", "packed"])
+def test_int8_edge_groups(moe, dev, sizes, layout):
     E = len(sizes)
-    _run_and_check(moe, dev, int(np.sum(sizes)), 256, 192, E, sizes, 50 + E)
+    _run_and_check(moe, dev, int(np.sum(sizes)), 256, 192, E, sizes, 50 + E, layout=layout)
 
 
-def test_int8_small_dims(moe, dev):
-    _run_and_check(moe, dev, 40, 16, 16, 3, [10, 20, 10], 61)
-    _run_and_check(moe, dev, 70, 144, 48, 2, [33, 37], 62)      # K tail, N < 128
+@pytest.mark.parametrize("layout", ["plain", "packed"])
+def test_int8_small_dims(moe, dev, layout):
+    _run_and_check(moe, dev, 40, 16, 16, 3, [10, 20, 10], 61, layout=layout)
+    _run_and_check(moe, dev, 70, 144, 48, 2, [33, 37], 62, layout=layout)   # K tail, N < 128
+    _run_and_check(moe, dev, 90, 80, 272, 2, [60, 30], 65, layout=layout)   # N past one tile
 
 
 def test_int8_empty(moe, dev):

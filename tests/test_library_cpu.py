@@ -54,7 +54,7 @@ def test_only_declared_symbols_exported(mod):
 def test_codes_match_binding(mod):
     d = _defines()
     assert d["MOE_DTYPE_F32"] == mod.DTYPE["f32"] and d["MOE_DTYPE_BF16"] == mod.DTYPE["bf16"]
-    assert d["MOE_DTYPE_F16"] == mod.DTYPE["f16"]
+    assert d["MOE_DTYPE_F16"] == mod.DTYPE["f16"] and d["MOE_DTYPE_I8"] == mod.DTYPE["i8"]
     assert d["MOE_SCORING_SOFTMAX"] == mod.SCORING["softmax"]
     assert d["MOE_SCORING_SIGMOID"] == mod.SCORING["sigmoid"]
 
@@ -196,24 +196,33 @@ def test_packed_weights_size_and_validation(mod):
     # ragged: N and K rounded up to whole tiles and stages (zero padded)
     assert mod.moe_packed_weights_size(3, 80, 40, "none") == 3 * 1 * 2 * 16384
     assert mod.moe_packed_weights_size(3, 96, 40, "silu_mul") == 3 * 1 * 2 * 16384
-    assert L.moe_packed_weights_size(3, 80, 44, 0) == 0                 # K % 8
-    assert L.moe_packed_weights_size(3, 48, 40, 1) == 0                 # silu: (N/2) % 16
-    assert L.moe_pack_weights(f, 3, 80, 40, 0, None, 1 << 20, None) == d["MOE_ERR_NULL"]
-    assert L.moe_pack_weights(f, 3, 80, 40, 0, f, 16384, None) == d["MOE_ERR_SHAPE"]
-    assert L.moe_pack_weights(f, 3, 80, 40, 7, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
-    assert L.moe_pack_weights(ctypes.c_void_p(264), 3, 80, 40, 0, f, 1 << 20,
+    # int8 GMM weights: 64 int8 per stage
+    assert mod.moe_packed_weights_size(32, 4096, 4096, "none", "i8") == 32 * 16 * 64 * 16384
+    assert mod.moe_packed_weights_size(2, 272, 80, "none", "i8") == 2 * 2 * 2 * 16384
+    assert L.moe_packed_weights_size(3, 2, 64, 64, 1) == 0               # int8 has no SiLU pairing
+    assert L.moe_packed_weights_size(3, 2, 64, 40, 0) == 0               # int8: K % 16
+    assert L.moe_packed_weights_size(1, 3, 80, 44, 0) == 0               # K % 8
+    assert L.moe_packed_weights_size(1, 3, 48, 40, 1) == 0               # silu: (N/2) % 16
+    assert L.moe_packed_weights_size(0, 3, 80, 40, 0) == 0               # f32 weights
+    assert L.moe_pack_weights(f, 1, 3, 80, 40, 0, None, 1 << 20, None) == d["MOE_ERR_NULL"]
+    assert L.moe_pack_weights(f, 1, 3, 80, 40, 0, f, 16384, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_pack_weights(f, 1, 3, 80, 40, 7, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_pack_weights(f, 2, 3, 80, 40, 0, f, 1 << 20, None) == d["MOE_ERR_DTYPE"]
+    assert L.moe_pack_weights(f, 3, 3, 80, 64, 1, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_pack_weights(ctypes.c_void_p(264), 1, 3, 80, 40, 0, f, 1 << 20,
                               None) == d["MOE_ERR_SHAPE"]
 
 
 def test_gmm_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)
-    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4008, 4096, 32, None) == d["MOE_ERR_SHAPE"]
-    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4096, 4100, 32, None) == d["MOE_ERR_SHAPE"]
-    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 4096, 4096, 0, None) == d["MOE_ERR_SHAPE"]
-    assert L.gmm_int8(f, None, f, f, f, None, f, 2048, 4096, 4096, 32, None) == d["MOE_ERR_NULL"]
-    assert L.gmm_int8(f, f, f, f, f, None, f, 2048, 1 << 20, 4096, 32, None) == d["MOE_ERR_SHAPE"]
-    assert L.gmm_int8(None, f, None, f, f, None, None, 0, 4096, 4096, 32, None) == 0   # M = 0
+    assert L.gmm_int8(f, f, 0, f, f, f, None, f, 2048, 4008, 4096, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, f, 0, f, f, f, None, f, 2048, 4096, 4100, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, f, 0, f, f, f, None, f, 2048, 4096, 4096, 0, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, None, 0, f, f, f, None, f, 2048, 4096, 4096, 32, None) == d["MOE_ERR_NULL"]
+    assert L.gmm_int8(f, f, 0, f, f, f, None, f, 2048, 1 << 20, 4096, 32, None) == d["MOE_ERR_SHAPE"]
+    assert L.gmm_int8(f, f, 2, f, f, f, None, f, 2048, 4096, 4096, 32, None) == d["MOE_ERR_CONFIG"]
+    assert L.gmm_int8(None, f, 0, None, f, f, None, None, 0, 4096, 4096, 32, None) == 0   # M = 0
 
 
 def test_forward_block_m_choice(mod):

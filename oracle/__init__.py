@@ -22,7 +22,8 @@ Sources, cited in every docstring by these tags (section names as on the page):
       "在 CPU 上运行 Triton" (seeded example printout), "练习" and answers.
 [GMM] Low-precision grouped GEMM article (www.pwwt.cn/news/5863887/):
       §2.1 definition, §2.2 arithmetic intensity, §2.3 error sources,
-      §3.1 interface, §3.2 quantisation, §5.3 INT8 accumulation.
+      §3.1 interface, §3.2 quantisation, §4 in-kernel quantisation,
+      §5.3 INT8 accumulation.
 
 Functions whose result has a plain definition are that definition written out;
 none of them is blocked, fused or reordered beyond what the passage states.
@@ -35,6 +36,8 @@ from .gemm import grouped_gemm_sorted, index_fused_gemm, silu, silu_and_mul
 from .layer import (moe_layer_expert_loop, moe_layer_token_loop,
                     moe_forward, dense_swiglu)
 from .gmm import gmm, gmm_int8, quantize_weight_per_channel, quantize_per_token
+from .quant_layer import (quantize_rows_f32, moe_layer_w8a8_expert_loop,
+                          moe_layer_w8a8_token_loop)
 from .bf16 import bf16_bits_to_f64
 
 __all__ = [
@@ -43,5 +46,6 @@ __all__ = [
     "grouped_gemm_sorted", "index_fused_gemm", "silu", "silu_and_mul",
     "moe_layer_expert_loop", "moe_layer_token_loop", "moe_forward",
     "dense_swiglu", "gmm", "gmm_int8", "quantize_weight_per_channel",
-    "quantize_per_token", "bf16_bits_to_f64",
+    "quantize_per_token", "bf16_bits_to_f64", "quantize_rows_f32",
+    "moe_layer_w8a8_expert_loop", "moe_layer_w8a8_token_loop",
 ]

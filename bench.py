@@ -97,6 +97,30 @@ def pack(torch, moe, w1, w2, timer):
     return p1, p2, ms
 
 
+def device_quantize(torch, w):
+    """Per-output-channel symmetric int8 of a device bf16 [E, N, K] tensor
+    (input preparation for the int8 layer), one expert at a time."""
+    E, N, K = w.shape
+    q = torch.empty((E, N, K), dtype=torch.int8, device=w.device)
+    s = torch.empty((E, N), dtype=torch.float32, device=w.device)
+    for e in range(E):
+        we = w[e].float()
+        amax = we.abs().amax(dim=1, keepdim=True)
+        se = torch.where(amax == 0, torch.ones_like(amax), amax / 127.0)
+        q[e] = torch.clamp(torch.round(we / se), -127, 127).to(torch.int8)
+        s[e] = se.squeeze(1)
+    return q, s
+
+
+def w8a8_weights(torch, moe, w1, w2):
+    """Packed int8 weights and their per-channel scales."""
+    w1q, s1 = device_quantize(torch, w1)
+    w2q, s2 = device_quantize(torch, w2)
+    p1, p2 = moe.moe_pack_weights(w1q, "silu_mul"), moe.moe_pack_weights(w2q, "none")
+    del w1q, w2q
+    return p1, s1, p2, s2
+
+
 def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     import synth
     cfg = synth.CONFIGS["prefill"]
@@ -119,6 +143,15 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     if plain:
         ms_plain = wall_steps(torch, step_plain, steps, warmup)
         res["plain_weights"] = dict(ms=ms_plain, tflops=flops / ms_plain * 1e-9)
+        # the same layer with int8 weights and int8 activations (moe_forward_w8a8)
+        q1, s1, q2, s2 = w8a8_weights(torch, moe, w1_plain, w2_plain)
+        ws8 = torch.empty(moe.moe_forward_w8a8_workspace_size(T, H, I, E, K), dtype=torch.uint8,
+                          device=dev)
+        ms8 = wall_steps(torch, lambda: moe.moe_forward_w8a8(x, g, q1, s1, q2, s2, K, out=out,
+                                                             workspace=ws8), steps, warmup)
+        res["w8a8"] = dict(ms=ms8, tops=flops / ms8 * 1e-9,
+                           frac_int8=flops / ms8 * 1e-9 / PEAK_INT8_TOPS)
+        del q1, q2, ws8
 
     # Per-kernel breakdown: the same five launches moe_forward makes, each
     # timed with HIP events on the stream they run on.
@@ -186,14 +219,30 @@ def bench_decode(torch, moe, dev, name, steps, warmup, timer):
     nbytes = n_exp * per_expert + 2 * T * H * 2
     mean, med = timer.run(lambda: run(w1, w2), max(steps, 10))
     ms_plain = wall_steps(torch, lambda: run(w1_plain, w2_plain), steps, warmup)
-    del w1, w2, w1_plain, w2_plain
+    del w1, w2
+    # int8 weights and activations: half the weight bytes
+    q1, s1, q2, s2 = w8a8_weights(torch, moe, w1_plain, w2_plain)
+    del w1_plain, w2_plain
+    torch.cuda.empty_cache()
+    ws8 = torch.empty(moe.moe_forward_w8a8_workspace_size(T, H, I, E, K), dtype=torch.uint8,
+                      device=dev)
+
+    def run8():
+        moe.moe_forward_w8a8(x, g, q1, s1, q2, s2, K, cfg.groups, cfg.topk_group, "softmax", True,
+                             cfg.scale, out=out, topk_ids_out=ids, workspace=ws8)
+
+    ms8 = wall_steps(torch, run8, steps, warmup)
+    nbytes8 = n_exp * (3 * I * H + 4 * (2 * I + H)) + 2 * T * H * 2
+    del q1, q2, ws8
     torch.cuda.empty_cache()
     return dict(ms=ms, event_mean_ms=mean, touched_experts=n_exp, bytes=nbytes,
                 gbs=nbytes / ms * 1e-6, frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
                 flops=6.0 * T * K * H * I, block_m=moe.moe_forward_block_m(T, E, K, "bf16", "packed"),
                 pack_weights_ms=pack_ms,
                 plain_weights=dict(ms=ms_plain, gbs=nbytes / ms_plain * 1e-6,
-                                   block_m=moe.moe_forward_block_m(T, E, K)))
+                                   block_m=moe.moe_forward_block_m(T, E, K)),
+                w8a8=dict(ms=ms8, bytes=nbytes8, gbs=nbytes8 / ms8 * 1e-6,
+                          frac_hbm=nbytes8 / ms8 * 1e-6 / PEAK_HBM_GBS))
 
 
 def bench_int8(torch, moe, dev, steps, warmup, timer):
@@ -347,7 +396,7 @@ def main():
                     block_m=pre["block_m"],
                     flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
     components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
-                  "prefill_pack_weights_ms": pre["pack_weights_ms"]}
+                  "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

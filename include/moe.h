@@ -58,7 +58,7 @@ extern "C" {
 #define MOE_DTYPE_F32   0
 #define MOE_DTYPE_BF16  1
 #define MOE_DTYPE_F16   2
-#define MOE_DTYPE_I8    3   /* int8 weights (moe_pack_weights / gmm_int8 only) */
+#define MOE_DTYPE_I8    3   /* int8 (packing, quantisation and the int8 paths only) */
 
 #define MOE_SCORING_SOFTMAX 0
 #define MOE_SCORING_SIGMOID 1
@@ -165,7 +165,7 @@ MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int
  * are zero.
  *
  *   w         [E, N, K] of dtype (read only).
- *   dtype     MOE_DTYPE_BF16 or MOE_DTYPE_I8 (int8 only with epilogue NONE).
+ *   dtype     MOE_DTYPE_BF16 or MOE_DTYPE_I8.
  *   epilogue  the epilogue of the GEMM that will use the packed weights.
  *   packed    output, at least moe_packed_weights_size(...) bytes.
  * Requirements: bf16 as moe_grouped_gemm for N and K; int8 as gmm_int8;
@@ -258,6 +258,53 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
                 float routed_scaling_factor, int32_t block_m, void* out,
                 float* topk_weights_out, int32_t* topk_ids_out, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* ---- INT8 activations and the INT8 fused layer ------------------------
+ * moe_quantize_rows: symmetric per-row int8 quantisation, [GMM] 3.2 (per
+ * token for activations): scale[r] = max|x[r, :]| / 127 (1 for an all-zero
+ * row), q[r, c] = clamp(round_half_even(x[r, c] / scale[r]), -127, 127).
+ * Computed in float32 with IEEE division, so the codes are a pure function
+ * of the row's float32 values.
+ *   x       [rows, ld] f32 or bf16 (x_dtype), first cols used.
+ *   q       [rows, cols] int8 out.      scales  [rows] f32 out.
+ * Requirements: cols % 8 == 0, ld >= cols, ld % 8 == 0, x and q 16-byte
+ * aligned.  rows = 0 is a no-op.
+ */
+MOE_API int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                              int64_t ld, int8_t* q, float* scales, void* stream);
+
+/* moe_forward_w8a8: moe_forward with int8 weights and int8 activations in
+ * both GEMMs (per-channel weight scales and per-token activation scales,
+ * [GMM] 3.2; exact int32 sums, [GMM] 5.3; activations quantised before
+ * their GEMM, [GMM] 4):
+ *   xq, sx = moe_quantize_rows(x)
+ *   h[pair] = silu(gate) * up, gate/up[n] = sx[t] * w1_scales[e, n] *
+ *             sum_k xq[t, k] * w1q[e, n, k]      (float32)
+ *   hq, sh = per-row int8 of h (one row per pair)
+ *   out[t] = sum_k w[t,k] * sh[pair] * w2_scales[e, n] * sum_j hq[j] * w2q[e, n, j]
+ * Routing, alignment and the final reduce are moe_forward's.
+ *   w1q [E, 2I, H] int8 and w1_scales [E, 2I] f32; w2q [E, H, I] int8 and
+ *   w2_scales [E, H] f32; with w_layout MOE_WEIGHTS_PACKED, w1q packed by
+ *   moe_pack_weights(MOE_DTYPE_I8, MOE_EPILOGUE_SILU_MUL) and w2q with
+ *   MOE_EPILOGUE_NONE.
+ *   x [T, H] bf16 or f32; out [T, H] in x's dtype.
+ *   block_m  0 (chosen, at least 64) or 64, 128, 256.
+ *   ws       at least moe_forward_w8a8_workspace_size(...) bytes, 256-byte
+ *            aligned.
+ * Requirements: H % 16 == 0, I % 16 == 0, H and I <= 131072, plus
+ * moe_route's; scale arrays 16-byte aligned.
+ */
+MOE_API size_t moe_forward_w8a8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
+                                               int32_t topk, int32_t block_m);
+
+MOE_API int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating,
+                             const int8_t* w1q, const float* w1_scales, const int8_t* w2q,
+                             const float* w2_scales, int32_t w_layout, int64_t T, int32_t H,
+                             int32_t I, int32_t E, int32_t topk, int32_t num_expert_group,
+                             int32_t topk_group, int32_t scoring, int32_t renormalize,
+                             float routed_scaling_factor, int32_t block_m, void* out,
+                             float* topk_weights_out, int32_t* topk_ids_out, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---- INT8 grouped GEMM -------------------------------------------------
  * gmm_int8: [GMM] 2.1 and 3.1.  The input rows are sorted by expert; rows

@@ -17,6 +17,7 @@ __all__ = [
     "moe_align_max_padded", "moe_align_block_size", "moe_grouped_gemm",
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
+    "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -66,6 +67,13 @@ def _load():
                               i32, f32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
     L.gmm_int8.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.moe_quantize_rows.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    L.moe_quantize_rows.restype = ctypes.c_int
+    L.moe_forward_w8a8_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.moe_forward_w8a8_workspace_size.restype = sz
+    L.moe_forward_w8a8.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_w8a8.restype = ctypes.c_int
     L.gmm_int8.restype = ctypes.c_int
     return L
 
@@ -302,3 +310,65 @@ def gmm_int8(input, weights, scales_x, scales_w, expert_offsets, expert_sizes=No
         _ptr(expert_sizes, torch.int32, "expert_sizes"), _ptr(output, torch.float16, "output"),
         M, K, N, E, _stream(stream)))
     return output
+
+
+def moe_quantize_rows(x, q=None, scales=None, stream=None):
+    """Symmetric per-row int8 quantisation of x [rows, cols] (f32 or bf16;
+    rows may be strided).  Returns (q [rows, cols] int8, scales [rows] float32)."""
+    torch = _torch()
+    rows, cols = x.shape
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with contiguous rows")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check("moe_quantize_rows", lib.moe_quantize_rows(
+        x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), _ptr(q, torch.int8, "q"),
+        _ptr(scales, torch.float32, "scales"), _stream(stream)))
+    return q, scales
+
+
+def moe_forward_w8a8_workspace_size(T, H, I, E, topk, block_m=0):
+    return int(lib.moe_forward_w8a8_workspace_size(T, H, I, E, topk, block_m))
+
+
+def _int8_weights(w, epilogue, name):
+    torch = _torch()
+    if isinstance(w, PackedWeights):
+        if w.dtype != "i8" or w.epilogue != epilogue:
+            raise TypeError("%s must be int8 weights packed for epilogue %r" % (name, epilogue))
+        return _ptr(w.data, torch.uint8, name), WEIGHTS["packed"], w.shape
+    return _ptr(w, torch.int8, name), WEIGHTS["plain"], tuple(w.shape)
+
+
+def moe_forward_w8a8(x, gating, w1q, w1_scales, w2q, w2_scales, topk, num_expert_group=1,
+                     topk_group=1, scoring="softmax", renormalize=True,
+                     routed_scaling_factor=1.0, block_m=0, out=None, topk_weights_out=None,
+                     topk_ids_out=None, workspace=None, stream=None):
+    """Fused-MoE layer with int8 weights (w1q [E, 2I, H], w2q [E, H, I], plain
+    int8 tensors or both PackedWeights) and per-channel f32 scales
+    (w1_scales [E, 2I], w2_scales [E, H]); activations are quantised per
+    token inside.  Returns out [T, H] in x's dtype."""
+    torch = _torch()
+    T, H = x.shape
+    w1_ptr, l1, (E, twoI, _) = _int8_weights(w1q, "silu_mul", "w1q")
+    w2_ptr, l2, _ = _int8_weights(w2q, "none", "w2q")
+    if l1 != l2:
+        raise ValueError("w1q and w2q must both be plain or both packed")
+    I = twoI // 2
+    if out is None:
+        out = torch.empty_like(x)
+    need = moe_forward_w8a8_workspace_size(T, H, I, E, topk, block_m)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_forward_w8a8", lib.moe_forward_w8a8(
+        _ptr(x, None, "x"), _dtype_code(x), _ptr(gating, torch.float32, "gating"),
+        w1_ptr, _ptr(w1_scales, torch.float32, "w1_scales"), w2_ptr,
+        _ptr(w2_scales, torch.float32, "w2_scales"), l1, T, H, I, E, topk,
+        num_expert_group, topk_group, SCORING[scoring], int(bool(renormalize)),
+        float(routed_scaling_factor), block_m, _ptr(out, x.dtype, "out"),
+        _ptr(topk_weights_out, torch.float32, "topk_weights_out"),
+        _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out

@@ -42,7 +42,14 @@ int64_t align_max_padded(int64_t P, int32_t E, int32_t B) {
 int check_gemm(const moe::MoeGemmArgs& a) {
   if (!a.B || !a.total) return MOE_ERR_NULL;
   if (a.max_padded > 0 && (!a.A || !a.C || !a.sorted_ids || !a.expert_ids)) return MOE_ERR_NULL;
-  if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16 && a.a_dtype != MOE_DTYPE_I8)
+    return MOE_ERR_DTYPE;
+  if (a.a_dtype == MOE_DTYPE_I8) {   // int8 tokens and weights (moe_forward_w8a8)
+    if (a.block_m < 64 || !a.a_scales || !a.b_scales) return MOE_ERR_CONFIG;
+    if (a.c_dtype != MOE_DTYPE_F32 && a.c_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+    if (a.K % 16 != 0 || a.lda % 16 != 0) return MOE_ERR_SHAPE;
+    if (!aligned16(a.b_scales)) return MOE_ERR_SHAPE;
+  }
   if (a.c_dtype != MOE_DTYPE_F32 && a.c_dtype != MOE_DTYPE_BF16 && a.c_dtype != MOE_DTYPE_F16)
     return MOE_ERR_DTYPE;
   if (a.epilogue != MOE_EPILOGUE_NONE && a.epilogue != MOE_EPILOGUE_SILU_MUL) return MOE_ERR_CONFIG;
@@ -51,7 +58,7 @@ int check_gemm(const moe::MoeGemmArgs& a) {
   if (!valid_block_m(a.block_m)) return MOE_ERR_CONFIG;
   if (a.block_m == 256 && a.a_dtype == MOE_DTYPE_F32) return MOE_ERR_CONFIG;
   if (a.a_rows == MOE_ROWS_PAIR && a.a_row_div < 1) return MOE_ERR_CONFIG;
-  if (a.b_packed && (a.block_m < 64 || a.a_dtype != MOE_DTYPE_BF16)) return MOE_ERR_CONFIG;
+  if (a.b_packed && (a.block_m < 64 || a.a_dtype == MOE_DTYPE_F32)) return MOE_ERR_CONFIG;
   if (a.E < 1 || a.N < 16 || a.K < 8 || a.K % 8 != 0) return MOE_ERR_SHAPE;
   const int64_t nout = a.epilogue == MOE_EPILOGUE_SILU_MUL ? a.N / 2 : a.N;
   if (a.epilogue == MOE_EPILOGUE_SILU_MUL ? (a.N % 32 != 0) : (a.N % 16 != 0)) return MOE_ERR_SHAPE;
@@ -108,6 +115,36 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
+  L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
+  L.bytes = off;
+  return L;
+}
+
+// Workspace of moe_forward_w8a8 (256-byte aligned pieces).
+struct W8a8Layout {
+  size_t w, ids, sorted, eids, total, xq, sx, h, hq, sh, y, bytes;
+  int64_t max_padded;
+  int block_m;
+};
+
+W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t block_m,
+                       int32_t x_dtype) {
+  W8a8Layout L{};
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, MOE_WEIGHTS_PACKED);
+  const int64_t P = T * topk;
+  L.max_padded = align_max_padded(P, E, L.block_m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+  L.w = take(sizeof(float) * (size_t)P);
+  L.ids = take(sizeof(int32_t) * (size_t)P);
+  L.sorted = take(sizeof(int32_t) * (size_t)L.max_padded);
+  L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
+  L.total = take(sizeof(int32_t));
+  L.xq = take((size_t)T * (size_t)H);
+  L.sx = take(sizeof(float) * (size_t)T);
+  L.h = take(sizeof(float) * (size_t)L.max_padded * (size_t)I);
+  L.hq = take((size_t)L.max_padded * (size_t)I);
+  L.sh = take(sizeof(float) * (size_t)L.max_padded);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.bytes = off;
   return L;
@@ -174,8 +211,8 @@ size_t moe_packed_weights_size(int32_t dtype, int32_t E, int64_t N, int64_t K, i
     if (epilogue == MOE_EPILOGUE_SILU_MUL ? (N % 32 != 0) : (N % 16 != 0)) return 0;
     elem = 2;
   } else if (dtype == MOE_DTYPE_I8) {
-    if (epilogue != MOE_EPILOGUE_NONE) return 0;
-    if (N < 16 || N % 16 != 0 || K < 16 || K % 16 != 0 || K > 131072) return 0;
+    if (N < 16 || K < 16 || K % 16 != 0 || K > 131072) return 0;
+    if (epilogue == MOE_EPILOGUE_SILU_MUL ? (N % 32 != 0) : (N % 16 != 0)) return 0;
     elem = 1;
   } else {
     return 0;
@@ -189,7 +226,6 @@ int moe_pack_weights(const void* w, int32_t dtype, int32_t E, int64_t N, int64_t
                      void* packed, size_t packed_bytes, void* stream) {
   if (epilogue != MOE_EPILOGUE_NONE && epilogue != MOE_EPILOGUE_SILU_MUL) return MOE_ERR_CONFIG;
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_I8) return MOE_ERR_DTYPE;
-  if (dtype == MOE_DTYPE_I8 && epilogue != MOE_EPILOGUE_NONE) return MOE_ERR_CONFIG;
   const size_t need = moe_packed_weights_size(dtype, E, N, K, epilogue);
   if (need == 0) return MOE_ERR_SHAPE;
   if (!w || !packed) return MOE_ERR_NULL;
@@ -211,6 +247,7 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   a.a_row_div = a_row_div < 1 ? 1 : a_row_div;
   if (a_rows == MOE_ROWS_PAIR && a_row_div < 1) return MOE_ERR_CONFIG;
   if (!valid_layout(b_layout)) return MOE_ERR_CONFIG;
+  if (a_dtype == MOE_DTYPE_I8) return MOE_ERR_DTYPE;   // int8 runs through moe_forward_w8a8
   a.B = B; a.b_packed = b_layout == MOE_WEIGHTS_PACKED; a.E = E; a.N = N; a.K = K;
   a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.total = num_tokens_post_padded;
   a.max_padded = max_padded; a.block_m = block_m; a.num_valid = num_valid_pairs;
@@ -300,6 +337,104 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
 
   st = enqueue_gemm(g1, s);
   if (st != MOE_OK) return st;
+  st = enqueue_gemm(g2, s);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
+}
+
+int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                      int8_t* q, float* scales, void* stream) {
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (rows < 0 || cols < 8 || cols % 8 != 0 || ld < cols || ld % 8 != 0) return MOE_ERR_SHAPE;
+  if (rows >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_quantize_rows(x, x_dtype, rows, cols, ld, nullptr, nullptr, 0, q,
+                                              scales, as_stream(stream)));
+}
+
+size_t moe_forward_w8a8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                       int32_t block_m) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
+  if (block_m != 0 && (!valid_block_m(block_m) || block_m < 64)) return 0;
+  size_t most = 0;
+  for (int32_t dt : {MOE_DTYPE_BF16, MOE_DTYPE_F32}) {
+    const size_t b = w8a8_layout(T, H, I, E, topk, block_m, dt).bytes;
+    most = b > most ? b : most;
+  }
+  return most;
+}
+
+int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const int8_t* w1q,
+                     const float* w1_scales, const int8_t* w2q, const float* w2_scales,
+                     int32_t w_layout, int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                     int32_t num_expert_group, int32_t topk_group, int32_t scoring,
+                     int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
+                     float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
+  if (block_m != 0 && (!valid_block_m(block_m) || block_m < 64)) return MOE_ERR_CONFIG;
+  if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0 || H > 131072 || I > 131072)
+    return MOE_ERR_SHAPE;
+  int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !gating || !w1q || !w2q || !w1_scales || !w2_scales || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1q) || !aligned16(w2q) || !aligned16(out) ||
+      !aligned16(w1_scales) || !aligned16(w2_scales))
+    return MOE_ERR_SHAPE;
+  const W8a8Layout L = w8a8_layout(T, H, I, E, topk, block_m, x_dtype);
+  if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
+  if (L.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
+
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  float* w = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(base + L.w);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(base + L.eids);
+  int32_t* total = reinterpret_cast<int32_t*>(base + L.total);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + L.xq);
+  float* sx = reinterpret_cast<float*>(base + L.sx);
+  float* h = reinterpret_cast<float*>(base + L.h);
+  int8_t* hq = reinterpret_cast<int8_t*>(base + L.hq);
+  float* sh = reinterpret_cast<float*>(base + L.sh);
+  void* y = base + L.y;
+  hipStream_t s = as_stream(stream);
+  const int64_t P = T * topk;
+  const bool packed = w_layout == MOE_WEIGHTS_PACKED;
+
+  moe::MoeGemmArgs g1{};
+  g1.A = xq; g1.a_dtype = MOE_DTYPE_I8; g1.lda = H; g1.a_rows = MOE_ROWS_PAIR; g1.a_row_div = topk;
+  g1.a_scales = sx; g1.B = w1q; g1.b_packed = packed; g1.b_scales = w1_scales;
+  g1.E = E; g1.N = 2 * (int64_t)I; g1.K = H;
+  g1.sorted_ids = sorted; g1.expert_ids = eids; g1.total = total; g1.max_padded = L.max_padded;
+  g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
+  g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_F32; g1.ldc = I;
+  g1.c_rows = MOE_ROWS_SORTED;
+  st = check_gemm(g1);
+  if (st != MOE_OK) return st;
+  moe::MoeGemmArgs g2 = g1;
+  g2.A = hq; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1; g2.a_scales = sh;
+  g2.B = w2q; g2.b_scales = w2_scales; g2.N = H; g2.K = I; g2.topk_weights = w;
+  g2.epilogue = MOE_EPILOGUE_NONE; g2.C = y; g2.c_dtype = x_dtype; g2.ldc = H;
+  g2.c_rows = MOE_ROWS_PAIR;
+  st = check_gemm(g2);
+  if (st != MOE_OK) return st;
+
+  hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
+                                     renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_align(ids, P, E, L.block_m, sorted, eids, total, L.max_padded, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_quantize_rows(x, x_dtype, T, H, H, nullptr, nullptr, 0, xq, sx, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  st = enqueue_gemm(g1, s);
+  if (st != MOE_OK) return st;
+  err = moe::launch_quantize_rows(h, MOE_DTYPE_F32, L.max_padded, I, I, sorted, total, P, hq, sh, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
   st = enqueue_gemm(g2, s);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));

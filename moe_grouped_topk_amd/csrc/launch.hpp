@@ -53,6 +53,10 @@ struct MoeGemmArgs {
   int c_dtype;            // 0 f32, 1 bf16, 2 f16
   int64_t ldc;
   int c_rows;             // 0 pair, 1 sorted
+  // int8 operands (a_dtype 3, B int8): exact int32 sums, then
+  //   value = sum * a_scales[A row] * b_scales[e * N + n]
+  const float* a_scales;  // indexed like A rows
+  const float* b_scales;  // [E, N]
 };
 
 // MFMA tile kernel, block_m 64 or 128.
@@ -78,5 +82,14 @@ struct GmmI8Args {
 };
 
 hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream);
+
+// Symmetric per-row int8 quantisation in float32: scale = max|row| / 127
+// (1 for an all-zero row), q = clamp(rint(x / scale), -127, 127).  x dtype
+// 0 f32 or 1 bf16, row stride ld elements.  With sorted_ids != nullptr only
+// rows r < *total whose sorted_ids[r] < num_valid are processed (the valid
+// rows of a sorted buffer); the others are left untouched.
+hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                const int32_t* sorted_ids, const int32_t* total, int64_t num_valid,
+                                int8_t* q, float* scales, hipStream_t stream);
 
 }  // namespace moe

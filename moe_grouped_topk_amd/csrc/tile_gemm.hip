@@ -553,15 +553,30 @@ __device__ __forceinline__ void wave_rows(int wn, int (&wrow)[RB]) {
 
 // Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and, for
 // g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
-template <int RB, int CB, int EPI, int CDT>
+// fp32 values of accumulator entries 4g .. 4g+3: the sums themselves (bf16
+// MFMA), or the exact int32 sums times the row scale and four channel
+// scales (int8 MFMA).
+__device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int g, float, const f32x4_t&) {
+  return f32x4_t{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+}
+__device__ __forceinline__ f32x4_t acc4(const i32x16_t& a, int g, float as, const f32x4_t& bs) {
+  return f32x4_t{(float)a[4 * g] * as * bs[0], (float)a[4 * g + 1] * as * bs[1],
+                 (float)a[4 * g + 2] * as * bs[2], (float)a[4 * g + 3] * as * bs[3]};
+}
+
+// Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and, for
+// g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
+template <int RB, int CB, int EPI, int CDT, int KIND>
 __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile& t,
-                                             const int* rowinfo, const int (&wrow)[RB],
-                                             int tcol0, const f32x16_t (&acc)[RB][CB]) {
+                                             const int* rowinfo, const int (&wrow)[RB], int tcol0,
+                                             const typename Mma<KIND>::acc_t (&acc)[RB][CB]) {
   const int lane = threadIdx.x & 63;
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
   constexpr int ce = ElemBytes<CDT>::value;
   const int rsub = 4 * (lane >> 5);
+  const float* bsc = KIND ? a.b_scales + (int64_t)t.e * a.N : nullptr;
+  const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int trow = tcol0 + cb * 32 + (lane & 31);
@@ -569,31 +584,41 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
     if (p < 0 || p >= a.num_valid) continue;
     const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + trow;
     const float w = a.topk_weights ? a.topk_weights[p] : 1.0f;
+    float as = 1.0f;
+    if constexpr (KIND != 0)
+      as = a.a_scales[a.a_rows == 0 ? (int64_t)(p / a.a_row_div) : t.s0 + trow];
     uint8_t* rowp = Cb + crow * a.ldc * ce;
     if (EPI) {
 #pragma unroll
       for (int j = 0; j < RB / 2; ++j) {
-        const f32x16_t gt = acc[j][cb], up = acc[j + RB / 2][cb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t col = t.c0 + wrow[j] + 8 * g + rsub;
-          if (col < Nout)
-            store4<CDT>(rowp + col * ce, silu_f32(gt[4 * g]) * up[4 * g] * w,
-                        silu_f32(gt[4 * g + 1]) * up[4 * g + 1] * w,
-                        silu_f32(gt[4 * g + 2]) * up[4 * g + 2] * w,
-                        silu_f32(gt[4 * g + 3]) * up[4 * g + 3] * w);
+          if (col < Nout) {
+            f32x4_t sg = one4, su = one4;
+            if constexpr (KIND != 0) {
+              sg = *reinterpret_cast<const f32x4_t*>(bsc + col);
+              su = *reinterpret_cast<const f32x4_t*>(bsc + Nout + col);
+            }
+            const f32x4_t gt = acc4(acc[j][cb], g, as, sg);
+            const f32x4_t up = acc4(acc[j + RB / 2][cb], g, as, su);
+            store4<CDT>(rowp + col * ce, silu_f32(gt[0]) * up[0] * w, silu_f32(gt[1]) * up[1] * w,
+                        silu_f32(gt[2]) * up[2] * w, silu_f32(gt[3]) * up[3] * w);
+          }
         }
       }
     } else {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const f32x16_t v = acc[rb][cb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int64_t col = t.c0 + wrow[rb] + 8 * g + rsub;
-          if (col < a.N)
-            store4<CDT>(rowp + col * ce, v[4 * g] * w, v[4 * g + 1] * w, v[4 * g + 2] * w,
-                        v[4 * g + 3] * w);
+          if (col < a.N) {
+            f32x4_t sc = one4;
+            if constexpr (KIND != 0) sc = *reinterpret_cast<const f32x4_t*>(bsc + col);
+            const f32x4_t v = acc4(acc[rb][cb], g, as, sc);
+            store4<CDT>(rowp + col * ce, v[0] * w, v[1] * w, v[2] * w, v[3] * w);
+          }
         }
       }
     }
@@ -677,11 +702,13 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
   mainloop<C, 0, true>(smem, src, wrow_bytes, wrow, tcol0, acc);
-  moe_epilogue<S::RB, S::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
+  moe_epilogue<S::RB, S::CB, EPI, CDT, 0>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
 // Direct-to-LDS variant (bf16 tokens).
-template <class C, int EPI, int CDT>
+//   KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights with
+//   per-row and per-channel scales applied in the epilogue.
+template <class C, int EPI, int CDT, int KIND>
 __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGemmArgs a) {
   constexpr int BN = C::BN, BM = C::BM;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -693,15 +720,16 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
-  const int64_t wrow_bytes = a.K * 2;
+  constexpr int eb = KIND ? 1 : 2;                 // operand element bytes
+  const int64_t wrow_bytes = a.K * eb;
   const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)t.e * a.N * wrow_bytes;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
-  const int64_t arow_bytes = a.lda * 2;
+  const int64_t arow_bytes = a.lda * eb;
   // packed weights: this tile's blocks; BN == kPackRows and the tile's
   // columns are the packed tile's (checked by the launcher)
   const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
                       ((int64_t)t.e * packed_tiles(a.N, EPI) + t.nt) *
-                          packed_kstages(a.K, 2) * kPackBlockBytes;
+                          packed_kstages(a.K, eb) * kPackBlockBytes;
   const uint8_t* rowp[C::NI];
   uint32_t pk_mask = 0;
 #pragma unroll
@@ -723,16 +751,16 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
   int wrow[C::RB];
   wave_rows<BN, C::WN, C::RB, EPI>(wn, wrow);
   const int tcol0 = wm * (BM / C::WM);
-  f32x16_t acc[C::RB][C::CB];
+  typename Mma<KIND>::acc_t acc[C::RB][C::CB];
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
-  mainloop_dma_live<C, 0>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+  mainloop_dma_live<C, KIND>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
                           live_rows<BM>(rowinfo, a.num_valid), acc);
-  moe_epilogue<C::RB, C::CB, EPI, CDT>(a, t, rowinfo, wrow, tcol0, acc);
+  moe_epilogue<C::RB, C::CB, EPI, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -896,7 +924,7 @@ hipError_t ensure_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <class C, int EPI, bool TF32, int CDT>
+template <class C, int EPI, bool TF32, int CDT, int KIND = 0>
 hipError_t launch_tile_t(const MoeGemmArgs& a, hipStream_t stream) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   const int64_t ncols = EPI ? C::BN / 2 : C::BN;
@@ -905,7 +933,7 @@ hipError_t launch_tile_t(const MoeGemmArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   void (*k)(MoeGemmArgs);
   if constexpr (TF32) k = moe_gemm_tile_kernel<C, EPI, CDT>;
-  else k = moe_gemm_dma_kernel<C, EPI, CDT>;
+  else k = moe_gemm_dma_kernel<C, EPI, CDT, KIND>;
   constexpr size_t lds = C::kBytes;
   const hipError_t st = ensure_lds(k, lds);
   if (st != hipSuccess) return st;
@@ -960,6 +988,13 @@ hipError_t launch_tile_bm(const MoeGemmArgs& a, hipStream_t s) {
   typedef typename TileFor<BM>::Dma D;
   static_assert(D::BN == kPackRows, "packed weights are cut into tiles of the kernel's BN rows");
   if (a.b_packed && a.a_dtype == 0) return hipErrorInvalidValue;   // rejected by the ABI layer
+  if (a.a_dtype == 3) {   // int8 tokens and weights; f32 or bf16 output
+    if (a.c_dtype == 0)
+      return a.epilogue ? launch_tile_t<D, 1, false, 0, 1>(a, s) : launch_tile_t<D, 0, false, 0, 1>(a, s);
+    if (a.c_dtype == 1)
+      return a.epilogue ? launch_tile_t<D, 1, false, 1, 1>(a, s) : launch_tile_t<D, 0, false, 1, 1>(a, s);
+    return hipErrorInvalidValue;
+  }
   if (a.a_dtype != 0)
     return a.epilogue ? launch_tile_c<D, 1, false>(a, s) : launch_tile_c<D, 0, false>(a, s);
   if constexpr (BM > 128) {

@@ -199,7 +199,7 @@ def test_packed_weights_size_and_validation(mod):
     # int8 GMM weights: 64 int8 per stage
     assert mod.moe_packed_weights_size(32, 4096, 4096, "none", "i8") == 32 * 16 * 64 * 16384
     assert mod.moe_packed_weights_size(2, 272, 80, "none", "i8") == 2 * 2 * 2 * 16384
-    assert L.moe_packed_weights_size(3, 2, 64, 64, 1) == 0               # int8 has no SiLU pairing
+    assert L.moe_packed_weights_size(3, 2, 64, 64, 1) == 2 * 1 * 1 * 16384   # int8 gate/up pairs
     assert L.moe_packed_weights_size(3, 2, 64, 40, 0) == 0               # int8: K % 16
     assert L.moe_packed_weights_size(1, 3, 80, 44, 0) == 0               # K % 8
     assert L.moe_packed_weights_size(1, 3, 48, 40, 1) == 0               # silu: (N/2) % 16
@@ -208,9 +208,45 @@ def test_packed_weights_size_and_validation(mod):
     assert L.moe_pack_weights(f, 1, 3, 80, 40, 0, f, 16384, None) == d["MOE_ERR_SHAPE"]
     assert L.moe_pack_weights(f, 1, 3, 80, 40, 7, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
     assert L.moe_pack_weights(f, 2, 3, 80, 40, 0, f, 1 << 20, None) == d["MOE_ERR_DTYPE"]
-    assert L.moe_pack_weights(f, 3, 3, 80, 64, 1, f, 1 << 20, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_pack_weights(f, 3, 3, 80, 64, 1, f, 1 << 20, None) == d["MOE_ERR_SHAPE"]  # N % 32
     assert L.moe_pack_weights(ctypes.c_void_p(264), 1, 3, 80, 40, 0, f, 1 << 20,
                               None) == d["MOE_ERR_SHAPE"]
+
+
+def test_quantize_rows_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    assert L.moe_quantize_rows(f, 3, 4, 64, 64, f, f, None) == d["MOE_ERR_DTYPE"]
+    assert L.moe_quantize_rows(f, 1, 4, 60, 64, f, f, None) == d["MOE_ERR_SHAPE"]    # cols % 8
+    assert L.moe_quantize_rows(f, 1, 4, 64, 32, f, f, None) == d["MOE_ERR_SHAPE"]    # ld < cols
+    assert L.moe_quantize_rows(f, 1, 4, 64, 68, f, f, None) == d["MOE_ERR_SHAPE"]    # ld % 8
+    assert L.moe_quantize_rows(None, 1, 4, 64, 64, f, f, None) == d["MOE_ERR_NULL"]
+    assert L.moe_quantize_rows(ctypes.c_void_p(264), 1, 4, 64, 64, f, f, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_quantize_rows(None, 1, 0, 64, 64, None, None, None) == 0          # no rows
+
+
+def test_forward_w8a8_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    ws = mod.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2)
+    assert ws > 0 and ws % 256 == 0
+    assert mod.lib.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2, 32) == 0   # block_m < 64
+    args = [f, 1, f, f, f, f, f, 0, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, f,
+            1 << 30, None]
+    a = list(args); a[1] = 2
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_DTYPE"]
+    a = list(args); a[7] = 5
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[18] = 32
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[9] = 120      # H % 16
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_SHAPE"]
+    a = list(args); a[4] = None     # w1_scales
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_NULL"]
+    a = list(args); a[22] = None
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_WORKSPACE"]
+    a = list(args); a[8] = 0        # T = 0
+    assert L.moe_forward_w8a8(*a) == 0
 
 
 def test_gmm_validation(mod):

@@ -11,7 +11,8 @@
 // no rounding of exp() can merge or swap two candidates.  A candidate is the
 // 64-bit value (key << 32) | (0xffffffff - index): its maximum is the largest
 // logit with the lowest index among equals.  Each top-k round is a lane-local
-// max over V values plus a 6-step xor-shuffle max across the wave.
+// max over V values plus a 6-step xor-shuffle max across the wave (group
+// stage); the final top-k is a radix select on the keys with ballots.
 // Weights (softmax + renormalise) are a softmax over the k selected logits
 // alone, since the full-row denominator cancels (section 七); the other
 // variants keep the full denominator or use the sigmoid scores.
@@ -74,25 +75,67 @@ route_kernel(const float* __restrict__ gating, int64_t T, int E, int topk,
     }
   }
 
-  // Top-k rounds ([GTK] 3.5, 八): lane r keeps the r-th pick.
-  int my_id = 0;
-  float my_x = 0.0f;
-  float top_x = 0.0f;
-  for (int r = 0; r < topk; ++r) {
-    uint64_t best = 0ull;
+  // Top-k ([GTK] 3.5, 八), by a radix select on the 32-bit keys: bit by bit
+  // from the top, keep the largest threshold th with at least topk keys >= th
+  // (ballot counts, no cross-lane data movement).  The picks are the keys
+  // above th plus, among the keys equal to th, the lowest indices.  Masked
+  // and absent experts hold key 0, which no finite or -inf logit reaches.
+  uint32_t key[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) best = cand[j] > best ? cand[j] : best;
-    best = wave_max_u64(best);
-    const int id = (int)(0xffffffffu - (uint32_t)best);
-    const float xv = key_float((uint32_t)(best >> 32));
-    if (r == 0) top_x = xv;
-    if (lane == r) { my_id = id; my_x = xv; }
-    if (id >= e0 && id < e0 + V) {
+  for (int j = 0; j < V; ++j) key[j] = (uint32_t)(cand[j] >> 32);
+  uint32_t th = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = th | (1u << b);
+    int n = 0;
 #pragma unroll
-      for (int j = 0; j < V; ++j)
-        if (e0 + j == id) cand[j] = 0ull;
-    }
+    for (int j = 0; j < V; ++j) n += __popcll(__ballot(key[j] >= c));
+    if (n >= topk) th = c;
   }
+  // keys strictly above th are all picked; ties at th fill the rest in index
+  // order (expert e = lane * V + j, so index order is lane order, then j)
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) above += __popcll(__ballot(key[j] > th));
+  int need = topk - above;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  bool pick[V];
+  uint64_t tie_before = 0;   // ties at th in lanes below this one (all j)
+#pragma unroll
+  for (int j = 0; j < V; ++j) tie_before += __popcll(__ballot(key[j] == th) & lt_mask);
+  int rank_tie = (int)tie_before;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const bool tie = key[j] == th && key[j] != 0u;
+    pick[j] = key[j] > th || (tie && rank_tie < need);
+    if (key[j] == th) ++rank_tie;
+  }
+  // Order the picks (key descending, index ascending): the rank of a pick is
+  // the number of picks ahead of it.  Picks are gathered into lanes 0..topk-1
+  // by their position in index order, then each compares against the others.
+  int before = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) before += __popcll(__ballot(pick[j]) & lt_mask);
+  __shared__ uint64_t s_pick[4][kWave];
+  const int wslot = (threadIdx.x / kWave) & 3;
+  int q = before;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (pick[j]) s_pick[wslot][q++] = cand[j];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const uint64_t mine_c = lane < topk ? s_pick[wslot][lane] : 0ull;
+  int rank = 0;
+  for (int r = 0; r < topk; ++r) rank += s_pick[wslot][r] > mine_c;
+  // lane r must end up with the r-th pick: move through LDS once more
+  __builtin_amdgcn_wave_barrier();
+  if (lane < topk) s_pick[wslot][rank] = mine_c;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const uint64_t my_c = lane < topk ? s_pick[wslot][lane] : 0ull;
+  const int my_id = (int)(0xffffffffu - (uint32_t)my_c);
+  const float my_x = key_float((uint32_t)(my_c >> 32));
+  // the first pick is the row's largest logit: the best expert's group is kept
+  const float top_x = key_float((uint32_t)(s_pick[wslot][0] >> 32));
 
   // Weights ([GTK] 3.1 and 3.6).
   float w;

@@ -130,18 +130,27 @@ MOE_API int moe_route(const float* gating, int64_t T, int32_t E, int32_t topk,
  *   num_tokens_post_padded [1] int32 out: total (a multiple of block_m).
  *   max_padded             capacity of sorted_token_ids; must be at least
  *                          moe_align_max_padded(num_pairs, E, block_m).
+ *   ws, ws_bytes           optional device workspace of at least
+ *                          moe_align_workspace_size(num_pairs, E) bytes
+ *                          (16-byte aligned): with it the alignment runs as
+ *                          two kernels (per-chunk counts, then placement);
+ *                          NULL runs one kernel with no workspace.  Both give
+ *                          identical outputs.
  * Null pointers are accepted only for buffers of capacity 0 (and topk_ids
  * when num_pairs = 0); num_tokens_post_padded is always written.
  * Errors: NULLs, num_pairs < 0 or >= 2^31, E outside [1, MOE_MAX_EXPERTS],
- * block_m outside [1, 1024], max_padded too small.  Expert ids outside
+ * block_m outside [1, 1024], max_padded too small, workspace too small
+ * (MOE_ERR_WORKSPACE).  Expert ids outside
  * [0, E) are outside the contract (they are dropped, not written).
  */
 MOE_API int64_t moe_align_max_padded(int64_t num_pairs, int32_t E, int32_t block_m);
 
+MOE_API size_t moe_align_workspace_size(int64_t num_pairs, int32_t E);
+
 MOE_API int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E,
                          int32_t block_m, int32_t* sorted_token_ids,
                          int32_t* expert_ids, int32_t* num_tokens_post_padded,
-                         int64_t max_padded, void* stream);
+                         int64_t max_padded, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- packed expert weights --------------------------------------------
  * moe_pack_weights: one-time re-layout of expert weights [E, N, K] (bf16 for

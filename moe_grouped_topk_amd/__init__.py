@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "MoeError", "LIB_PATH", "lib", "moe_status_string", "moe_route",
-    "moe_align_max_padded", "moe_align_block_size", "moe_grouped_gemm",
+    "moe_align_max_padded", "moe_align_workspace_size", "moe_align_block_size", "moe_grouped_gemm",
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
     "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
@@ -50,7 +50,9 @@ def _load():
     L.moe_route.restype = ctypes.c_int
     L.moe_align_max_padded.argtypes = [i64, i32, i32]
     L.moe_align_max_padded.restype = i64
-    L.moe_align_block_size.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, vp]
+    L.moe_align_workspace_size.argtypes = [i64, i32]
+    L.moe_align_workspace_size.restype = sz
+    L.moe_align_block_size.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, vp, sz, vp]
     L.moe_align_block_size.restype = ctypes.c_int
     L.moe_packed_weights_size.argtypes = [i32, i32, i64, i64, i32]
     L.moe_packed_weights_size.restype = sz
@@ -145,10 +147,17 @@ def moe_align_max_padded(num_pairs, num_experts, block_m):
     return int(lib.moe_align_max_padded(int(num_pairs), int(num_experts), int(block_m)))
 
 
+def moe_align_workspace_size(num_pairs, num_experts):
+    return int(lib.moe_align_workspace_size(int(num_pairs), int(num_experts)))
+
+
 def moe_align_block_size(topk_ids, num_experts, block_m, sorted_token_ids=None,
-                         expert_ids=None, num_tokens_post_padded=None, stream=None):
+                         expert_ids=None, num_tokens_post_padded=None, workspace=None,
+                         stream=None):
     """Returns (sorted_token_ids [max_padded] int32, expert_ids
-    [max_padded // block_m] int32, num_tokens_post_padded [1] int32)."""
+    [max_padded // block_m] int32, num_tokens_post_padded [1] int32).
+    workspace: optional uint8 device tensor of moe_align_workspace_size
+    bytes (selects the two-kernel path; same outputs)."""
     torch = _torch()
     P = topk_ids.numel()
     cap = moe_align_max_padded(P, num_experts, block_m)
@@ -166,7 +175,8 @@ def moe_align_block_size(topk_ids, num_experts, block_m, sorted_token_ids=None,
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
         _ptr(expert_ids, torch.int32, "expert_ids"),
         _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
-        sorted_token_ids.numel(), _stream(stream)))
+        sorted_token_ids.numel(), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
     return sorted_token_ids, expert_ids, num_tokens_post_padded
 
 

@@ -288,6 +288,220 @@ align_expert_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   if (blockIdx.x == 0 && tid == 0) *total_out = total;
 }
 
+// ---------------------------------------------------------------------------
+// Two-kernel variant with a workspace (moe_forward).  The pairs are cut into
+// chunks of `chunk` ids, one workgroup each.
+//   count: per-chunk histogram hist[c][e] into the workspace;
+//   place: every chunk reads all counts, scans the padded segment sizes, and
+//          places its own pairs: expert e's pairs of chunk c start at
+//          seg[e] + (pairs of e in chunks before c); inside the chunk each wave
+//          owns a contiguous run and ranks matching lanes with one ballot per
+//          bit of the expert id, so segments stay in ascending pair order.
+//          Placeholders, expert ids per block and the unused tail are split
+//          over the chunks.
+constexpr int kCountThreads = 256;
+constexpr int kPlaceThreads = 512;
+constexpr int kPlaceWaves = kPlaceThreads / kWave;
+
+__global__ void __launch_bounds__(kCountThreads)
+align_count_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int chunk,
+                   int32_t* __restrict__ hist) {
+  extern __shared__ int cnt[];
+  for (int e = threadIdx.x; e < E; e += kCountThreads) cnt[e] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
+  constexpr int kB = 8;   // ids per thread in flight at once
+  for (int base = c0; base < c1; base += kB * kCountThreads) {
+    int v[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int i = base + j * kCountThreads + (int)threadIdx.x;
+      v[j] = i < c1 ? topk_ids[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (v[j] >= 0 && v[j] < E) atomicAdd(&cnt[v[j]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kCountThreads) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Exclusive scan of one int per thread over a kPlaceThreads workgroup.
+__device__ __forceinline__ int place_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kPlaceWaves ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kPlaceWaves; off <<= 1) {
+      const int y = __shfl_up(w, off, kWave);
+      if (lane >= off) w += y;
+    }
+    if (lane < kPlaceWaves) tmp[kPlaceWaves + lane] = w;
+  }
+  __syncthreads();
+  total = tmp[2 * kPlaceWaves - 1];
+  const int before = wave ? tmp[kPlaceWaves + wave - 1] : 0;
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(kPlaceThreads)
+align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, int chunk, int nchunk,
+                   const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
+                   int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out,
+                   int max_padded) {
+  extern __shared__ int smem[];
+  int* seg = smem;                               // [E + 1] segment starts
+  int* cur = seg + (E + 1);                      // [kPlaceWaves][E] per-wave cursors
+  int* tot = cur + kPlaceWaves * E;              // [E] pairs per expert
+  int* tmp = tot + E;                            // [2 * kPlaceWaves]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int c = blockIdx.x;
+
+  // totals, and pairs of each expert in the chunks before this one
+  int padded[2] = {0, 0}, before_c[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    if (e < E) {
+      int t = 0, b = 0;
+#pragma unroll 16
+      for (int cc = 0; cc < nchunk; ++cc) {   // independent loads, issued together
+        const int h = hist[(int64_t)cc * E + e];
+        t += h;
+        b += cc < c ? h : 0;
+      }
+      tot[e] = t;
+      padded[q] = (t + B - 1) / B * B;
+      before_c[q] = b;
+    }
+  }
+  int total;
+  const int start = place_exclusive_scan(padded[0] + padded[1], tmp, total);
+  if (2 * tid < E) seg[2 * tid] = start;
+  if (2 * tid + 1 < E) seg[2 * tid + 1] = start + padded[0];
+  if (tid == 0) seg[E] = total;
+  for (int i = tid; i < kPlaceWaves * E; i += kPlaceThreads) cur[i] = 0;
+  __syncthreads();
+
+  // per-wave counts of this chunk, then each wave's first slot per expert
+  const int c0 = c * chunk, c1 = min(P, c0 + chunk);
+  const int run = (chunk + kPlaceWaves * kWave - 1) / (kPlaceWaves * kWave) * kWave;
+  const int r0 = min(c1, c0 + wave * run), r1 = min(c1, r0 + run);
+  // the wave's run is read once into registers, kR ids per lane at a time
+  constexpr int kR = 4;
+  const bool one_batch = r1 - r0 <= kR * kWave;
+  int v[kR];
+#pragma unroll
+  for (int j = 0; j < kR; ++j) {
+    const int i = r0 + j * kWave + lane;
+    v[j] = i < r1 ? topk_ids[i] : -1;
+  }
+  if (one_batch) {
+#pragma unroll
+    for (int j = 0; j < kR; ++j)
+      if (v[j] >= 0 && v[j] < E) atomicAdd(&cur[wave * E + v[j]], 1);
+  } else {
+    for (int i = r0 + lane; i < r1; i += kWave) {
+      const int e = topk_ids[i];
+      if (e >= 0 && e < E) atomicAdd(&cur[wave * E + e], 1);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    if (e < E) {
+      int run_e = seg[e] + before_c[q];
+      for (int w = 0; w < kPlaceWaves; ++w) {
+        const int n = cur[w * E + e];
+        cur[w * E + e] = run_e;
+        run_e += n;
+      }
+    }
+  }
+  __syncthreads();
+
+  // stable scatter: lanes with the same expert find each other by ballots
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = r0, j = 0; base < r1; base += kWave, ++j) {
+    const int i = base + lane;
+    int e;
+    if (one_batch) {   // j < kR here
+      e = v[0];
+#pragma unroll
+      for (int q = 1; q < kR; ++q) e = j == q ? v[q] : e;
+    } else {
+      e = i < r1 ? topk_ids[i] : -1;
+    }
+    const bool ok = e >= 0 && e < E;
+    uint64_t match = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    if (ok) {
+      const int pos = cur[wave * E + e];
+      sorted_ids[pos + __popcll(match & lt_mask)] = i;
+      if ((match >> lane) == 1ull) cur[wave * E + e] = pos + __popcll(match);   // highest lane
+    }
+  }
+
+  // placeholders and expert ids of the segments, experts split over chunks
+  for (int e = c; e < E; e += nchunk) {
+    const int s0 = seg[e], s1 = seg[e + 1];
+    for (int s = s0 + tot[e] + tid; s < s1; s += kPlaceThreads) sorted_ids[s] = P;
+    for (int b = s0 / B + tid; b < s1 / B; b += kPlaceThreads) expert_ids[b] = e;
+  }
+  const int stride = nchunk * kPlaceThreads, first = c * kPlaceThreads + tid;
+  for (int s = total + first; s < max_padded; s += stride) sorted_ids[s] = P;
+  for (int b = total / B + first; b < max_padded / B; b += stride) expert_ids[b] = -1;
+  if (c == 0 && tid == 0) *total_out = total;
+}
+
+int64_t align_ws_chunk(int64_t P) {
+  const int64_t c = (P + 1023) / 1024;   // at most 1024 chunks
+  return c < 2048 ? 2048 : c;
+}
+
+size_t align_ws_bytes(int64_t P, int E) {
+  const int64_t chunk = align_ws_chunk(P);
+  const int64_t n = P > 0 ? (P + chunk - 1) / chunk : 1;
+  return sizeof(int32_t) * (size_t)n * (size_t)E;
+}
+
+hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
+                           int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
+                           hipStream_t stream) {
+  const int64_t chunk = align_ws_chunk(P);
+  const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
+  hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
+                     stream, topk_ids, (int)P, E, (int)chunk, hist);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
+  if (lds > 65536) {
+    st = hipFuncSetAttribute((const void*)align_place_kernel,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (st != hipSuccess) return st;
+  }
+  hipLaunchKernelGGL(align_place_kernel, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
+                     (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
+                     (int)max_padded);
+  return hipGetLastError();
+}
+
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
                         int64_t max_padded, hipStream_t stream) {

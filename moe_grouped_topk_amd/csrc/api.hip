@@ -96,7 +96,7 @@ int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t 
 bool valid_layout(int32_t l) { return l == MOE_WEIGHTS_PLAIN || l == MOE_WEIGHTS_PACKED; }
 
 struct ForwardLayout {
-  size_t w, ids, sorted, eids, total, h, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, h, y, bytes;
   int64_t max_padded;
   int block_m;
 };
@@ -114,6 +114,7 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.sorted = take(sizeof(int32_t) * (size_t)L.max_padded);
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
+  L.hist = take(moe::align_ws_bytes(P, E));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.bytes = off;
@@ -122,7 +123,7 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
 
 // Workspace of moe_forward_w8a8 (256-byte aligned pieces).
 struct W8a8Layout {
-  size_t w, ids, sorted, eids, total, xq, sx, h, hq, sh, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, xq, sx, h, hq, sh, y, bytes;
   int64_t max_padded;
   int block_m;
 };
@@ -140,6 +141,7 @@ W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
   L.sorted = take(sizeof(int32_t) * (size_t)L.max_padded);
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
+  L.hist = take(moe::align_ws_bytes(P, E));
   L.xq = take((size_t)T * (size_t)H);
   L.sx = take(sizeof(float) * (size_t)T);
   L.h = take(sizeof(float) * (size_t)L.max_padded * (size_t)I);
@@ -184,9 +186,15 @@ int64_t moe_align_max_padded(int64_t num_pairs, int32_t E, int32_t block_m) {
   return align_max_padded(num_pairs, E, block_m);
 }
 
+size_t moe_align_workspace_size(int64_t num_pairs, int32_t E) {
+  if (num_pairs < 0 || num_pairs >= INT32_MAX || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  return moe::align_ws_bytes(num_pairs, E);
+}
+
 int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, int32_t block_m,
                          int32_t* sorted_token_ids, int32_t* expert_ids,
-                         int32_t* num_tokens_post_padded, int64_t max_padded, void* stream) {
+                         int32_t* num_tokens_post_padded, int64_t max_padded, void* ws,
+                         size_t ws_bytes, void* stream) {
   if (!num_tokens_post_padded) return MOE_ERR_NULL;
   if (num_pairs > 0 && !topk_ids) return MOE_ERR_NULL;
   // empty buffers (capacity 0) may come with null pointers
@@ -197,6 +205,12 @@ int moe_align_block_size(const int32_t* topk_ids, int64_t num_pairs, int32_t E, 
   if (block_m < 1 || block_m > 1024) return MOE_ERR_CONFIG;
   if (max_padded < align_max_padded(num_pairs, E, block_m) || max_padded >= INT32_MAX)
     return MOE_ERR_SHAPE;
+  if (ws) {
+    if (ws_bytes < moe::align_ws_bytes(num_pairs, E) || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_align_ws(topk_ids, num_pairs, E, block_m, sorted_token_ids,
+                                           expert_ids, num_tokens_post_padded, max_padded,
+                                           reinterpret_cast<int32_t*>(ws), as_stream(stream)));
+  }
   return hip_status(moe::launch_align(topk_ids, num_pairs, E, block_m, sorted_token_ids,
                                       expert_ids, num_tokens_post_padded, max_padded,
                                       as_stream(stream)));
@@ -315,7 +329,8 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_align(ids, P, E, L.block_m, sorted, eids, total, L.max_padded, s);
+  err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
+                             reinterpret_cast<int32_t*>(base + L.hist), s);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
   moe::MoeGemmArgs g1{};
@@ -427,7 +442,8 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_align(ids, P, E, L.block_m, sorted, eids, total, L.max_padded, s);
+  err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
+                             reinterpret_cast<int32_t*>(base + L.hist), s);
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = moe::launch_quantize_rows(x, x_dtype, T, H, H, nullptr, nullptr, 0, xq, sx, s);
   if (err != hipSuccess) return MOE_ERR_HIP;

@@ -15,6 +15,13 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,
                         int64_t max_padded, hipStream_t stream);
 
+// The same alignment in two kernels (per-chunk counts, then placement),
+// with a workspace of align_ws_bytes(P, E) bytes for the counts.
+size_t align_ws_bytes(int64_t P, int E);
+hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
+                           int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
+                           hipStream_t stream);
+
 // Packed expert weights (see moe_pack_weights in moe.h): tiles of 256 rows,
 // K stages of 64 bytes, one 16 KiB block per (expert, tile, stage).
 constexpr int kPackRows = 256;

@@ -125,23 +125,29 @@ def test_route_empty(moe, dev):
 
 # ---- alignment ------------------------------------------------------------
 
-def _align_gpu(moe, ids_np, E, B, dev):
+def _align_gpu(moe, ids_np, E, B, dev, ws=False):
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
-    s, e, tot = moe.moe_align_block_size(ids, E, B)
+    wsb = None
+    if ws:   # the two-kernel path; the buffers start as garbage on purpose
+        wsb = torch.full((moe.moe_align_workspace_size(ids.numel(), E),), 0x5a, dtype=torch.uint8,
+                         device=dev)
+    s, e, tot = moe.moe_align_block_size(ids, E, B, workspace=wsb)
     torch.cuda.synchronize()
     return s.cpu().numpy(), e.cpu().numpy(), int(tot.cpu().numpy()[0])
 
 
 def _check_align(moe, ids_np, E, B, dev):
-    s, e, total = _align_gpu(moe, ids_np, E, B, dev)
+    """Both alignment paths (workspace-free and two-kernel) against the oracle."""
     rs, re_, rtotal = oracle.moe_align_block_size(ids_np, E, B)
     P = np.asarray(ids_np).size
-    assert total == rtotal
-    assert (s[:total] == rs).all()
-    assert (e[:total // B] == re_).all()
-    assert (s[total:] == P).all()
-    assert (e[total // B:] == -1).all()
-    assert s.size == moe.moe_align_max_padded(P, E, B)
+    for ws in (False, True):
+        s, e, total = _align_gpu(moe, ids_np, E, B, dev, ws)
+        assert total == rtotal, ws
+        assert (s[:total] == rs).all(), ws
+        assert (e[:total // B] == re_).all(), ws
+        assert (s[total:] == P).all(), ws
+        assert (e[total // B:] == -1).all(), ws
+        assert s.size == moe.moe_align_max_padded(P, E, B)
 
 
 def test_align_msg_printout(moe, dev, golden_dir):

@@ -127,11 +127,17 @@ def test_route_validation(mod):
 def test_align_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)
-    assert L.moe_align_block_size(f, 10, 8, 4, None, f, f, 36, None) == d["MOE_ERR_NULL"]
-    assert L.moe_align_block_size(None, 10, 8, 4, f, f, f, 36, None) == d["MOE_ERR_NULL"]
-    assert L.moe_align_block_size(f, 10, 8, 4, f, f, f, 35, None) == d["MOE_ERR_SHAPE"]
-    assert L.moe_align_block_size(f, 10, 2000, 4, f, f, f, 1 << 20, None) == d["MOE_ERR_SHAPE"]
-    assert L.moe_align_block_size(f, 10, 8, 0, f, f, f, 36, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_align_block_size(f, 10, 8, 4, None, f, f, 36, None, 0, None) == d["MOE_ERR_NULL"]
+    assert L.moe_align_block_size(None, 10, 8, 4, f, f, f, 36, None, 0, None) == d["MOE_ERR_NULL"]
+    assert L.moe_align_block_size(f, 10, 8, 4, f, f, f, 35, None, 0, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_align_block_size(f, 10, 2000, 4, f, f, f, 1 << 20, None, 0,
+                                  None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_align_block_size(f, 10, 8, 0, f, f, f, 36, None, 0, None) == d["MOE_ERR_CONFIG"]
+    need = mod.moe_align_workspace_size(10, 8)
+    assert need >= 8 * 4
+    assert L.moe_align_block_size(f, 10, 8, 4, f, f, f, 36, f, need - 4,
+                                  None) == d["MOE_ERR_WORKSPACE"]
+    assert mod.moe_align_workspace_size(-1, 8) == 0
 
 
 def test_gemm_validation(mod):

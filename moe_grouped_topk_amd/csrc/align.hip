@@ -305,8 +305,10 @@ constexpr int kPlaceWaves = kPlaceThreads / kWave;
 
 __global__ void __launch_bounds__(kCountThreads)
 align_count_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int chunk,
-                   int32_t* __restrict__ hist) {
+                   int32_t* __restrict__ hist, int32_t* __restrict__ zero, int nzero) {
   extern __shared__ int cnt[];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += kCountThreads) zero[i] = 0;
   for (int e = threadIdx.x; e < E; e += kCountThreads) cnt[e] = 0;
   __syncthreads();
   const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
@@ -357,7 +359,7 @@ __global__ void __launch_bounds__(kPlaceThreads)
 align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, int chunk, int nchunk,
                    const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
                    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out,
-                   int max_padded) {
+                   int max_padded, int32_t* __restrict__ blk_start) {
   extern __shared__ int smem[];
   int* seg = smem;                               // [E + 1] segment starts
   int* cur = seg + (E + 1);                      // [kPlaceWaves][E] per-wave cursors
@@ -468,6 +470,8 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
   for (int s = total + first; s < max_padded; s += stride) sorted_ids[s] = P;
   for (int b = total / B + first; b < max_padded / B; b += stride) expert_ids[b] = -1;
   if (c == 0 && tid == 0) *total_out = total;
+  if (c == 0 && blk_start)
+    for (int e = tid; e <= E; e += kPlaceThreads) blk_start[e] = seg[e] / B;
 }
 
 int64_t align_ws_chunk(int64_t P) {
@@ -483,11 +487,11 @@ size_t align_ws_bytes(int64_t P, int E) {
 
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
-                           hipStream_t stream) {
+                           hipStream_t stream, int32_t* zero, int nzero, int32_t* blk_start) {
   const int64_t chunk = align_ws_chunk(P);
   const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
   hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
-                     stream, topk_ids, (int)P, E, (int)chunk, hist);
+                     stream, topk_ids, (int)P, E, (int)chunk, hist, zero, zero ? nzero : 0);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
@@ -498,7 +502,7 @@ hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int
   }
   hipLaunchKernelGGL(align_place_kernel, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
                      (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
-                     (int)max_padded);
+                     (int)max_padded, blk_start);
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t 
 bool valid_layout(int32_t l) { return l == MOE_WEIGHTS_PLAIN || l == MOE_WEIGHTS_PACKED; }
 
 struct ForwardLayout {
-  size_t w, ids, sorted, eids, total, hist, h, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, ctr, bstart, h, y, bytes;
   int64_t max_padded;
   int block_m;
 };
@@ -115,6 +115,8 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
   L.hist = take(moe::align_ws_bytes(P, E));
+  L.ctr = take(sizeof(int32_t) * (size_t)moe::fused_counters(L.max_padded / L.block_m));
+  L.bstart = take(sizeof(int32_t) * ((size_t)E + 1));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.bytes = off;
@@ -329,8 +331,15 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
+  // the tile path runs both GEMMs in one persistent launch, whose counters
+  // the alignment zeroes
+  const bool fused = L.block_m >= 64 && x_dtype == MOE_DTYPE_BF16;
+  int32_t* ctr = reinterpret_cast<int32_t*>(base + L.ctr);
+  const int64_t nblk_max = L.max_padded / L.block_m;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
-                             reinterpret_cast<int32_t*>(base + L.hist), s);
+                             reinterpret_cast<int32_t*>(base + L.hist), s, fused ? ctr : nullptr,
+                             moe::fused_counters(nblk_max),
+                             fused ? reinterpret_cast<int32_t*>(base + L.bstart) : nullptr);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
   moe::MoeGemmArgs g1{};
@@ -350,9 +359,15 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   st = check_gemm(g2);
   if (st != MOE_OK) return st;
 
-  st = enqueue_gemm(g1, s);
-  if (st != MOE_OK) return st;
-  st = enqueue_gemm(g2, s);
+  if (fused) {
+    moe::FusedArgs f{};
+    f.g1 = g1; f.g2 = g2; f.ctr = ctr; f.nblk_max = (int)nblk_max;
+    f.blk_start = reinterpret_cast<const int32_t*>(base + L.bstart);
+    st = hip_status(moe::launch_moe_ffn_fused(f, s));
+  } else {
+    st = enqueue_gemm(g1, s);
+    if (st == MOE_OK) st = enqueue_gemm(g2, s);
+  }
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }

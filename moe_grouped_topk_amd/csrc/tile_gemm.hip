@@ -240,6 +240,16 @@ __device__ __forceinline__ void mainloop(uint8_t* smem, const Src<C>& src, int64
   }
 }
 
+// threadIdx.x behind an empty asm.  The tile code derives its lane-dependent
+// values from this, so the persistent kernel recomputes them for every tile
+// instead of the compiler hoisting them out of its loop, where they would
+// hold registers across the whole K loop.
+__device__ __forceinline__ int tile_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // Direct-to-LDS K loop (bf16 / int8 operands).
 //
@@ -267,6 +277,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void dma16(uint32_t m0, const void* g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(g) : "memory", "m0");
+}
+
+// The same load at agent scope (sc1): it sees stores that other XCDs made
+// with agent-scope coherent stores, which their L2 may not have written back.
+__device__ __forceinline__ void dma16_coh(uint32_t m0, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
                :: "s"(m0), "v"(g) : "memory", "m0");
 }
 
@@ -329,12 +346,13 @@ struct DmaCfg {
 //   (the valid rows of a tile come first); the others are neither read from
 //   LDS nor multiplied.  Every wave still issues its loads and meets every
 //   barrier.
-template <class C, int KIND, int NCB>
+//   COH: token rows are read with agent-scope loads (dma16_coh).
+template <class C, int KIND, int NCB, bool COH = false>
 __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                              uint32_t pk_mask, int64_t kbytes,
                                              const int (&wrow)[C::RB], int tcol0,
                                              typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const uint32_t sbase = lds_addr(smem);
   const int chunk_pos = lane & 3;
   const int nk = (int)((kbytes + C::ROWB - 1) / C::ROWB);
@@ -350,7 +368,8 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
                               ? (int64_t)kt * kPackBlockBytes
                               : (koff + c * 16 < kbytes ? koff + c * 16 : 0);   // past K: row start
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (uint32_t)((wave * C::NI + j) * 1024));
-      dma16(m0, rowp[j] + off);
+      if (COH && wave * C::NI + j >= C::BN / 16) dma16_coh(m0, rowp[j] + off);
+      else dma16(m0, rowp[j] + off);
     }
   };
   // zero the chunks of a partial stage that lie past K (after its loads landed)
@@ -425,7 +444,7 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
 
 // Runs the K loop specialised for this wave's number of live column blocks
 // (wave-uniform), so the loop itself has no per-block branches.
-template <class C, int KIND>
+template <class C, int KIND, bool COH = false>
 __device__ __forceinline__ void mainloop_dma_live(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                                   uint32_t pk_mask, int64_t kbytes,
                                                   const int (&wrow)[C::RB], int tcol0,
@@ -435,14 +454,14 @@ __device__ __forceinline__ void mainloop_dma_live(uint8_t* smem, const uint8_t* 
   ncb = __builtin_amdgcn_readfirstlane(ncb < 0 ? 0 : (ncb > C::CB ? C::CB : ncb));
   pk_mask = __builtin_amdgcn_readfirstlane(pk_mask);
   if constexpr (C::CB >= 4) {
-    if (ncb == 4) return mainloop_dma<C, KIND, 4>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
-    if (ncb == 3) return mainloop_dma<C, KIND, 3>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 4) return mainloop_dma<C, KIND, 4, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 3) return mainloop_dma<C, KIND, 3, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
   }
   if constexpr (C::CB >= 2) {
-    if (ncb == 2) return mainloop_dma<C, KIND, 2>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 2) return mainloop_dma<C, KIND, 2, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
   }
-  if (ncb == 1) return mainloop_dma<C, KIND, 1>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
-  mainloop_dma<C, KIND, 0>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  if (ncb == 1) return mainloop_dma<C, KIND, 1, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  mainloop_dma<C, KIND, 0, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -477,30 +496,35 @@ struct MoeTile {
   int64_t s0, c0;
 };
 
-// Logical tile order.  Block-major numbering (L = blk * ntile + nt) gives
-// each expert one contiguous range of m_e * ntile tiles.  Inside that range
-// the tiles are renumbered n-tile-major (L = base + nt * m_e + mb), so the
-// m_e tiles that read the same weight slice are neighbours: they are
-// dispatched together and stream that slice through L2 once.  The workgroup
-// finds its expert's block range from one read of expert_ids around its
-// block-major block (a window of blockDim.x blocks).  Experts longer than
-// half the window keep block-major order; that choice depends only on the
-// expert, so every workgroup of an expert uses the same numbering and the
-// mapping stays a bijection.  Uses two barriers; s_win: 3 ints of LDS.
-template <int BN, int BM, int EPI>
-__device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t, int* s_win) {
+// Output tiles along N.
+template <int BN, int EPI>
+__device__ __forceinline__ int moe_ntiles(const MoeGemmArgs& a) {
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   const int64_t ncols = EPI ? BN / 2 : BN;            // output columns per tile
-  const int ntile = (int)((Nout + ncols - 1) / ncols);
-  const int nblk = *a.total / BM;
-  const int live = nblk * ntile;
-  if ((int)blockIdx.x >= live) return false;
-  const int L = xcd_remap((int)blockIdx.x, live);
+  return (int)((Nout + ncols - 1) / ncols);
+}
+
+// Tile of logical index L, 0 <= L < nblk * ntile.  Block-major numbering
+// (L = blk * ntile + nt) gives each expert one contiguous range of
+// m_e * ntile tiles.  Inside that range the tiles are renumbered
+// n-tile-major (L = base + nt * m_e + mb), so the m_e tiles that read the
+// same weight slice are neighbours: they are dispatched together and stream
+// that slice through L2 once.  The workgroup finds its expert's block range
+// from one read of expert_ids around its block-major block (a window of
+// blockDim.x blocks).  Experts longer than half the window keep block-major
+// order; that choice depends only on the expert, so every workgroup of an
+// expert uses the same numbering and the mapping stays a bijection.  Uses
+// two barriers; s_win: 3 ints of LDS.
+template <int BN, int BM, int EPI>
+__device__ __forceinline__ bool moe_tile_at(const MoeGemmArgs& a, int L, int nblk, MoeTile& t,
+                                            int* s_win) {
+  const int64_t ncols = EPI ? BN / 2 : BN;
+  const int ntile = moe_ntiles<BN, EPI>(a);
   const int bm = L / ntile;                           // block-major block
   const int half = (int)blockDim.x / 2;
-  const int idx = bm - half + (int)threadIdx.x;       // window [bm - half, bm + half)
+  const int idx = bm - half + (int)tile_tid();       // window [bm - half, bm + half)
   const int v = (idx >= 0 && idx < nblk) ? a.expert_ids[idx] : -2;
-  if (threadIdx.x == 0) { s_win[1] = INT32_MAX; s_win[2] = -1; }
+  if (tile_tid() == 0) { s_win[1] = INT32_MAX; s_win[2] = -1; }
   if (idx == bm) s_win[0] = v;
   __syncthreads();
   const int e = s_win[0];
@@ -522,6 +546,15 @@ __device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t, int* 
   t.s0 = (int64_t)t.blk * BM;
   t.c0 = (int64_t)t.nt * ncols;
   return t.e >= 0;
+}
+
+// Tile of this workgroup in a grid of one workgroup per tile; false if none.
+template <int BN, int BM, int EPI>
+__device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t, int* s_win) {
+  const int nblk = *a.total / BM;
+  const int live = nblk * moe_ntiles<BN, EPI>(a);
+  if ((int)blockIdx.x >= live) return false;
+  return moe_tile_at<BN, BM, EPI>(a, xcd_remap((int)blockIdx.x, live), nblk, t, s_win);
 }
 
 // Local weight row of tile row r (0 <= r < BN) -> global row of expert e,
@@ -570,7 +603,7 @@ template <int RB, int CB, int EPI, int CDT, int KIND>
 __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile& t,
                                              const int* rowinfo, const int (&wrow)[RB], int tcol0,
                                              const typename Mma<KIND>::acc_t (&acc)[RB][CB]) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tile_tid() & 63;
   const int64_t Nout = EPI ? a.N / 2 : a.N;
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
   constexpr int ce = ElemBytes<CDT>::value;
@@ -627,7 +660,7 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
 
 template <int BM>
 __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile& t, int* rowinfo) {
-  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+  for (int r = tile_tid(); r < BM; r += blockDim.x) {
     const int p = a.sorted_ids[t.s0 + r];
     rowinfo[r] = (p >= 0 && p < a.num_valid) ? p : -1;
   }
@@ -638,7 +671,7 @@ __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile
 // rowinfo: the tile's entries, -1 or a raw sorted id (>= num_valid = placeholder).
 template <int BM>
 __device__ __forceinline__ int live_rows(const int* rowinfo, int64_t num_valid) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tile_tid() & 63;
   uint32_t last = 0;
 #pragma unroll
   for (int r = lane; r < BM; r += 64) {
@@ -673,7 +706,7 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
   if (!moe_tile<BN, BM, EPI>(a, t, s_win)) return;
   load_rowinfo<BM>(a, t, rowinfo);
 
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = tile_tid(), wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int lrow = tid >> 3;
   const int64_t Nout = EPI ? a.N / 2 : a.N;
@@ -705,20 +738,82 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
   moe_epilogue<S::RB, S::CB, EPI, CDT, 0>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
-// Direct-to-LDS variant (bf16 tokens).
-//   KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights with
-//   per-row and per-channel scales applied in the epilogue.
-template <class C, int EPI, int CDT, int KIND>
-__global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGemmArgs a) {
-  constexpr int BN = C::BN, BM = C::BM;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int rowinfo[BM];
-  MoeTile t;
-  __shared__ int s_win[3];
-  if (!moe_tile<BN, BM, EPI>(a, t, s_win)) return;
-  load_rowinfo<BM>(a, t, rowinfo);   // one global round trip, then LDS
+// 16 bytes with one agent-scope (sc1) store.
+__device__ __forceinline__ void store16_coh(void* dst, const u32x4_t& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(v) : "memory");
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// SiLU epilogue (bf16 tokens and weights, bf16 output) that stages the tile
+// in LDS and writes whole 256-byte row segments with agent-scope stores.
+// Written straight from the MFMA layout, each store instruction would touch
+// 32 rows with 16 bytes each; agent-scope stores go through to memory and
+// would then move partial lines.  Reuses the K ring, which every wave has
+// finished reading at the first barrier.
+template <class C>
+__device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const MoeTile& t,
+                                                     const int* rowinfo,
+                                                     const int (&wrow)[C::RB], int tcol0,
+                                                     const f32x16_t (&acc)[C::RB][C::CB],
+                                                     uint8_t* smem) {
+  constexpr int RB = C::RB, CB = C::CB, BM = C::BM, HC = C::BN / 2;   // BM rows x HC columns
+  constexpr int PITCH = HC * 2 + 16;          // LDS bytes per token row
+  constexpr int LPR = HC * 2 / 16;            // lanes per row in the store phase
+  constexpr int RPP = C::THREADS / LPR;       // rows per store pass
+  static_assert(BM * PITCH <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0,
+                "staged epilogue shape");
+  const int tid = tile_tid(), lane = tid & 63;
+  const int rsub = 4 * (lane >> 5);
+  __syncthreads();
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int trow = tcol0 + cb * 32 + (lane & 31);
+    uint8_t* dst = smem + trow * PITCH;
+#pragma unroll
+    for (int j = 0; j < RB / 2; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wrow[j] + 8 * g + rsub;
+        const f32x16_t& gt = acc[j][cb];
+        const f32x16_t& up = acc[j + RB / 2][cb];
+        const uint2 v = make_uint2(
+            pack_bf16x2(silu_f32(gt[4 * g]) * up[4 * g], silu_f32(gt[4 * g + 1]) * up[4 * g + 1]),
+            pack_bf16x2(silu_f32(gt[4 * g + 2]) * up[4 * g + 2],
+                        silu_f32(gt[4 * g + 3]) * up[4 * g + 3]));
+        *reinterpret_cast<uint2*>(dst + col * 2) = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t Nout = a.N / 2;
+  uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
+  const int ch = tid % LPR;
+  const int64_t col = t.c0 + ch * 8;          // 8 columns; Nout is a multiple of 16
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += RPP) {
+    const int r = r0 + tid / LPR;
+    const int p = rowinfo[r];
+    if (p < 0 || p >= a.num_valid || col >= Nout) continue;
+    const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + r;
+    store16_coh(Cb + (crow * a.ldc + col) * 2,
+                *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16));
+  }
+}
+
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// One tile with the direct-to-LDS loop (rowinfo already loaded): operand
+// addresses, K loop, after_loop(), epilogue.  COH_A: token rows are read
+// with agent-scope loads; COH_C: the SiLU output is written with
+// agent-scope stores.
+template <class C, int EPI, int CDT, int KIND, bool COH_A = false, bool COH_C = false,
+          class Hook = NoHook>
+__device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile& t, uint8_t* smem,
+                                             const int* rowinfo, Hook after_loop = Hook()) {
+  constexpr int BN = C::BN, BM = C::BM;
+
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
   constexpr int eb = KIND ? 1 : 2;                 // operand element bytes
   const int64_t wrow_bytes = a.K * eb;
@@ -758,9 +853,240 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
-  mainloop_dma_live<C, KIND>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
-                          live_rows<BM>(rowinfo, a.num_valid), acc);
-  moe_epilogue<C::RB, C::CB, EPI, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc);
+  mainloop_dma_live<C, KIND, COH_A>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
+                                    live_rows<BM>(rowinfo, a.num_valid), acc);
+  after_loop();
+  if constexpr (COH_C) {
+    static_assert(EPI == 1 && CDT == 1 && KIND == 0, "coherent stores: bf16 SiLU output");
+    silu_epilogue_staged<C>(a, t, rowinfo, wrow, tcol0, acc, smem);
+  } else {
+    moe_epilogue<C::RB, C::CB, EPI, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc);
+  }
+}
+
+// Direct-to-LDS variant (bf16 tokens), one workgroup per tile.
+//   KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights with
+//   per-row and per-channel scales applied in the epilogue.
+template <class C, int EPI, int CDT, int KIND>
+__global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[C::BM];
+  MoeTile t;
+  __shared__ int s_win[3];
+  if (!moe_tile<C::BN, C::BM, EPI>(a, t, s_win)) return;
+  load_rowinfo<C::BM>(a, t, rowinfo);   // one global round trip, then LDS
+  run_dma_tile<C, EPI, CDT, KIND>(a, t, smem, rowinfo);
+}
+
+// ---------------------------------------------------------------------------
+// Both GEMMs of the layer in one persistent launch (bf16 tokens, direct-to-LDS
+// tiles).  Each workgroup takes tasks from work queues until all are done:
+//   gate_up tiles (g1, SiLU epilogue): h is written with agent-scope stores;
+//   down tiles (g2): each first waits until every gate_up tile of its token
+//     block has written its part of h, then reads h with agent-scope loads
+//     (h was written by other XCDs, whose L2 may still hold it dirty).
+// The token blocks are cut into one contiguous range per XCD, at expert
+// boundaries where that keeps the ranges balanced (queue_blocks).  Queue q
+// holds the gate_up tiles and, separately, the down tiles of range q, each in
+// expert-local n-tile-major order (fused_tile), so tiles that share a weight
+// slice run together on one XCD and share its L2.  A workgroup drains its own
+// XCD's gate_up queue, then its down queue (whose first blocks finished
+// first), then takes gate_up tiles, then down tiles, from the other queues.
+// Down tiles of a queue are taken only once its gate_up queue is empty: every
+// gate_up tile a down tile waits for has then been taken by a running
+// workgroup that waits for nothing, so every wait ends.  The next claim on the
+// own queue is issued after a tile's K loop and used after its epilogue, and
+// a gate_up tile is counted for its block at the start of the next task, once
+// its stores have completed, so neither costs a round trip of its own.
+// Counters, zeroed before the launch (fused_counters(nblk_max) ints):
+//   [0, 8) gate_up queue heads, [8, 16) down queue heads,
+//   [16, 16 + nblk_max) gate_up tiles finished per token block,
+//   [16 + nblk_max] set to 1 if a wait ran into its spin limit (a fault of
+//   the launch: down tiles then read h early).
+constexpr int kFusedSpinLimit = 1 << 20;   // about a second of polling
+constexpr int kFusedMaxExperts = 1024;
+
+// Token-block ranges of the queues: qb[q] .. qb[q + 1] for q < kNumXcd.  The
+// cut near q * nblk / 8 moves up to the next expert start when that is at
+// most nblk / 32 blocks away, else it splits the expert.  bs: [E + 1] first
+// block of each expert, then the number of blocks.
+__device__ __forceinline__ void queue_blocks(const int* bs, int E, int* qb) {
+  const int nblk = bs[E];
+  qb[0] = 0;
+  qb[kNumXcd] = nblk;
+  for (int q = 1; q < kNumXcd; ++q) {
+    const int target = (int)((int64_t)q * nblk / kNumXcd);
+    int lo = 0, hi = E;                        // the first e with bs[e] >= target
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (bs[mid] >= target) hi = mid; else lo = mid + 1;
+    }
+    const int slack = nblk / 32 > 1 ? nblk / 32 : 1;
+    qb[q] = bs[lo] - target <= slack ? bs[lo] : target;
+  }
+}
+
+// Tile v of queue range [b0, b1) (ntile tiles per block).  Inside the range
+// the tiles of each expert (clipped to the range) are numbered n-tile-major,
+// so the tiles of one weight slice are neighbours.  Every thread finds the
+// expert by a binary search of its own (no barrier).
+template <int BN, int BM, int EPI>
+__device__ __forceinline__ void fused_tile(const MoeGemmArgs& a, int v, int b0, int b1,
+                                           const int* bs, int E, MoeTile& t) {
+  const int ntile = moe_ntiles<BN, EPI>(a);
+  const int bm = b0 + v / ntile;             // block-major block
+  int lo = 0, hi = E;                        // the last e with bs[e] <= bm (empty experts skipped)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (bs[mid] <= bm) lo = mid; else hi = mid;
+  }
+  const int first = bs[lo] > b0 ? bs[lo] : b0;
+  const int end = bs[lo + 1] < b1 ? bs[lo + 1] : b1;
+  const int local = v - (first - b0) * ntile;
+  t.e = lo;
+  t.nt = local / (end - first);
+  t.blk = first + local % (end - first);
+  t.s0 = (int64_t)t.blk * BM;
+  t.c0 = (int64_t)t.nt * (EPI ? BN / 2 : BN);
+}
+
+__device__ __forceinline__ int xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & (kNumXcd - 1));
+}
+
+typedef const __attribute__((address_space(4))) FusedArgs* KArgPtr;
+
+__device__ __forceinline__ KArgPtr opaque(KArgPtr p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+// Two workgroups of 8 waves per CU need at most 128 VGPRs: ask for
+// OCC * waves / 4 waves per SIMD.
+template <class C, int CDT>
+__global__ void __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256)
+moe_ffn_fused_kernel(FusedArgs f) {
+  const KArgPtr kargs = (KArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int BN = C::BN, BM = C::BM;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[BM];
+  __shared__ int s_task;
+  __shared__ int s_bs[kFusedMaxExperts + 1];
+  __shared__ int s_qb[kNumXcd + 1];
+  const int E = f.g1.E;
+  for (int e = tile_tid(); e <= E; e += C::THREADS) s_bs[e] = f.blk_start[e];
+  __syncthreads();
+  if (tile_tid() == 0) queue_blocks(s_bs, E, s_qb);
+  __syncthreads();
+  const int ntile[2] = {moe_ntiles<BN, 1>(f.g1), moe_ntiles<BN, 0>(f.g2)};
+  const int xcd = xcc_id();
+  int* const heads = f.ctr;                   // [phase][queue]
+  int* const done = f.ctr + 2 * kNumXcd;
+  const int lane = tile_tid() & 63;
+  // tasks of queue q in phase p
+  auto count = [&](int p, int q) { return (s_qb[q + 1] - s_qb[q]) * ntile[p]; };
+  int own = 0;        // thread 0: the own queue's phase being drained (2: both empty)
+  int pre = -1;       // thread 0: head returned by the prefetched claim on (own, xcd)
+  int pending = -1;   // thread 0: block of the last gate_up tile, not yet counted
+  int pending_any = 0;   // every thread: the last task was a gate_up tile
+
+  for (;;) {
+    if (tile_tid() < 64) {   // wave 0 claims the next task: v | q << 24 | p << 27
+      int task = -1;
+      if (lane == 0) {
+        // the prefetched claim on the own queue, then the own queue's phases
+        while (own < 2) {
+          const int v = pre >= 0 ? pre
+                                 : __hip_atomic_fetch_add(heads + kNumXcd * own + xcd, 1,
+                                                          __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+          pre = -1;
+          if (v < count(own, xcd)) { task = v | (xcd << 24) | (own << 27); break; }
+          ++own;
+        }
+      }
+      task = __shfl(task, 0, 64);
+      while (task < 0) {
+        // steal: read all heads at once; gate_up tiles of any queue first, then
+        // down tiles of queues whose gate_up tiles have all been taken
+        const int q = lane & (kNumXcd - 1), p = (lane >> 3) & 1;
+        const int head = lane < 2 * kNumXcd
+                             ? __hip_atomic_load(heads + kNumXcd * p + q, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 0;
+        const bool left = lane < 2 * kNumXcd && head < count(p, q);
+        const uint32_t m = (uint32_t)__ballot(left);
+        const uint32_t m0 = m & 0xffu, m1 = (m >> 8) & ~m0 & 0xffu;
+        const uint32_t mm = m0 ? m0 : m1;
+        if (mm == 0) break;
+        const uint32_t rot = ((mm >> xcd) | (mm << (kNumXcd - xcd))) & ((1u << kNumXcd) - 1);
+        const int qc = (xcd + __builtin_ctz(rot)) & (kNumXcd - 1), pc = m0 ? 0 : 1;
+        int v = 0;
+        if (lane == 0)
+          v = __hip_atomic_fetch_add(heads + kNumXcd * pc + qc, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        v = __shfl(v, 0, 64);
+        if (v < count(pc, qc)) task = v | (qc << 24) | (pc << 27);
+      }
+      if (lane == 0) s_task = task;
+    }
+    // The previous gate_up tile's h stores have completed in every wave
+    // (they overlapped the claim): count the tile for its block.
+    if (__builtin_amdgcn_readfirstlane(pending_any)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tile_tid() == 0 && pending >= 0) {
+      __hip_atomic_fetch_add(done + pending, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pending = -1;
+    }
+    const int task = s_task;
+    if (task < 0) return;
+    const int phase = (task >> 27) & 1, tq = (task >> 24) & (kNumXcd - 1), v = task & 0xffffff;
+    const int b0 = s_qb[tq], b1 = s_qb[tq + 1];
+    // the next claim on the own queue goes out after the K loop; its
+    // latency hides behind the epilogue
+    auto prefetch = [&]() {
+      if (tile_tid() == 0 && own < 2)
+        pre = __hip_atomic_fetch_add(heads + kNumXcd * own + xcd, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // The GEMM arguments are re-read from the kernel-argument segment for
+    // every tile (the empty asm hides that they never change): kept live
+    // across the loop they would not fit the scalar registers.
+    const KArgPtr kp = opaque(kargs);
+    MoeTile t;
+    if (phase == 0) {
+      const MoeGemmArgs g1 = *(const MoeGemmArgs*)&kp->g1;
+      fused_tile<BN, BM, 1>(g1, v, b0, b1, s_bs, E, t);
+      load_rowinfo<BM>(g1, t, rowinfo);
+      run_dma_tile<C, 1, 1, 0, false, true>(g1, t, smem, rowinfo, prefetch);
+      if (tile_tid() == 0) pending = t.blk;
+      pending_any = 1;
+    } else {
+      const MoeGemmArgs g2 = *(const MoeGemmArgs*)&kp->g2;
+      fused_tile<BN, BM, 0>(g2, v, b0, b1, s_bs, E, t);
+      // the block's count is read in the same round trip as the row info
+      int cnt = ntile[0];
+      if (tile_tid() == 0)
+        cnt = __hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      load_rowinfo<BM>(g2, t, rowinfo);
+      if (tile_tid() == 0 && cnt < ntile[0]) {
+        int spins = 0;
+        while (__hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               ntile[0]) {
+          __builtin_amdgcn_s_sleep(8);
+          if (++spins == kFusedSpinLimit) {
+            __hip_atomic_store(done + f.nblk_max, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      run_dma_tile<C, 0, CDT, 0, true, false>(g2, t, smem, rowinfo, prefetch);
+      pending_any = 0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -783,7 +1109,7 @@ __global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kern
   __shared__ int scan_buf[NT];
   __shared__ int rowinfo[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int E = a.E;
   const int M = (int)a.M;
@@ -1012,6 +1338,64 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
     case 64: return launch_tile_bm<64>(a, stream);
     case 128: return launch_tile_bm<128>(a, stream);
     default: return launch_tile_bm<256>(a, stream);
+  }
+}
+
+int fused_counters(int64_t nblk_max) { return (int)(2 * kNumXcd + nblk_max + 1); }
+
+namespace {
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int BM, int CDT>
+hipError_t launch_fused_t(const FusedArgs& f, hipStream_t s) {
+  typedef typename TileFor<BM>::Dma C;
+  auto k = moe_ffn_fused_kernel<C, CDT>;
+  constexpr size_t lds = C::kBytes;
+  const hipError_t st = ensure_lds(k, lds);
+  if (st != hipSuccess) return st;
+  // one workgroup per slot: more would only find the queues empty
+  int64_t tasks = (f.g1.max_padded / BM) *
+                  ((f.g1.N / 2 + C::BN / 2 - 1) / (C::BN / 2) + (f.g2.N + C::BN - 1) / C::BN);
+  int64_t grid = (int64_t)device_cus() * C::OCC;
+  if (tasks < grid) grid = tasks;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(C::THREADS), lds, s, f);
+  return hipGetLastError();
+}
+
+template <int BM>
+hipError_t launch_fused_bm(const FusedArgs& f, hipStream_t s) {
+  switch (f.g2.c_dtype) {
+    case 0: return launch_fused_t<BM, 0>(f, s);
+    case 1: return launch_fused_t<BM, 1>(f, s);
+    default: return launch_fused_t<BM, 2>(f, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream) {
+  if (f.g1.a_dtype != 1 || f.g2.a_dtype != 1 || f.g1.c_dtype != 1 || !f.g1.epilogue ||
+      f.g1.topk_weights || f.g2.epilogue || f.g1.block_m != f.g2.block_m || !f.ctr ||
+      !f.blk_start || f.g1.E > kFusedMaxExperts)
+    return hipErrorInvalidValue;   // the ABI layer only builds valid pairs
+  switch (f.g1.block_m) {
+    case 64: return launch_fused_bm<64>(f, stream);
+    case 128: return launch_fused_bm<128>(f, stream);
+    case 256: return launch_fused_bm<256>(f, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -147,3 +147,27 @@ def test_decode_layer_sampled(moe, dev, name):
     assert (ids_p == ids).all()
     assert max_abs_rel(_out_host(out_p)[rows], ref) <= BAR_BF16
     del d["w1_packed"], d["w2_packed"]
+
+
+@pytest.mark.parametrize("block_m", [64, 128, 256])
+def test_layer_reuses_workspace(moe, dev, block_m):
+    """Consecutive layers on one workspace that starts full of garbage, with
+    different tokens and sizes: the counters of the persistent GEMM launch
+    start from zero in every call, and no call reads another call's h."""
+    from synth.configs import Config
+    cfgs = [Config(12, "reuse", T=T, H=256, I=384, E=16, topk=4, x_dtype="bf16", w_std=0.05,
+                   extra={"sub": i}) for i, T in enumerate([600, 150, 601])]
+    need = max(moe.moe_forward_workspace_size(c.T, c.H, c.I, c.E, c.topk, block_m) for c in cfgs)
+    ws = torch.full((need,), 0x5a, dtype=torch.uint8, device=dev)
+    for c in cfgs:
+        d = layer_inputs(c, dev)
+        ref = oracle.moe_layer_expert_loop(d["x_host"], d["w1_host"], d["w2_host"],
+                                           *oracle.grouped_topk(d["gating_host"], c.topk))
+        for layout in ("plain", "packed"):
+            w1, w2 = _packed(moe, d) if layout == "packed" else (d["w1"], d["w2"])
+            out = moe.moe_forward(d["x"], d["gating"], w1, w2, c.topk, block_m=block_m,
+                                  workspace=ws)
+            torch.cuda.synchronize()
+            err = max_abs_rel(_out_host(out), ref)
+            print("reuse T=%d %s block_m %d err=%.3e" % (c.T, layout, block_m, err))
+            assert err <= BAR_BF16

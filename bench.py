@@ -2,8 +2,9 @@
 
 A step is one moe_forward of the prefill-shaped layer (T=4096, H=2048,
 I=768, E=128, top-8 softmax with renormalisation): routing, alignment, the
-gate_up GEMM with SiLU*up, the down GEMM with the routing weight and the
-top-k reduce, on seeded synthetic inputs already resident in HBM.  The
+gate_up GEMM with SiLU*up and the down GEMM with the routing weight (one
+persistent launch), and the top-k reduce, on seeded synthetic inputs
+already resident in HBM.  The
 expert weights are in the packed tile layout (moe_pack_weights, done once
 before timing, as at model load; its time is reported).  The headline value
 is that step's throughput in TFLOP/s (6*T*topk*H*I algorithmic FLOPs,
@@ -32,10 +33,10 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
-# HBM bytes per launch of the gate_up kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled
-# by a 1 GiB copy (profiles/prefill_layer_packed_bm128.md).  Only valid for that kernel
-# configuration; reported as null for any other block size.
-GATE_UP_TRAFFIC = {"block_m": 128, "bytes": 1.230e9 + 0.053e9}
+# HBM bytes per launch of the fused gate_up + down kernel, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill layer).  Only
+# valid for that kernel configuration; null for any other block size or once the kernel changes.
+FFN_TRAFFIC = {"block_m": 128, "bytes": None}
 
 
 def log(msg):
@@ -153,24 +154,32 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
                            frac_int8=flops / ms8 * 1e-9 / PEAK_INT8_TOPS)
         del q1, q2, ws8
 
-    # Per-kernel breakdown: the same five launches moe_forward makes, each
-    # timed with HIP events on the stream they run on.
+    # Per-kernel breakdown: the launches moe_forward makes (route, the
+    # two-kernel alignment, both GEMMs in one persistent launch), each timed
+    # with HIP events on the stream they run on; the top-k reduce is the rest
+    # of the step.  The two GEMMs as separate launches are timed for reference.
     P = T * K
     bm = moe.moe_forward_block_m(T, E, K, "bf16", "packed")   # the block size used here
     w_t, ids_t = moe.moe_route(g, K)
-    sorted_ids, eids, total = moe.moe_align_block_size(ids_t, E, bm)
+    aws = torch.empty(moe.moe_align_workspace_size(P, E), dtype=torch.uint8, device=dev)
+    sorted_ids, eids, total = moe.moe_align_block_size(ids_t, E, bm, workspace=aws)
     cap = sorted_ids.numel()
     h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((P, H), dtype=torch.bfloat16, device=dev)   # y in x's dtype
+    fws = torch.empty(moe.moe_grouped_ffn_workspace_size(cap, E, bm), dtype=torch.uint8,
+                      device=dev)
     torch.cuda.synchronize()
     reps = max(steps, 10)
     parts = {
         "route": lambda: moe.moe_route(g, K, topk_weights=w_t, topk_ids=ids_t),
-        "align": lambda: moe.moe_align_block_size(ids_t, E, bm, sorted_ids, eids, total),
-        "gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
+        "align": lambda: moe.moe_align_block_size(ids_t, E, bm, sorted_ids, eids, total,
+                                                  workspace=aws),
+        "ffn_gate_up_and_down": lambda: moe.moe_grouped_ffn(
+            x, w1, w2, K, sorted_ids, eids, total, bm, w_t, h=h, y=y, workspace=fws),
+        "separate_gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
             x, w1, sorted_ids, eids, total, bm, P, a_rows="pair", a_row_div=K,
             epilogue="silu_mul", C=h, c_rows="sorted"),
-        "gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
+        "separate_gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
             h, w2, sorted_ids, eids, total, bm, P, a_rows="sorted", topk_weights=w_t,
             C=y, c_rows="pair"),
     }
@@ -180,16 +189,18 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
             fn()
         mean, med = timer.run(fn, reps)
         br[name] = dict(mean_ms=mean, median_ms=med)
-    # top-k reduce: run through moe_forward's own path is not separable from
-    # Python, so it is the step minus the other four (reported as such).
     gemm1_flops = 2.0 * P * H * 2 * I
     gemm2_flops = 2.0 * P * I * H
-    br["gemm1_gate_up_silu"]["tflops"] = gemm1_flops / br["gemm1_gate_up_silu"]["mean_ms"] * 1e-9
-    br["gemm2_down_weighted"]["tflops"] = gemm2_flops / br["gemm2_down_weighted"]["mean_ms"] * 1e-9
+    br["ffn_gate_up_and_down"]["tflops"] = (gemm1_flops + gemm2_flops) / \
+        br["ffn_gate_up_and_down"]["mean_ms"] * 1e-9
+    br["separate_gemm1_gate_up_silu"]["tflops"] = \
+        gemm1_flops / br["separate_gemm1_gate_up_silu"]["mean_ms"] * 1e-9
+    br["separate_gemm2_down_weighted"]["tflops"] = \
+        gemm2_flops / br["separate_gemm2_down_weighted"]["mean_ms"] * 1e-9
     br["remainder_reduce_and_gaps_ms"] = ms - sum(
-        br[k]["mean_ms"] for k in ("route", "align", "gemm1_gate_up_silu", "gemm2_down_weighted"))
+        br[k]["mean_ms"] for k in ("route", "align", "ffn_gate_up_and_down"))
     res["breakdown"] = br
-    res["gemm1_flops"] = gemm1_flops
+    res["ffn_flops"] = gemm1_flops + gemm2_flops
     res["block_m"] = bm
     res["inputs"] = (x_host, g_host, w1_plain, w2_plain)
     return res
@@ -386,15 +397,17 @@ def main():
 
     log("prefill layer")
     pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
-    g1 = pre["breakdown"]["gemm1_gate_up_silu"]
-    roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=g1["tflops"] / PEAK_BF16_TFLOPS,
-                    traffic=(GATE_UP_TRAFFIC["bytes"] if pre["block_m"] == GATE_UP_TRAFFIC["block_m"]
+    ffn = pre["breakdown"]["ffn_gate_up_and_down"]
+    roofline = dict(bound="mfma", achieved=ffn["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=ffn["tflops"] / PEAK_BF16_TFLOPS,
+                    traffic=(FFN_TRAFFIC["bytes"] if pre["block_m"] == FFN_TRAFFIC["block_m"]
                              else None),
                     traffic_unit="bytes per launch",
-                    kernel="moe_gemm_dma_kernel (gate_up GEMM, SiLU*up epilogue, packed weights)",
+                    kernel="moe_ffn_fused_kernel (gate_up with SiLU*up, then down with the "
+                           "routing weight, one persistent launch, packed weights; timed with "
+                           "its set-up kernel)",
                     block_m=pre["block_m"],
-                    flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
+                    flops_per_launch=pre["ffn_flops"], mean_ms=ffn["mean_ms"])
     components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}
     if args.copy_calibration:

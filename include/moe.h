@@ -227,12 +227,55 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
                      const float* topk_weights, int32_t epilogue, void* C,
                      int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream);
 
+/* ---- both GEMMs in one launch ------------------------------------------
+ * moe_grouped_ffn: the two fused_moe_kernel calls of [MSG] fused MoE
+ * (FusedMoeBackend.forward: gate_up with silu_and_mul, then down with the
+ * routing weight), as one persistent launch for bf16 tokens.  With
+ * moe_grouped_gemm's notation, for every valid entry p at sorted position s
+ * of a block of expert e:
+ *     h[s] = silu(x[p / topk] . W1[e][0:I]^T) * (x[p / topk] . W1[e][I:2I]^T)
+ *     y[p] = topk_weights[p] * (h[s] . W2[e]^T)
+ * i.e. moe_grouped_gemm(x, MOE_ROWS_PAIR, topk, w1, EPILOGUE_SILU_MUL -> h,
+ * MOE_ROWS_SORTED) followed by moe_grouped_gemm(h, MOE_ROWS_SORTED, w2,
+ * topk_weights -> y, MOE_ROWS_PAIR), with the same tiles and arithmetic (the
+ * results are bit-identical).  A down tile starts as soon as every gate_up
+ * tile of its token block has written its part of h, so the two GEMMs
+ * overlap instead of each ending with a partly idle device.
+ *
+ *   x        [T, H] bf16.
+ *   w1, w2   [E, 2I, H] and [E, H, I] bf16, both plain or both packed
+ *            (w_layout; w1 packed with MOE_EPILOGUE_SILU_MUL, w2 with
+ *            MOE_EPILOGUE_NONE).
+ *   sorted_token_ids / expert_ids / num_tokens_post_padded: as written by
+ *            moe_align_block_size for the T * topk pairs with the same
+ *            block_m; max_padded is the capacity of sorted_token_ids.
+ *   topk_weights  [T * topk] f32, pair order.
+ *   h        [max_padded, I] bf16 out (placeholder rows are not written).
+ *   y        [T * topk, H] out in y_dtype (F32, BF16 or F16).
+ *   block_m  64, 128 or 256.
+ *   ws       at least moe_grouped_ffn_workspace_size(max_padded, E,
+ *            block_m) bytes, 256-byte aligned; its contents need not be
+ *            initialised (a small set-up kernel runs first).
+ * Calls that share a workspace must not overlap in time.
+ * Requirements: H % 16 == 0, I % 16 == 0, E <= MOE_MAX_EXPERTS, x, w1, w2,
+ * h and y 16-byte aligned.  T = 0 is a no-op.
+ */
+MOE_API size_t moe_grouped_ffn_workspace_size(int64_t max_padded, int32_t E, int32_t block_m);
+
+MOE_API int moe_grouped_ffn(const void* x, int64_t T, int32_t H, int32_t topk, const void* w1,
+                            const void* w2, int32_t w_layout, int32_t E, int32_t I,
+                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                            const int32_t* num_tokens_post_padded, int64_t max_padded,
+                            int32_t block_m, const float* topk_weights, void* h, void* y,
+                            int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- whole layer -------------------------------------------------------
  * moe_forward: [MSG] fused MoE, FusedMoeBackend.forward, with routing per
  * moe_route: route -> align -> gate_up GEMM with silu(gate)*up in its
  * epilogue (intermediate h kept in sorted order, bf16) -> down GEMM times
  * the routing weight -> per-token sum over the topk slots, written in x's
  * dtype.  out[t] = sum_k w[t,k] * W2[e] (silu(W1g[e] x[t]) * (W1u[e] x[t])).
+ * With bf16 x and block_m >= 64 the two GEMMs run as in moe_grouped_ffn.
  *
  *   x        [T, H] bf16 or f32 (x_dtype); out [T, H] in the same dtype.
  *   gating   [T, E] f32 logits.

@@ -93,6 +93,10 @@ struct FusedArgs {
 };
 int fused_counters(int64_t nblk_max);
 hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream);
+// Counters and blk_start of a fused launch from expert_ids and the total
+// alone (one small kernel): ctr gets fused_counters(nblk_max) zeros.
+hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int block_m, int E,
+                           int64_t nblk_max, int32_t* blk_start, int32_t* ctr, hipStream_t stream);
 
 struct GmmI8Args {
   const int8_t* X;

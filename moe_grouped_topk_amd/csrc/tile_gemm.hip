@@ -346,12 +346,20 @@ struct DmaCfg {
 //   (the valid rows of a tile come first); the others are neither read from
 //   LDS nor multiplied.  Every wave still issues its loads and meets every
 //   barrier.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
 //   COH: token rows are read with agent-scope loads (dma16_coh).
-template <class C, int KIND, int NCB, bool COH = false>
+//   issued_all(): called once the last stage's loads have been issued; a
+//   memory operation it issues is newer than every load the remaining waits
+//   count, so it never holds them up.
+template <class C, int KIND, int NCB, bool COH = false, class Hook = NoHook>
 __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                              uint32_t pk_mask, int64_t kbytes,
                                              const int (&wrow)[C::RB], int tcol0,
-                                             typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
+                                             typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
+                                             Hook issued_all = Hook()) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const uint32_t sbase = lds_addr(smem);
   const int chunk_pos = lane & 3;
@@ -425,6 +433,7 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
   // Stage s goes to LDS buffer s % NSTAGE; all NSTAGE buffers start loading.
   const int pre = nk < C::NSTAGE ? nk : C::NSTAGE;
   for (int kt = 0; kt < pre; ++kt) issue(kt);
+  if (pre == nk) issued_all();
   u32x4_t a0[C::RB], b0[C::CB], a1[C::RB], b1[C::CB];
   publish(0, pre - 1);
   load_frags(0, 0, a0, b0);
@@ -435,7 +444,10 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
       const int last = (kt + C::NSTAGE - 1 < nk - 1) ? kt + C::NSTAGE - 1 : nk - 1;
       publish(kt + 1, last - (kt + 1));
       // every wave has finished reading stage kt: refill its buffer
-      if (kt + C::NSTAGE < nk) issue(kt + C::NSTAGE);
+      if (kt + C::NSTAGE < nk) {
+        issue(kt + C::NSTAGE);
+        if (kt + C::NSTAGE == nk - 1) issued_all();
+      }
       load_frags(kt + 1, 0, a0, b0);
     }
     mfmas(a1, b1);
@@ -444,24 +456,29 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
 
 // Runs the K loop specialised for this wave's number of live column blocks
 // (wave-uniform), so the loop itself has no per-block branches.
-template <class C, int KIND, bool COH = false>
+template <class C, int KIND, bool COH = false, class Hook = NoHook>
 __device__ __forceinline__ void mainloop_dma_live(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                                   uint32_t pk_mask, int64_t kbytes,
                                                   const int (&wrow)[C::RB], int tcol0,
                                                   int valid_rows,
-                                                  typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
+                                                  typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
+                                                  Hook issued_all = Hook()) {
   int ncb = (valid_rows - tcol0 + 31) / 32;
   ncb = __builtin_amdgcn_readfirstlane(ncb < 0 ? 0 : (ncb > C::CB ? C::CB : ncb));
   pk_mask = __builtin_amdgcn_readfirstlane(pk_mask);
   if constexpr (C::CB >= 4) {
-    if (ncb == 4) return mainloop_dma<C, KIND, 4, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
-    if (ncb == 3) return mainloop_dma<C, KIND, 3, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 4) return mainloop_dma<C, KIND, 4, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
+                                                 issued_all);
+    if (ncb == 3) return mainloop_dma<C, KIND, 3, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
+                                                 issued_all);
   }
   if constexpr (C::CB >= 2) {
-    if (ncb == 2) return mainloop_dma<C, KIND, 2, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 2) return mainloop_dma<C, KIND, 2, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
+                                                 issued_all);
   }
-  if (ncb == 1) return mainloop_dma<C, KIND, 1, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
-  mainloop_dma<C, KIND, 0, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  if (ncb == 1) return mainloop_dma<C, KIND, 1, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
+                                                 issued_all);
+  mainloop_dma<C, KIND, 0, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc, issued_all);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,12 +675,15 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
   }
 }
 
-template <int BM>
+// DRAIN: every thread also waits for all its earlier memory operations (the
+// previous tile's stores) before the barrier, in the shadow of these loads.
+template <int BM, bool DRAIN = false>
 __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile& t, int* rowinfo) {
   for (int r = tile_tid(); r < BM; r += blockDim.x) {
     const int p = a.sorted_ids[t.s0 + r];
     rowinfo[r] = (p >= 0 && p < a.num_valid) ? p : -1;
   }
+  if (DRAIN) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
 
@@ -799,18 +819,15 @@ __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const
   }
 }
 
-struct NoHook {
-  __device__ void operator()() const {}
-};
-
 // One tile with the direct-to-LDS loop (rowinfo already loaded): operand
-// addresses, K loop, after_loop(), epilogue.  COH_A: token rows are read
-// with agent-scope loads; COH_C: the SiLU output is written with
-// agent-scope stores.
+// addresses, K loop (issued_all() once its last loads are issued),
+// after_loop(), epilogue.  COH_A: token rows are read with agent-scope loads;
+// COH_C: the SiLU output is written with agent-scope stores.
 template <class C, int EPI, int CDT, int KIND, bool COH_A = false, bool COH_C = false,
-          class Hook = NoHook>
+          class Hook1 = NoHook, class Hook2 = NoHook>
 __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile& t, uint8_t* smem,
-                                             const int* rowinfo, Hook after_loop = Hook()) {
+                                             const int* rowinfo, Hook1 issued_all = Hook1(),
+                                             Hook2 after_loop = Hook2()) {
   constexpr int BN = C::BN, BM = C::BM;
 
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
@@ -854,7 +871,7 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
   mainloop_dma_live<C, KIND, COH_A>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
-                                    live_rows<BM>(rowinfo, a.num_valid), acc);
+                                    live_rows<BM>(rowinfo, a.num_valid), acc, issued_all);
   after_loop();
   if constexpr (COH_C) {
     static_assert(EPI == 1 && CDT == 1 && KIND == 0, "coherent stores: bf16 SiLU output");
@@ -894,10 +911,11 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGem
 // first), then takes gate_up tiles, then down tiles, from the other queues.
 // Down tiles of a queue are taken only once its gate_up queue is empty: every
 // gate_up tile a down tile waits for has then been taken by a running
-// workgroup that waits for nothing, so every wait ends.  The next claim on the
-// own queue is issued after a tile's K loop and used after its epilogue, and
-// a gate_up tile is counted for its block at the start of the next task, once
-// its stores have completed, so neither costs a round trip of its own.
+// workgroup that waits for nothing, so every wait ends.  The next claim on
+// the own queue is issued once a tile's last loads are issued and used after
+// its epilogue, and a gate_up tile is counted for its block once its stores
+// have completed, in the shadow of the next tile's row-info loads, so
+// neither costs a round trip of its own.
 // Counters, zeroed before the launch (fused_counters(nblk_max) ints):
 //   [0, 8) gate_up queue heads, [8, 16) down queue heads,
 //   [16, 16 + nblk_max) gate_up tiles finished per token block,
@@ -973,6 +991,10 @@ moe_ffn_fused_kernel(FusedArgs f) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[BM];
   __shared__ int s_task;
+  // thread 0's bookkeeping, kept in LDS rather than in registers of every lane
+  __shared__ int s_own;       // the own queue's phase being drained (2: both empty)
+  __shared__ int s_pre;       // head returned by the claim issued during the last tile
+  __shared__ int s_pending;   // block of the last gate_up tile, not yet counted
   __shared__ int s_bs[kFusedMaxExperts + 1];
   __shared__ int s_qb[kNumXcd + 1];
   const int E = f.g1.E;
@@ -980,23 +1002,27 @@ moe_ffn_fused_kernel(FusedArgs f) {
   __syncthreads();
   if (tile_tid() == 0) queue_blocks(s_bs, E, s_qb);
   __syncthreads();
-  const int ntile[2] = {moe_ntiles<BN, 1>(f.g1), moe_ntiles<BN, 0>(f.g2)};
+  const int nt1 = moe_ntiles<BN, 1>(f.g1), nt2 = moe_ntiles<BN, 0>(f.g2);
   const int xcd = xcc_id();
   int* const heads = f.ctr;                   // [phase][queue]
   int* const done = f.ctr + 2 * kNumXcd;
   const int lane = tile_tid() & 63;
   // tasks of queue q in phase p
-  auto count = [&](int p, int q) { return (s_qb[q + 1] - s_qb[q]) * ntile[p]; };
-  int own = 0;        // thread 0: the own queue's phase being drained (2: both empty)
-  int pre = -1;       // thread 0: head returned by the prefetched claim on (own, xcd)
-  int pending = -1;   // thread 0: block of the last gate_up tile, not yet counted
-  int pending_any = 0;   // every thread: the last task was a gate_up tile
+  auto count = [&](int p, int q) { return (s_qb[q + 1] - s_qb[q]) * (p ? nt2 : nt1); };
+  if (tile_tid() == 0) { s_own = 0; s_pre = -1; s_pending = -1; }
+  auto count_pending = [&]() {
+    if (tile_tid() == 0 && s_pending >= 0) {
+      __hip_atomic_fetch_add(done + s_pending, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_pending = -1;
+    }
+  };
 
   for (;;) {
     if (tile_tid() < 64) {   // wave 0 claims the next task: v | q << 24 | p << 27
       int task = -1;
       if (lane == 0) {
-        // the prefetched claim on the own queue, then the own queue's phases
+        // the claim issued during the last tile, then the own queue's phases
+        int own = s_own, pre = s_pre;
         while (own < 2) {
           const int v = pre >= 0 ? pre
                                  : __hip_atomic_fetch_add(heads + kNumXcd * own + xcd, 1,
@@ -1006,6 +1032,8 @@ moe_ffn_fused_kernel(FusedArgs f) {
           if (v < count(own, xcd)) { task = v | (xcd << 24) | (own << 27); break; }
           ++own;
         }
+        s_own = own;
+        s_pre = -1;
       }
       task = __shfl(task, 0, 64);
       while (task < 0) {
@@ -1032,24 +1060,23 @@ moe_ffn_fused_kernel(FusedArgs f) {
       }
       if (lane == 0) s_task = task;
     }
-    // The previous gate_up tile's h stores have completed in every wave
-    // (they overlapped the claim): count the tile for its block.
-    if (__builtin_amdgcn_readfirstlane(pending_any)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tile_tid() == 0 && pending >= 0) {
-      __hip_atomic_fetch_add(done + pending, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      pending = -1;
+    const int task = __builtin_amdgcn_readfirstlane(s_task);
+    if (task < 0) {
+      // once every wave's stores have completed, count the last gate_up tile
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      count_pending();
+      return;
     }
-    const int task = s_task;
-    if (task < 0) return;
     const int phase = (task >> 27) & 1, tq = (task >> 24) & (kNumXcd - 1), v = task & 0xffffff;
     const int b0 = s_qb[tq], b1 = s_qb[tq + 1];
-    // the next claim on the own queue goes out after the K loop; its
-    // latency hides behind the epilogue
-    auto prefetch = [&]() {
-      if (tile_tid() == 0 && own < 2)
-        pre = __hip_atomic_fetch_add(heads + kNumXcd * own + xcd, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    // the next claim on the own queue goes out once this tile's last loads
+    // are issued; its latency hides behind the end of the K loop
+    auto claim_ahead = [&]() {
+      if (tile_tid() == 0 && s_own < 2)
+        s_pre = __hip_atomic_fetch_add(heads + kNumXcd * s_own + xcd, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     };
     // The GEMM arguments are re-read from the kernel-argument segment for
     // every tile (the empty asm hides that they never change): kept live
@@ -1059,22 +1086,24 @@ moe_ffn_fused_kernel(FusedArgs f) {
     if (phase == 0) {
       const MoeGemmArgs g1 = *(const MoeGemmArgs*)&kp->g1;
       fused_tile<BN, BM, 1>(g1, v, b0, b1, s_bs, E, t);
-      load_rowinfo<BM>(g1, t, rowinfo);
-      run_dma_tile<C, 1, 1, 0, false, true>(g1, t, smem, rowinfo, prefetch);
-      if (tile_tid() == 0) pending = t.blk;
-      pending_any = 1;
+      // the last tile's stores complete in the shadow of the row-info loads;
+      // then the last gate_up tile is counted for its block
+      load_rowinfo<BM, true>(g1, t, rowinfo);
+      count_pending();
+      run_dma_tile<C, 1, 1, 0, false, true>(g1, t, smem, rowinfo, claim_ahead);
+      if (tile_tid() == 0) s_pending = t.blk;
     } else {
       const MoeGemmArgs g2 = *(const MoeGemmArgs*)&kp->g2;
       fused_tile<BN, BM, 0>(g2, v, b0, b1, s_bs, E, t);
       // the block's count is read in the same round trip as the row info
-      int cnt = ntile[0];
+      int cnt = nt1;
       if (tile_tid() == 0)
         cnt = __hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      load_rowinfo<BM>(g2, t, rowinfo);
-      if (tile_tid() == 0 && cnt < ntile[0]) {
+      load_rowinfo<BM, true>(g2, t, rowinfo);
+      count_pending();
+      if (tile_tid() == 0 && cnt < nt1) {
         int spins = 0;
-        while (__hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               ntile[0]) {
+        while (__hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt1) {
           __builtin_amdgcn_s_sleep(8);
           if (++spins == kFusedSpinLimit) {
             __hip_atomic_store(done + f.nblk_max, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1083,8 +1112,7 @@ moe_ffn_fused_kernel(FusedArgs f) {
         }
       }
       __syncthreads();
-      run_dma_tile<C, 0, CDT, 0, true, false>(g2, t, smem, rowinfo, prefetch);
-      pending_any = 0;
+      run_dma_tile<C, 0, CDT, 0, true, false>(g2, t, smem, rowinfo, claim_ahead);
     }
   }
 }
@@ -1342,6 +1370,48 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
 }
 
 int fused_counters(int64_t nblk_max) { return (int)(2 * kNumXcd + nblk_max + 1); }
+
+// Set-up of a fused launch from the alignment outputs alone: zero the
+// counters and find each expert's first block.  Blocks are in ascending
+// expert order, so a suffix minimum over the experts' first blocks gives an
+// expert without blocks the start of the next expert that has some (what the
+// fused kernel's binary search expects); bs[E] = the number of blocks.
+constexpr int kPrepThreads = 1024;
+static_assert(kPrepThreads >= kFusedMaxExperts, "one thread per expert");
+
+__global__ void __launch_bounds__(kPrepThreads)
+ffn_prep_kernel(const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ total, int B,
+                int E, int nblk_max, int32_t* __restrict__ bs, int32_t* __restrict__ ctr,
+                int nctr) {
+  __shared__ int start[kFusedMaxExperts];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nctr; i += kPrepThreads) ctr[i] = 0;
+  int nblk = *total / B;
+  nblk = nblk < nblk_max ? nblk : nblk_max;
+  if (tid < E) start[tid] = nblk;
+  __syncthreads();
+  for (int b = tid; b < nblk; b += kPrepThreads) {
+    const int e = expert_ids[b];
+    if (e >= 0 && e < E && (b == 0 || expert_ids[b - 1] != e)) start[e] = b;
+  }
+  __syncthreads();
+  for (int off = 1; off < E; off <<= 1) {
+    const int v = (tid < E && tid + off < E) ? min(start[tid], start[tid + off]) : 0;
+    __syncthreads();
+    if (tid < E && tid + off < E) start[tid] = v;
+    __syncthreads();
+  }
+  if (tid < E) bs[tid] = start[tid];
+  if (tid == 0) bs[E] = nblk;
+}
+
+hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int block_m, int E,
+                           int64_t nblk_max, int32_t* blk_start, int32_t* ctr, hipStream_t stream) {
+  if (E < 1 || E > kFusedMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_ids, total,
+                     block_m, E, (int)nblk_max, blk_start, ctr, fused_counters(nblk_max));
+  return hipGetLastError();
+}
 
 namespace {
 

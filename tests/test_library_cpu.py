@@ -169,6 +169,38 @@ def test_gemm_validation(mod):
     assert call(bl=1, a_dtype=0) == d["MOE_ERR_CONFIG"]          # packed needs bf16 A
 
 
+def test_grouped_ffn_workspace_and_validation(mod):
+    L, d = mod.lib, _defines()
+    f = ctypes.c_void_p(256)
+    # counters (16 + blocks + 1 ints, padded to 256 bytes), then E + 1 expert starts
+    assert mod.moe_grouped_ffn_workspace_size(49024, 128, 128) == 1792 + 4 * 129
+    assert mod.moe_grouped_ffn_workspace_size(512, 8, 32) == 0          # not a tile block size
+    assert mod.moe_grouped_ffn_workspace_size(512, 2048, 64) == 0       # too many experts
+    ws_need = mod.moe_grouped_ffn_workspace_size(512, 8, 64)
+    base = dict(x=f, T=64, H=128, topk=2, w1=f, w2=f, wl=0, E=8, I=256, s=f, e=f, tot=f,
+                maxp=512, bm=64, w=f, h=f, y=f, yd=1, ws=f, wsb=ws_need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.moe_grouped_ffn(a["x"], a["T"], a["H"], a["topk"], a["w1"], a["w2"], a["wl"],
+                                 a["E"], a["I"], a["s"], a["e"], a["tot"], a["maxp"], a["bm"],
+                                 a["w"], a["h"], a["y"], a["yd"], a["ws"], a["wsb"], None)
+    assert call(x=None) == d["MOE_ERR_NULL"]
+    assert call(w=None) == d["MOE_ERR_NULL"]
+    assert call(bm=32) == d["MOE_ERR_CONFIG"]          # tile block sizes only
+    assert call(wl=2) == d["MOE_ERR_CONFIG"]
+    assert call(yd=3) == d["MOE_ERR_DTYPE"]
+    assert call(H=100) == d["MOE_ERR_SHAPE"]
+    assert call(I=40) == d["MOE_ERR_SHAPE"]
+    assert call(maxp=500) == d["MOE_ERR_SHAPE"]        # not a multiple of block_m
+    assert call(E=2048) == d["MOE_ERR_SHAPE"]
+    assert call(ws=None) == d["MOE_ERR_WORKSPACE"]
+    assert call(wsb=ws_need - 4) == d["MOE_ERR_WORKSPACE"]
+    assert call(ws=ctypes.c_void_p(512 + 64)) == d["MOE_ERR_WORKSPACE"]   # alignment
+    assert call(h=ctypes.c_void_p(264)) == d["MOE_ERR_SHAPE"]             # misaligned h
+    assert call(T=0) == 0                                                  # no-op
+
+
 def test_forward_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)

@@ -885,7 +885,8 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
 //   KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights with
 //   per-row and per-channel scales applied in the epilogue.
 template <class C, int EPI, int CDT, int KIND>
-__global__ void __launch_bounds__(C::THREADS, C::OCC) moe_gemm_dma_kernel(MoeGemmArgs a) {
+__global__ void __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256)
+moe_gemm_dma_kernel(MoeGemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[C::BM];
   MoeTile t;
@@ -1120,15 +1121,18 @@ moe_ffn_fused_kernel(FusedArgs f) {
 // ---------------------------------------------------------------------------
 // INT8 GMM: rows [off[e], off[e+1]) of X use W[e]; fp16 output.
 #ifndef MOE_GMM_NSTAGE
+#define MOE_GMM_BM 128
 #define MOE_GMM_NSTAGE 3
 #define MOE_GMM_OCC 2
 #define MOE_GMM_WN 4
 #define MOE_GMM_WM 2
 #endif
-typedef DmaCfg<256, 128, MOE_GMM_NSTAGE, MOE_GMM_WN, MOE_GMM_WM, MOE_GMM_OCC> GmmCfg;
+typedef DmaCfg<256, MOE_GMM_BM, MOE_GMM_NSTAGE, MOE_GMM_WN, MOE_GMM_WM, MOE_GMM_OCC> GmmCfg;
 static_assert(GmmCfg::BN == kPackRows, "packed int8 weights are cut into tiles of BN rows");
 
-__global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC) gmm_i8_tile_kernel(GmmI8Args a) {
+// OCC workgroups per CU: ask for OCC * waves / 4 waves per SIMD.
+__global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC * GmmCfg::THREADS / 256)
+gmm_i8_tile_kernel(GmmI8Args a) {
   typedef GmmCfg C;
   typedef C S;
   constexpr int BN = C::BN, BM = C::BM, NT = C::THREADS;

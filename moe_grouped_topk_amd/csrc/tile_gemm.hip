@@ -819,6 +819,64 @@ __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const
   }
 }
 
+// Plain epilogue (bf16 or f16 output, bf16 MFMA) through LDS: the tile is
+// written into the drained K ring in [token row][column] order, then each
+// output row's BN columns go out as whole 16-byte pieces, 32 lanes per row.
+// Straight from the MFMA layout each store instruction would cover 32 rows
+// with 16 bytes each.  wr: this thread's row weight (threads < BM), read
+// before the K loop.
+template <class C, int CDT>
+__device__ __forceinline__ void plain_epilogue_staged(const MoeGemmArgs& a, const MoeTile& t,
+                                                      const int* rowinfo,
+                                                      const int (&wrow)[C::RB], int tcol0,
+                                                      const f32x16_t (&acc)[C::RB][C::CB],
+                                                      uint8_t* smem, float wr) {
+  constexpr int RB = C::RB, CB = C::CB, BM = C::BM, BN = C::BN;
+  constexpr int PITCH = BN * 2 + 16;          // LDS bytes per token row
+  constexpr int LPR = BN * 2 / 16;            // lanes per row in the store phase
+  constexpr int RPP = C::THREADS / LPR;       // rows per store pass
+  static_assert(BM * PITCH + BM * 4 <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0 &&
+                    BM <= C::THREADS && (CDT == 1 || CDT == 2),
+                "staged epilogue shape");
+  float* s_w = reinterpret_cast<float*>(smem + BM * PITCH);
+  const int tid = tile_tid(), lane = tid & 63;
+  const int rsub = 4 * (lane >> 5);
+  __syncthreads();                            // every wave has left the K ring
+  if (tid < BM) s_w[tid] = wr;
+  __syncthreads();
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int trow = tcol0 + cb * 32 + (lane & 31);
+    const float w = s_w[trow];
+    uint8_t* dst = smem + trow * PITCH;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& v = acc[rb][cb];
+        const float a0 = v[4 * g] * w, a1 = v[4 * g + 1] * w, a2 = v[4 * g + 2] * w,
+                    a3 = v[4 * g + 3] * w;
+        const uint2 o = CDT == 1 ? make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3))
+                                 : make_uint2(pack_f16x2(a0, a1), pack_f16x2(a2, a3));
+        *reinterpret_cast<uint2*>(dst + (wrow[rb] + 8 * g + rsub) * 2) = o;
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
+  const int ch = tid % LPR;
+  const int64_t col = t.c0 + ch * 8;          // 8 columns; N is a multiple of 16
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += RPP) {
+    const int r = r0 + tid / LPR;
+    const int p = rowinfo[r];
+    if (p < 0 || p >= a.num_valid || col >= a.N) continue;
+    const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + r;
+    *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) =
+        *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+  }
+}
+
 // One tile with the direct-to-LDS loop (rowinfo already loaded): operand
 // addresses, K loop (issued_all() once its last loads are issued),
 // after_loop(), epilogue.  COH_A: token rows are read with agent-scope loads;
@@ -870,12 +928,24 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+  // 16-bit output without SiLU goes out through LDS when the tile fits the ring
+  constexpr bool kStagedPlain = EPI == 0 && KIND == 0 && (CDT == 1 || CDT == 2) &&
+                                BM * (BN * 2 + 16) + BM * 4 <= C::kBytes && BM <= C::THREADS;
+  float wr = 1.0f;   // this thread's row weight, read while the K loop runs
+  if constexpr (kStagedPlain) {
+    if (tid < BM && a.topk_weights) {
+      const int p = rowinfo[tid];
+      if (p >= 0 && p < a.num_valid) wr = a.topk_weights[p];
+    }
+  }
   mainloop_dma_live<C, KIND, COH_A>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
                                     live_rows<BM>(rowinfo, a.num_valid), acc, issued_all);
   after_loop();
   if constexpr (COH_C) {
     static_assert(EPI == 1 && CDT == 1 && KIND == 0, "coherent stores: bf16 SiLU output");
     silu_epilogue_staged<C>(a, t, rowinfo, wrow, tcol0, acc, smem);
+  } else if constexpr (kStagedPlain) {
+    plain_epilogue_staged<C, CDT>(a, t, rowinfo, wrow, tcol0, acc, smem, wr);
   } else {
     moe_epilogue<C::RB, C::CB, EPI, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc);
   }

@@ -178,6 +178,68 @@ def test_gemm_pair_rows(moe, dev, B, layout, epilogue, c_dtype):
     assert max_abs_rel(got, ref) <= _tol(c_dtype)
 
 
+def _selector(E, N, H, scale_of_expert):
+    """bf16 weights with one nonzero per output column: B[e, n, (3n + e) % H]
+    = scale_of_expert(e).  Every output is then one exact product."""
+    Bw = np.zeros((E, N, H), np.float32)
+    n = np.arange(N)
+    for e in range(E):
+        Bw[e, n, (3 * n + e) % H] = scale_of_expert(e)
+    return synth.f32_to_bf16_bits(Bw)
+
+
+@pytest.mark.parametrize("B,layout", CASES)
+@pytest.mark.parametrize("c_dtype", [torch.bfloat16, torch.float16])
+def test_gemm_output_rounding_exact(moe, dev, B, layout, c_dtype):
+    """16-bit outputs are the round-to-nearest-even of the float32 result,
+    bit for bit.  With a selector weight each output is a * c_e * w, where a
+    (bf16), c_e = 1 + (2e+1)/128 and w = 2^-j make a product that float32
+    holds exactly but 16 bits do not, ties included; torch's CPU conversion
+    of that exact product is the expected value."""
+    T, E, Kt, H, N = 89, 7, 3, 64, 96
+    ids, A, _, _ = _rand_case(B + 5, T, E, Kt, H, N)
+    Ab = synth.f32_to_bf16_bits(A * 3.0)
+    Bb = _selector(E, N, H, lambda e: 1.0 + (2 * e + 1) / 128.0)
+    P = ids.size
+    wts = np.ldexp(1.0, -(np.arange(P) % 4)).astype(np.float32)
+    sb, eb, tot, s, e, total = _meta(moe, ids, E, B, dev)
+    C = torch.full((P, N), float("nan"), dtype=c_dtype, device=dev)
+    moe.moe_grouped_gemm(bf16_dev(Ab, dev), _weights(moe, Bb, dev, layout, "none"), sb, eb, tot, B,
+                         P, a_rows="pair", a_row_div=Kt, topk_weights=torch.from_numpy(wts).to(dev),
+                         C=C, c_rows="pair")
+    torch.cuda.synchronize()
+    A64, B64 = oracle.bf16_bits_to_f64(Ab), oracle.bf16_bits_to_f64(Bb)
+    exact = np.einsum("pk,pnk->pn", A64[np.arange(P) // Kt], B64[ids.reshape(-1)]) * wts[:, None]
+    assert (exact.astype(np.float32).astype(np.float64) == exact).all()   # float32 holds it
+    ref = torch.from_numpy(exact.astype(np.float32)).to(c_dtype)
+    got = C.cpu()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # the case does exercise rounding: many products are not 16-bit values
+    assert (ref.double().numpy() != exact).mean() > 0.5
+
+
+@pytest.mark.parametrize("B", [b for b in BLOCKS if b != 256])
+def test_gemm_f32_input_rounding_exact(moe, dev, B):
+    """float32 tokens are rounded to bf16 on load, to nearest even: with a
+    selector weight of 1 the float32 output is exactly torch's bf16 rounding
+    of the token value."""
+    T, E, Kt, H, N = 61, 5, 2, 64, 48
+    ids, A, _, _ = _rand_case(B + 11, T, E, Kt, H, N)
+    A = A * np.float32(1.0 + 2.0 ** -9)         # values off the bf16 grid
+    Bb = _selector(E, N, H, lambda e: 1.0)
+    sb, eb, tot, s, e, total = _meta(moe, ids, E, B, dev)
+    P = ids.size
+    C = torch.full((P, N), float("nan"), dtype=torch.float32, device=dev)
+    moe.moe_grouped_gemm(torch.from_numpy(A).to(dev), bf16_dev(Bb, dev), sb, eb, tot, B, P,
+                         a_rows="pair", a_row_div=Kt, C=C, c_rows="pair")
+    torch.cuda.synchronize()
+    Ar = torch.from_numpy(A).to(torch.bfloat16).float().numpy()
+    ex = ids.reshape(-1)
+    cols = (3 * np.arange(N)[None, :] + ex[:, None]) % H
+    ref = Ar[(np.arange(P) // Kt)[:, None], cols]
+    assert np.array_equal(C.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("B", [b for b in BLOCKS if b != 256])
 def test_gemm_sorted_rows_and_f32_input(moe, dev, B):
     """A rows by sorted position (how the layer feeds its second GEMM), C rows

@@ -185,7 +185,7 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     }
     br = {}
     for name, fn in parts.items():
-        for _ in range(3):
+        for _ in range(warmup):
             fn()
         mean, med = timer.run(fn, reps)
         br[name] = dict(mean_ms=mean, median_ms=med)
@@ -375,8 +375,10 @@ def cpu_baseline(torch, prefill_inputs, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # enough warm-up for the GPU clock to settle after the host-side set-up
+    # of each measurement (about 50 ms of kernels); the timed steps are short
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="prefill headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true",

@@ -15,6 +15,9 @@ and times the oracle on a bounded sample of the prefill workload on the
 host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+       python bench.py --component decode16|decode64|int8gmm|routing|tiny
+The second form runs one of the secondary measurements alone and prints its
+result as one JSON object (for profiling a single workload).
 """
 
 import argparse
@@ -372,6 +375,17 @@ def cpu_baseline(torch, prefill_inputs, target_s=12.0):
                        "expert-loop layer, float64 NumPy; weights pre-decoded)" % (reps, S, cfg.T))
 
 
+def copy_calibration(torch, dev):
+    """Three 1 GiB device-to-device copies: known HBM bytes for scaling the
+    byte counters of a profiled run."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +394,8 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="prefill headline only")
+    ap.add_argument("--component", choices=["decode16", "decode64", "int8gmm", "routing", "tiny"],
+                    help="run this secondary measurement alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true",
                     help="skip the plain-layout comparison runs (profiling the measured path only)")
@@ -397,6 +413,22 @@ def main():
     dev = torch.device("cuda:0")
     timer = Timer(torch)
 
+    if args.component:
+        log(args.component)
+        fn = {"decode16": lambda: bench_decode(torch, moe, dev, "decode16", args.steps, args.warmup,
+                                               timer),
+              "decode64": lambda: bench_decode(torch, moe, dev, "decode64", args.steps, args.warmup,
+                                               timer),
+              "int8gmm": lambda: bench_int8(torch, moe, dev, args.steps, args.warmup, timer),
+              "routing": lambda: bench_routing(torch, moe, dev, args.steps, args.warmup, timer),
+              "tiny": lambda: bench_tiny(torch, moe, dev, args.steps, args.warmup, timer)}
+        res = fn[args.component]()
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps({"component": args.component, "steps": args.steps,
+                          "warmup": args.warmup, "result": res}), flush=True)
+        return
+
     log("prefill layer")
     pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
     ffn = pre["breakdown"]["ffn_gate_up_and_down"]
@@ -413,12 +445,7 @@ def main():
     components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        copy_calibration(torch, dev)
     if not args.quick:
         for name in ("decode16", "decode64"):
             log(name)

@@ -460,13 +460,28 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
     }
   }
 
-  // placeholders and expert ids of the segments, experts split over chunks
-  for (int e = c; e < E; e += nchunk) {
-    const int s0 = seg[e], s1 = seg[e + 1];
-    for (int s = s0 + tot[e] + tid; s < s1; s += kPlaceThreads) sorted_ids[s] = P;
-    for (int b = s0 / B + tid; b < s1 / B; b += kPlaceThreads) expert_ids[b] = e;
+  // Placeholders: the padding slots (fewer than B) of the experts
+  // e = c, c + nchunk, ..., flattened over (expert, slot) so that no thread
+  // walks the experts one after another.
+  const int nloc = c < E ? (E - c + nchunk - 1) / nchunk : 0;
+  for (int i = tid; i < nloc * B; i += kPlaceThreads) {
+    const int e = c + (i / B) * nchunk, s = i % B;
+    const int p = seg[e] + tot[e] + s;
+    if (p < seg[e + 1]) sorted_ids[p] = P;
   }
+  // Expert of each used block, blocks split over the chunks: the last
+  // expert whose segment starts at or before the block (that segment is not
+  // empty and holds the block).
   const int stride = nchunk * kPlaceThreads, first = c * kPlaceThreads + tid;
+  for (int b = first; b < total / B; b += stride) {
+    const int pos = b * B;
+    int lo = 0, hi = E;   // seg[lo] <= pos < seg[hi] (seg[E] = total)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg[mid] <= pos) lo = mid; else hi = mid;
+    }
+    expert_ids[b] = lo;
+  }
   for (int s = total + first; s < max_padded; s += stride) sorted_ids[s] = P;
   for (int b = total / B + first; b < max_padded / B; b += stride) expert_ids[b] = -1;
   if (c == 0 && tid == 0) *total_out = total;

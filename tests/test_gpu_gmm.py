@@ -62,6 +62,19 @@ def test_int8_edge_groups(moe, dev, sizes, layout):
 
 
 @pytest.mark.parametrize("layout", ["plain", "packed"])
+def test_int8_more_tiles_than_one_round(moe, dev, layout):
+    """About 600 tiles of 256 x 128: the first round of resident workgroups
+    and the second launch for the remaining tiles together write every
+    output once."""
+    rng = np.random.default_rng(77)
+    sizes = rng.integers(0, 500, size=40)
+    sizes[[3, 17]] = 0
+    sizes[5] = 1
+    M = int(sizes.sum())
+    _run_and_check(moe, dev, M, 64, 2048, 40, sizes, 78, layout=layout)
+
+
+@pytest.mark.parametrize("layout", ["plain", "packed"])
 def test_int8_small_dims(moe, dev, layout):
     _run_and_check(moe, dev, 40, 16, 16, 3, [10, 20, 10], 61, layout=layout)
     _run_and_check(moe, dev, 70, 144, 48, 2, [33, 37], 62, layout=layout)   # K tail, N < 128

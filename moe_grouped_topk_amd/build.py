@@ -14,6 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "align.hip", "tile_gemm.hip", "stream_gemm.hip", "pack.hip",
+           "small_layer.hip",
            "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

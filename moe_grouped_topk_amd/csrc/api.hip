@@ -99,7 +99,15 @@ struct ForwardLayout {
   size_t w, ids, sorted, eids, total, hist, ctr, bstart, h, y, bytes;
   int64_t max_padded;
   int block_m;
+  bool small;   // the layer after routing runs as one launch (small_layer.hip)
 };
+
+// Small layers with plain weights and the automatic block size skip the
+// alignment and run both GEMMs and the sum in one launch after routing.
+bool use_small_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t block_m,
+                     int32_t w_layout) {
+  return block_m == 0 && w_layout == MOE_WEIGHTS_PLAIN && moe::small_layer_fits(T, H, I, E, topk);
+}
 
 ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                              int32_t block_m, int32_t x_dtype, int32_t w_layout) {
@@ -119,6 +127,7 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.bstart = take(sizeof(int32_t) * ((size_t)E + 1));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
+  L.small = use_small_layer(T, H, I, E, topk, block_m, w_layout);
   L.bytes = off;
   return L;
 }
@@ -388,14 +397,20 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   void* y = base + L.y;   // per-pair down-projection rows, in x's dtype
   hipStream_t s = as_stream(stream);
   const int64_t P = T * topk;
+  int32_t* ctr = reinterpret_cast<int32_t*>(base + L.ctr);
 
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
+  if (L.small) {
+    moe::SmallLayerArgs a{};
+    a.x = x; a.x_dtype = x_dtype == MOE_DTYPE_F32 ? 0 : 1; a.ids = ids; a.w = w;
+    a.w1 = w1; a.w2 = w2; a.out = out; a.T = T; a.H = H; a.I = I; a.topk = topk;
+    return hip_status(moe::launch_small_layer(a, s));
+  }
   // the tile path runs both GEMMs in one persistent launch, whose counters
   // the alignment zeroes
   const bool fused = L.block_m >= 64 && x_dtype == MOE_DTYPE_BF16;
-  int32_t* ctr = reinterpret_cast<int32_t*>(base + L.ctr);
   const int64_t nblk_max = L.max_padded / L.block_m;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
                              reinterpret_cast<int32_t*>(base + L.hist), s, fused ? ctr : nullptr,

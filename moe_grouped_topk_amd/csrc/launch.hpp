@@ -98,6 +98,22 @@ hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream);
 hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int block_m, int E,
                            int64_t nblk_max, int32_t* blk_start, int32_t* ctr, hipStream_t stream);
 
+// The layer after routing in one launch, for small problems
+// (small_layer.hip): one workgroup per token.  H and I multiples of 8.
+struct SmallLayerArgs {
+  const void* x;
+  int x_dtype;            // 0 f32, 1 bf16; out in the same dtype
+  const int32_t* ids;     // [T * topk] routed experts, pair order
+  const float* w;         // [T * topk] routing weights
+  const void* w1;         // [E, 2I, H] bf16
+  const void* w2;         // [E, H, I] bf16
+  void* out;              // [T, H]
+  int64_t T;
+  int H, I, topk;
+};
+bool small_layer_fits(int64_t T, int H, int I, int E, int topk);
+hipError_t launch_small_layer(const SmallLayerArgs& a, hipStream_t stream);
+
 struct GmmI8Args {
   const int8_t* X;
   const int8_t* W;        // [E, N, K] int8, or packed (w_packed)

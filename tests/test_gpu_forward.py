@@ -171,3 +171,73 @@ def test_layer_reuses_workspace(moe, dev, block_m):
             err = max_abs_rel(_out_host(out), ref)
             print("reuse T=%d %s block_m %d err=%.3e" % (c.T, layout, block_m, err))
             assert err <= BAR_BF16
+
+
+# ---- small layers: routing, then one launch for the GEMMs and the sum ----
+
+def _small_case(cfg, dev, x_dtype=None, bias_expert=None):
+    d = layer_inputs(cfg, dev, x_dtype=x_dtype)
+    if bias_expert is not None:   # every token's best expert is the same one
+        g = d["gating_host"].astype(np.float32)
+        g[:, bias_expert] += np.float32(8.0)
+        d["gating_host"] = g.astype(np.float64)
+        d["gating"] = torch.from_numpy(g).to(dev)
+    return d
+
+
+def _check_small(moe, cfg, d, dev):
+    out, w, ids = _run(moe, cfg, d, 0, dev)
+    check_routing(w, ids, d["gating_host"], cfg.topk, cfg.renormalize, cfg.groups,
+                  cfg.topk_group, "softmax", cfg.scale)
+    ref = _oracle_rows(cfg, d, np.arange(cfg.T), w, ids)
+    err = max_abs_rel(_out_host(out), ref)
+    print("small layer %s err=%.3e" % (cfg.name, err))
+    assert err <= BAR_BF16
+    return out
+
+
+@pytest.mark.parametrize("case", ["tiny_bf16", "skewed", "dense", "grouped", "max_pairs",
+                                  "past_limit"])
+def test_small_layer_shapes(moe, dev, case):
+    """Automatic block size with plain weights: layers up to 2048 pairs (and
+    6 * pairs * H * I up to 2^28) run as routing plus one launch, one
+    workgroup per token; larger ones take the aligned path.  Covers one
+    expert with all the tokens, empty experts, E = 1 with H / 8 and I / 8 not
+    powers of two, grouped routing with a scale, the pair limit and just
+    past it."""
+    from synth.configs import Config
+    x_dtype = None
+    bias = None
+    if case == "tiny_bf16":
+        cfg, x_dtype = synth.CONFIGS["tiny"], "bf16"
+    elif case == "skewed":
+        cfg, bias = Config(13, "skewed", T=64, H=128, I=256, E=8, topk=2, x_dtype="f32"), 3
+    elif case == "dense":
+        cfg = Config(14, "dense", T=37, H=64, I=96, E=1, topk=1, x_dtype="f32", w_std=0.1)
+    elif case == "grouped":
+        cfg = Config(15, "grouped", T=50, H=64, I=128, E=64, topk=6, groups=8, topk_group=2,
+                     scale=2.5, x_dtype="bf16", w_std=0.05)
+    elif case == "max_pairs":
+        cfg = Config(16, "max pairs", T=256, H=128, I=128, E=32, topk=8, x_dtype="f32")
+    else:
+        cfg = Config(17, "past the pair limit", T=257, H=128, I=128, E=32, topk=8, x_dtype="f32")
+    d = _small_case(cfg, dev, x_dtype, bias)
+    _check_small(moe, cfg, d, dev)
+
+
+def test_small_layer_repeatable_on_garbage_workspace(moe, dev):
+    """A workspace full of garbage works, and repeated calls give identical
+    bits (fixed summation order)."""
+    cfg = synth.CONFIGS["tiny"]
+    d = layer_inputs(cfg, dev)
+    ws = torch.full((moe.moe_forward_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk),),
+                    0x7f, dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(3):
+        outs.append(moe.moe_forward(d["x"], d["gating"], d["w1"], d["w2"], cfg.topk,
+                                    workspace=ws).cpu())
+        torch.cuda.synchronize()
+    ref = oracle.moe_layer_expert_loop(d["x_host"], d["w1_host"], d["w2_host"],
+                                       *oracle.grouped_topk(d["gating_host"], cfg.topk))
+    assert max_abs_rel(outs[0].numpy(), ref) <= BAR_BF16
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])

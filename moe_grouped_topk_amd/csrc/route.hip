@@ -45,8 +45,33 @@ route_kernel(const float* __restrict__ gating, int64_t T, int E, int topk,
 
   // Group stage ([GTK] 3.2-3.4): group score = max logit of the group; keep
   // the topk_group best groups (ties -> lower group), mask the others.
-  if (G > 1) {
-    const int P = E / G;
+  const int P = G > 1 ? E / G : E;
+  const int seg = P / V;   // lanes per group when a group is a whole number of lanes
+  if (G > 1 && G <= kWave && P % V == 0 && (seg & (seg - 1)) == 0) {
+    // Each group is an aligned run of seg lanes: its max by seg-lane xor
+    // steps, all groups at once; then every group's rank among the G group
+    // maxima (ties to the lower group) from the maxima read lane by lane.
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t k = (uint32_t)(cand[j] >> 32);
+      m = k > m ? k : m;
+    }
+    for (int st = 1; st < seg; st <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m, st, kWave);
+      m = o > m ? o : m;
+    }
+    const int my_g = lane / seg;
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+      const uint32_t mg = (uint32_t)__builtin_amdgcn_readlane((int)m, g * seg);
+      rank += (mg > m || (mg == m && g < my_g)) ? 1 : 0;
+    }
+    if (rank >= topk_group) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) cand[j] = 0ull;
+    }
+  } else if (G > 1) {
     uint64_t gcand = 0ull;   // lane g < G holds group g's candidate
     for (int g = 0; g < G; ++g) {
       uint32_t m = 0u;

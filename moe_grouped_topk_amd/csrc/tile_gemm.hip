@@ -34,6 +34,8 @@
 //    contiguous run of tiles, so an expert's weight slab and its gathered
 //    rows are shared in one XCD's L2.
 
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1518,17 +1520,19 @@ hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int 
 
 namespace {
 
+// CUs of the current device, queried once per device (calls from several
+// host threads may race to fill the cache; they store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <int BM, int CDT>

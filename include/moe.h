@@ -334,8 +334,8 @@ MOE_API int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int6
  * their GEMM, [GMM] 4):
  *   xq, sx = moe_quantize_rows(x)
  *   h[pair] = silu(gate) * up, gate/up[n] = sx[t] * w1_scales[e, n] *
- *             sum_k xq[t, k] * w1q[e, n, k]      (float32)
- *   hq, sh = per-row int8 of h (one row per pair)
+ *             sum_k xq[t, k] * w1q[e, n, k]      (float32, stored as bf16)
+ *   hq, sh = per-row int8 of the bf16 h (one row per pair)
  *   out[t] = sum_k w[t,k] * sh[pair] * w2_scales[e, n] * sum_j hq[j] * w2q[e, n, j]
  * Routing, alignment and the final reduce are moe_forward's.
  *   w1q [E, 2I, H] int8 and w1_scales [E, 2I] f32; w2q [E, H, I] int8 and

@@ -155,7 +155,7 @@ W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
   L.hist = take(moe::align_ws_bytes(P, E));
   L.xq = take((size_t)T * (size_t)H);
   L.sx = take(sizeof(float) * (size_t)T);
-  L.h = take(sizeof(float) * (size_t)L.max_padded * (size_t)I);
+  L.h = take(2 * (size_t)L.max_padded * (size_t)I);   // bf16
   L.hq = take((size_t)L.max_padded * (size_t)I);
   L.sh = take(sizeof(float) * (size_t)L.max_padded);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
@@ -504,7 +504,7 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   int32_t* total = reinterpret_cast<int32_t*>(base + L.total);
   int8_t* xq = reinterpret_cast<int8_t*>(base + L.xq);
   float* sx = reinterpret_cast<float*>(base + L.sx);
-  float* h = reinterpret_cast<float*>(base + L.h);
+  void* h = base + L.h;   // gate_up output, bf16, quantised per row below
   int8_t* hq = reinterpret_cast<int8_t*>(base + L.hq);
   float* sh = reinterpret_cast<float*>(base + L.sh);
   void* y = base + L.y;
@@ -518,7 +518,7 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   g1.E = E; g1.N = 2 * (int64_t)I; g1.K = H;
   g1.sorted_ids = sorted; g1.expert_ids = eids; g1.total = total; g1.max_padded = L.max_padded;
   g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
-  g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_F32; g1.ldc = I;
+  g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I;
   g1.c_rows = MOE_ROWS_SORTED;
   st = check_gemm(g1);
   if (st != MOE_OK) return st;
@@ -540,7 +540,7 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   if (err != hipSuccess) return MOE_ERR_HIP;
   st = enqueue_gemm(g1, s);
   if (st != MOE_OK) return st;
-  err = moe::launch_quantize_rows(h, MOE_DTYPE_F32, L.max_padded, I, I, sorted, total, P, hq, sh, s);
+  err = moe::launch_quantize_rows(h, MOE_DTYPE_BF16, L.max_padded, I, I, sorted, total, P, hq, sh, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
   st = enqueue_gemm(g2, s);
   if (st != MOE_OK) return st;

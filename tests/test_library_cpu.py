@@ -308,3 +308,16 @@ def test_forward_block_m_choice(mod):
     assert mod.moe_forward_block_m(4096, 128, 8, weights="packed") == 128
     assert mod.lib.moe_forward_block_m(16, 0, 8, 1, 0) == -1
     assert mod.lib.moe_forward_block_m(16, 256, 8, 1, 5) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message before
+    touching torch or the GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""

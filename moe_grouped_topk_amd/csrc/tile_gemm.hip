@@ -788,59 +788,74 @@ __device__ __forceinline__ void store16_coh(void* dst, const u32x4_t& v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(v) : "memory");
 }
 
-// SiLU epilogue (bf16 tokens and weights, bf16 output) that stages the tile
-// in LDS and writes whole 256-byte row segments with agent-scope stores.
-// Written straight from the MFMA layout, each store instruction would touch
-// 32 rows with 16 bytes each; agent-scope stores go through to memory and
-// would then move partial lines.  Reuses the K ring, which every wave has
-// finished reading at the first barrier.
-template <class C>
+// SiLU epilogue with bf16 output that stages the tile in LDS and writes
+// whole 256-byte row segments (COH: with agent-scope stores, which go
+// through to memory; written straight from the MFMA layout each store
+// instruction would touch 32 rows with 16 bytes each, and agent-scope
+// stores would then move partial lines).  Reuses the K ring, which every
+// wave has finished reading at the first barrier.  wr / ar: this thread's
+// row weight and (int8) row scale (threads < BM), read before the K loop.
+template <class C, bool COH, int KIND>
 __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const MoeTile& t,
                                                      const int* rowinfo,
                                                      const int (&wrow)[C::RB], int tcol0,
-                                                     const f32x16_t (&acc)[C::RB][C::CB],
-                                                     uint8_t* smem) {
+                                                     const typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
+                                                     uint8_t* smem, float wr, float ar) {
   constexpr int RB = C::RB, CB = C::CB, BM = C::BM, HC = C::BN / 2;   // BM rows x HC columns
   constexpr int PITCH = HC * 2 + 16;          // LDS bytes per token row
   constexpr int LPR = HC * 2 / 16;            // lanes per row in the store phase
   constexpr int RPP = C::THREADS / LPR;       // rows per store pass
-  static_assert(BM * PITCH <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0,
+  static_assert(BM * PITCH + 2 * BM * 4 <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0 &&
+                    BM <= C::THREADS,
                 "staged epilogue shape");
+  float* s_w = reinterpret_cast<float*>(smem + BM * PITCH);
+  float* s_a = s_w + BM;
   const int tid = tile_tid(), lane = tid & 63;
   const int rsub = 4 * (lane >> 5);
+  const int64_t Nout = a.N / 2;
+  const float* bsc = KIND ? a.b_scales + (int64_t)t.e * a.N : nullptr;
+  const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
+  __syncthreads();                            // every wave has left the K ring
+  if (tid < BM) { s_w[tid] = wr; s_a[tid] = ar; }
   __syncthreads();
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int trow = tcol0 + cb * 32 + (lane & 31);
+    const float w = s_w[trow], as = s_a[trow];
     uint8_t* dst = smem + trow * PITCH;
 #pragma unroll
     for (int j = 0; j < RB / 2; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = wrow[j] + 8 * g + rsub;
-        const f32x16_t& gt = acc[j][cb];
-        const f32x16_t& up = acc[j + RB / 2][cb];
+        f32x4_t sg = one4, su = one4;
+        if constexpr (KIND != 0) {
+          const int64_t gc = t.c0 + col < Nout ? t.c0 + col : 0;   // past N: never stored
+          sg = *reinterpret_cast<const f32x4_t*>(bsc + gc);
+          su = *reinterpret_cast<const f32x4_t*>(bsc + Nout + gc);
+        }
+        const f32x4_t gt = acc4(acc[j][cb], g, as, sg);
+        const f32x4_t up = acc4(acc[j + RB / 2][cb], g, as, su);
         const uint2 v = make_uint2(
-            pack_bf16x2(silu_f32(gt[4 * g]) * up[4 * g], silu_f32(gt[4 * g + 1]) * up[4 * g + 1]),
-            pack_bf16x2(silu_f32(gt[4 * g + 2]) * up[4 * g + 2],
-                        silu_f32(gt[4 * g + 3]) * up[4 * g + 3]));
+            pack_bf16x2(silu_f32(gt[0]) * up[0] * w, silu_f32(gt[1]) * up[1] * w),
+            pack_bf16x2(silu_f32(gt[2]) * up[2] * w, silu_f32(gt[3]) * up[3] * w));
         *reinterpret_cast<uint2*>(dst + col * 2) = v;
       }
     }
   }
   __syncthreads();
-  const int64_t Nout = a.N / 2;
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
   const int ch = tid % LPR;
-  const int64_t col = t.c0 + ch * 8;          // 8 columns; Nout is a multiple of 16
+  const int64_t col = t.c0 + ch * 8;          // 8 columns; Nout is a multiple of 8
 #pragma unroll
   for (int r0 = 0; r0 < BM; r0 += RPP) {
     const int r = r0 + tid / LPR;
     const int p = rowinfo[r];
     if (p < 0 || p >= a.num_valid || col >= Nout) continue;
     const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + r;
-    store16_coh(Cb + (crow * a.ldc + col) * 2,
-                *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16));
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+    if constexpr (COH) store16_coh(Cb + (crow * a.ldc + col) * 2, v);
+    else *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) = v;
   }
 }
 
@@ -850,37 +865,44 @@ __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const
 // Straight from the MFMA layout each store instruction would cover 32 rows
 // with 16 bytes each.  wr: this thread's row weight (threads < BM), read
 // before the K loop.
-template <class C, int CDT>
+template <class C, int CDT, int KIND>
 __device__ __forceinline__ void plain_epilogue_staged(const MoeGemmArgs& a, const MoeTile& t,
                                                       const int* rowinfo,
                                                       const int (&wrow)[C::RB], int tcol0,
-                                                      const f32x16_t (&acc)[C::RB][C::CB],
-                                                      uint8_t* smem, float wr) {
+                                                      const typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
+                                                      uint8_t* smem, float wr, float ar) {
   constexpr int RB = C::RB, CB = C::CB, BM = C::BM, BN = C::BN;
   constexpr int PITCH = BN * 2 + 16;          // LDS bytes per token row
   constexpr int LPR = BN * 2 / 16;            // lanes per row in the store phase
   constexpr int RPP = C::THREADS / LPR;       // rows per store pass
-  static_assert(BM * PITCH + BM * 4 <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0 &&
+  static_assert(BM * PITCH + 2 * BM * 4 <= C::kBytes && C::THREADS % LPR == 0 && BM % RPP == 0 &&
                     BM <= C::THREADS && (CDT == 1 || CDT == 2),
                 "staged epilogue shape");
   float* s_w = reinterpret_cast<float*>(smem + BM * PITCH);
+  float* s_a = s_w + BM;
   const int tid = tile_tid(), lane = tid & 63;
   const int rsub = 4 * (lane >> 5);
+  const float* bsc = KIND ? a.b_scales + (int64_t)t.e * a.N : nullptr;
+  const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
   __syncthreads();                            // every wave has left the K ring
-  if (tid < BM) s_w[tid] = wr;
+  if (tid < BM) { s_w[tid] = wr; s_a[tid] = ar; }
   __syncthreads();
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int trow = tcol0 + cb * 32 + (lane & 31);
-    const float w = s_w[trow];
+    const float w = s_w[trow], as = s_a[trow];
     uint8_t* dst = smem + trow * PITCH;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x16_t& v = acc[rb][cb];
-        const float a0 = v[4 * g] * w, a1 = v[4 * g + 1] * w, a2 = v[4 * g + 2] * w,
-                    a3 = v[4 * g + 3] * w;
+        f32x4_t sc = one4;
+        if constexpr (KIND != 0) {
+          const int64_t gc = t.c0 + wrow[rb] + 8 * g + rsub;
+          sc = *reinterpret_cast<const f32x4_t*>(bsc + (gc < a.N ? gc : 0));   // past N: never stored
+        }
+        const f32x4_t v = acc4(acc[rb][cb], g, as, sc);
+        const float a0 = v[0] * w, a1 = v[1] * w, a2 = v[2] * w, a3 = v[3] * w;
         const uint2 o = CDT == 1 ? make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3))
                                  : make_uint2(pack_f16x2(a0, a1), pack_f16x2(a2, a3));
         *reinterpret_cast<uint2*>(dst + (wrow[rb] + 8 * g + rsub) * 2) = o;
@@ -954,24 +976,32 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
-  // 16-bit output without SiLU goes out through LDS when the tile fits the ring
-  constexpr bool kStagedPlain = EPI == 0 && KIND == 0 && (CDT == 1 || CDT == 2) &&
-                                BM * (BN * 2 + 16) + BM * 4 <= C::kBytes && BM <= C::THREADS;
-  float wr = 1.0f;   // this thread's row weight, read while the K loop runs
-  if constexpr (kStagedPlain) {
-    if (tid < BM && a.topk_weights) {
+  // 16-bit output goes out through LDS when the tile fits the ring (SiLU:
+  // bf16 output only)
+  constexpr bool kStagedPlain = EPI == 0 && (CDT == 1 || CDT == 2) &&
+                                BM * (BN * 2 + 16) + 2 * BM * 4 <= C::kBytes && BM <= C::THREADS;
+  constexpr bool kStagedSilu = EPI == 1 && CDT == 1 &&
+                               BM * (BN + 16) + 2 * BM * 4 <= C::kBytes && BM <= C::THREADS;
+  static_assert(!COH_C || kStagedSilu, "coherent stores: staged bf16 SiLU output");
+  // this thread's row weight and (int8) row scale, read while the K loop runs
+  float wr = 1.0f, ar = 1.0f;
+  if constexpr (kStagedPlain || kStagedSilu) {
+    if (tid < BM) {
       const int p = rowinfo[tid];
-      if (p >= 0 && p < a.num_valid) wr = a.topk_weights[p];
+      if (p >= 0 && p < a.num_valid) {
+        if (a.topk_weights) wr = a.topk_weights[p];
+        if constexpr (KIND != 0)
+          ar = a.a_scales[a.a_rows == 0 ? (int64_t)(p / a.a_row_div) : t.s0 + tid];
+      }
     }
   }
   mainloop_dma_live<C, KIND, COH_A>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
                                     live_rows<BM>(rowinfo, a.num_valid), acc, issued_all);
   after_loop();
-  if constexpr (COH_C) {
-    static_assert(EPI == 1 && CDT == 1 && KIND == 0, "coherent stores: bf16 SiLU output");
-    silu_epilogue_staged<C>(a, t, rowinfo, wrow, tcol0, acc, smem);
+  if constexpr (kStagedSilu) {
+    silu_epilogue_staged<C, COH_C, KIND>(a, t, rowinfo, wrow, tcol0, acc, smem, wr, ar);
   } else if constexpr (kStagedPlain) {
-    plain_epilogue_staged<C, CDT>(a, t, rowinfo, wrow, tcol0, acc, smem, wr);
+    plain_epilogue_staged<C, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc, smem, wr, ar);
   } else {
     moe_epilogue<C::RB, C::CB, EPI, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc);
   }

@@ -1376,29 +1376,53 @@ gmm_i8_tile_kernel(GmmI8Args a) {
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
 
   const int live_m = row_hi - row0 < BM ? row_hi - row0 : BM;
+  // this thread's row scale (threads < BM), read while the K loop runs
+  float ar = 0.0f;
+  if (tid < BM && rowinfo[tid] >= 0) ar = a.sx[rowinfo[tid]];
   mainloop_dma_live<C, 1>(smem, rowp, pk_mask, a.K, wrow, tcol0, live_m, acc);
 
-  uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
+  // Epilogue through LDS: the fp16 tile in [token row][column] order in the
+  // drained K ring, then each row's BN columns as whole 16-byte pieces
+  // (straight from the MFMA layout each store would cover 32 rows x 8 bytes).
+  constexpr int PITCH = BN * 2 + 16, LPR = BN * 2 / 16, RPP = NT / LPR;
+  static_assert(BM * PITCH + BM * 4 <= C::kBytes && NT % LPR == 0 && BM % RPP == 0 && BM <= NT,
+                "staged GMM epilogue shape");
+  float* s_a = reinterpret_cast<float*>(smem + BM * PITCH);
+  __syncthreads();                            // every wave has left the K ring
+  if (tid < BM) s_a[tid] = ar;
+  __syncthreads();
   const int rsub = 4 * (lane >> 5);
+  const float* swe = a.sw + (int64_t)e * a.N;
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) {
-    const int m = rowinfo[tcol0 + cb * 32 + (lane & 31)];
-    if (m < 0) continue;
-    const float sx = a.sx[m];
+    const int trow = tcol0 + cb * 32 + (lane & 31);
+    const float sx = s_a[trow];
+    uint8_t* dst = smem + trow * PITCH;
 #pragma unroll
     for (int rb = 0; rb < S::RB; ++rb) {
       const i32x16_t v = acc[rb][cb];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wrow[rb] + 8 * g + rsub;
-        if (n < a.N) {
-          const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(a.sw + (int64_t)e * a.N + n);
-          store4<2>(Yb + ((int64_t)m * a.N + n) * 2, (float)v[4 * g] * sx * sw[0],
-                    (float)v[4 * g + 1] * sx * sw[1], (float)v[4 * g + 2] * sx * sw[2],
-                    (float)v[4 * g + 3] * sx * sw[3]);
-        }
+        const int col = wrow[rb] + 8 * g + rsub;
+        const int64_t n = n0 + col;
+        const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(swe + (n < a.N ? n : 0));   // past N: never stored
+        *reinterpret_cast<uint2*>(dst + col * 2) =
+            make_uint2(pack_f16x2((float)v[4 * g] * sx * sw[0], (float)v[4 * g + 1] * sx * sw[1]),
+                       pack_f16x2((float)v[4 * g + 2] * sx * sw[2], (float)v[4 * g + 3] * sx * sw[3]));
       }
     }
+  }
+  __syncthreads();
+  uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
+  const int ch = tid % LPR;
+  const int64_t col = n0 + ch * 8;            // 8 columns; N is a multiple of 16
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += RPP) {
+    const int r = r0 + tid / LPR;
+    const int m = rowinfo[r];
+    if (m < 0 || col >= a.N) continue;
+    *reinterpret_cast<u32x4_t*>(Yb + ((int64_t)m * a.N + col) * 2) =
+        *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
   }
 }
 

@@ -286,9 +286,9 @@ MOE_API int moe_grouped_ffn(const void* x, int64_t T, int32_t H, int32_t topk, c
  *            moe_pack_weights (needs bf16 x; block_m 64, 128 or 256).
  *   topk_weights_out [T, topk] f32, topk_ids_out [T, topk] int32: optional
  *            (NULL = kept in the workspace only).
- *   block_m  0 = chosen from the average pairs per expert (16, 32, 64 or
- *            128; at least 64 with packed weights); otherwise one of the
- *            moe_grouped_gemm block sizes.  With 0, plain weights and a
+ *   block_m  0 = chosen from the average pairs per expert (64 or 128 with
+ *            bf16 x or packed weights; 16, 32, 64 or 128 for f32 x on plain
+ *            weights); otherwise one of the moe_grouped_gemm block sizes.  With 0, plain weights and a
  *            small layer (T * topk <= 2048 and 6 * T * topk * H * I <= 2^28)
  *            the alignment and the tiled GEMMs are skipped: after routing
  *            one launch computes each token's pairs in k order in fp32 (x

@@ -85,11 +85,14 @@ int enqueue_gemm(const moe::MoeGemmArgs& a, hipStream_t s) {
 // per expert those skip the MFMAs of empty token columns and stream weights.
 int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
   const double avg = (double)T * topk / (double)E;   // pairs per expert
-  const bool packed = w_layout == MOE_WEIGHTS_PACKED;
-  if (avg < 8.0 && !packed) return 16;
-  if (avg < 24.0 && !packed) return 32;
+  // bf16 tokens take the direct-to-LDS tile kernels at any size (decode
+  // T = 16 on plain weights: 1.59 ms at block 64 against 2.40 ms with the
+  // weight-streaming kernel at block 16); f32 tokens with plain weights keep
+  // the streaming kernel for few pairs per expert
+  const bool tile = w_layout == MOE_WEIGHTS_PACKED || x_dtype == MOE_DTYPE_BF16;
+  if (avg < 8.0 && !tile) return 16;
+  if (avg < 24.0 && !tile) return 32;
   if (avg < 96.0) return 64;
-  (void)x_dtype;
   return 128;   // 256 x 128 tiles, two workgroups per CU: measured ahead of 256 x 256
 }
 

@@ -302,7 +302,8 @@ def test_gmm_validation(mod):
 def test_forward_block_m_choice(mod):
     assert mod.moe_forward_block_m(4096, 128, 8) == 128          # prefill shape: 256 x 128 tiles
     assert mod.moe_forward_block_m(4096, 128, 8, "f32") == 128
-    assert mod.moe_forward_block_m(16, 256, 8) == 16             # decode shape
+    assert mod.moe_forward_block_m(16, 256, 8) == 64             # decode shape, bf16 x
+    assert mod.moe_forward_block_m(16, 256, 8, "f32") == 16      # f32 x, plain weights
     assert mod.moe_forward_block_m(64, 8, 2, "f32") == 32        # tiny layer
     assert mod.moe_forward_block_m(16, 256, 8, weights="packed") == 64    # tile kernels only
     assert mod.moe_forward_block_m(4096, 128, 8, weights="packed") == 128

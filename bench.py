@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # HBM bytes per launch of the fused gate_up + down kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill layer).  Only
 # valid for that kernel configuration; null for any other block size or once the kernel changes.
-FFN_TRAFFIC = {"block_m": 128, "bytes": 1.942e9 + 0.188e9}
+FFN_TRAFFIC = {"block_m": 128, "bytes": 1.929e9 + 0.188e9}
 
 
 def log(msg):

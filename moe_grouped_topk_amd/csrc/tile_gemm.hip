@@ -9,27 +9,31 @@
 // per-row and per-channel scales, int32 accumulation per section 5.3).
 //
 // gfx950 design (not the pages' Triton tiling):
-//  * 256 threads = 4 wave64s in a 2 (weight rows) x 2 (tokens) grid.  A tile
-//    is BN weight rows x BM tokens (BN 128/256, BM 64/128/256); a wave owns
-//    BN/2 x BM/2 and computes it with v_mfma_f32_32x32x16_bf16 (or
-//    v_mfma_i32_32x32x32_i8) blocks.  At BN = BM = 256 a wave holds a
-//    128 x 128 fp32 accumulator (256 registers, kept in AGPRs), which halves
-//    the LDS operand traffic per FLOP of a 64 x 64 wave tile.
 //  * Operands are swapped relative to the usual C = A.B^T picture: weight
 //    rows sit in the MFMA's row slot and tokens in its column slot, so each
-//    lane ends up with runs of 4 consecutive OUTPUT FEATURES of one token:
-//    packed stores, and gate and up (or a channel scale) in the same lane.
-//  * K advances 128 bytes per stage (64 bf16 or 128 int8 = 4 MFMA k-steps).
-//    Global -> registers -> LDS with two LDS stages and (for BM <= 128) two
-//    register buffers: the loads of stage k+2 are issued before the MFMAs of
-//    stage k, so two stages of loads are in flight while the matrix cores
-//    run (BM = 256 keeps one stage in flight to stay within 512 registers).  LDS
-//    rows are padded to 144 bytes, which makes every group of 8 lanes reading
-//    16 bytes hit 8 distinct bank quads.
+//    lane ends up with runs of 4 consecutive OUTPUT FEATURES of one token
+//    (v_mfma_f32_32x32x16_bf16 / v_mfma_i32_32x32x32_i8 blocks): packed
+//    stores, and gate and up (or a channel scale) in the same lane.
 //  * Token rows are gathered straight from x into LDS by pair index; the
 //    gathered tensor never exists in HBM.  Placeholder rows are masked at
-//    the store; loads and MFMAs are branch-free.
-//  * Tiles are numbered block-major (all n-tiles of a block adjacent, the
+//    the store.
+//  * Main path (bf16 and int8 operands, moe_gemm_dma_kernel,
+//    moe_ffn_fused_kernel, gmm_i8_tile_kernel): BN = 256 weight rows x BM =
+//    64/128/256 tokens per tile, loaded with direct-to-LDS loads
+//    (global_load_lds_dwordx4) into an NSTAGE ring of 64-byte K stages, with
+//    no staging registers.  Weights may come pre-packed (moe_pack_weights) so
+//    each wave's load is one contiguous, pre-swizzled 1 KiB piece.  Two
+//    workgroups per CU at BM 64/128: one workgroup's MFMAs run while the
+//    other waits for its loads.  Epilogues stage 16-bit output through LDS
+//    and store whole 16-byte pieces of each output row.
+//  * moe_ffn_fused_kernel runs gate_up and down of a layer in one persistent
+//    launch fed by per-XCD work queues; h crosses XCDs through agent-scope
+//    stores and loads (described where the kernel is defined).
+//  * float32 tokens (moe_gemm_tile_kernel): 4 waves in a 2 x 2 grid, global
+//    -> registers (rounded to bf16) -> LDS with 128-byte K stages, LDS rows
+//    padded to 144 bytes so every group of 8 lanes reading 16 bytes hits 8
+//    distinct bank quads.
+//  * Tiles are numbered block-major (the n-tiles of a block adjacent, the
 //    blocks of one expert adjacent), and xcd_remap gives each XCD one
 //    contiguous run of tiles, so an expert's weight slab and its gathered
 //    rows are shared in one XCD's L2.

@@ -314,6 +314,39 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
                 float* topk_weights_out, int32_t* topk_ids_out, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* ---- wait diagnostics of the persistent launch ---------------------------
+ * In the persistent gate_up + down launch (moe_grouped_ffn, and moe_forward
+ * with bf16 x and block_m >= 64) a down tile polls a per-block counter until
+ * every gate_up tile of its token block has stored its part of h.  Each poll
+ * loop is bounded: after the spin limit (about a second by default) the tile
+ * stops waiting, sets a flag and reads h as it is, so a broken launch still
+ * ends instead of hanging the GPU; the output of such a launch is wrong.  By
+ * construction every gate_up tile a down tile waits for is already running,
+ * so the limit is a safety net, not part of normal operation.
+ * The flag is one int32 in the caller's workspace, zeroed at the start of
+ * every launch and set to 1 by a wait that hit the limit; it keeps its value
+ * until the next call on that workspace.  Reading it is up to the caller
+ * (after the launch has completed, e.g. a stream sync).
+ *
+ * moe_forward_wait_flag_offset: byte offset of the flag in moe_forward's
+ *   workspace for these arguments (the same ones as moe_forward's; block_m 0
+ *   = the automatic choice).  MOE_ERR_CONFIG if this layer runs no
+ *   persistent launch (f32 x, block_m 16/32, or the one-launch small layer),
+ *   other negative MOE_ERR_* codes for invalid arguments.
+ * moe_grouped_ffn_wait_flag_offset: the same for moe_grouped_ffn's
+ *   workspace (max_padded and block_m as passed to it).
+ * moe_set_wait_spin_limit: polls before a wait gives up, for every later
+ *   launch in this process (0 restores the default).  A hook for tests of
+ *   the failure path: a tiny limit makes waits give up early, so the flag
+ *   is set while every kernel still ends normally.  MOE_ERR_CONFIG if
+ *   spins < 0.  Not synchronised with launches already enqueued.
+ */
+MOE_API int64_t moe_forward_wait_flag_offset(int64_t T, int32_t H, int32_t I, int32_t E,
+                                             int32_t topk, int32_t block_m, int32_t x_dtype,
+                                             int32_t w_layout);
+MOE_API int64_t moe_grouped_ffn_wait_flag_offset(int64_t max_padded, int32_t block_m);
+MOE_API int moe_set_wait_spin_limit(int32_t spins);
+
 /* ---- INT8 activations and the INT8 fused layer ------------------------
  * moe_quantize_rows: symmetric per-row int8 quantisation, [GMM] 3.2 (per
  * token for activations): scale[r] = max|x[r, :]| / 127 (1 for an all-zero

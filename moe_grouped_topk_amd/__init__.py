@@ -19,6 +19,8 @@ __all__ = [
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
     "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
+    "moe_forward_wait_flag_offset", "moe_grouped_ffn_wait_flag_offset", "moe_set_wait_spin_limit",
+    "wait_flag",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -74,6 +76,12 @@ def _load():
     L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
                               i32, f32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_wait_flag_offset.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
+    L.moe_forward_wait_flag_offset.restype = i64
+    L.moe_grouped_ffn_wait_flag_offset.argtypes = [i64, i32]
+    L.moe_grouped_ffn_wait_flag_offset.restype = i64
+    L.moe_set_wait_spin_limit.argtypes = [i32]
+    L.moe_set_wait_spin_limit.restype = ctypes.c_int
     L.gmm_int8.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.moe_quantize_rows.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     L.moe_quantize_rows.restype = ctypes.c_int
@@ -310,6 +318,33 @@ def moe_forward_block_m(T, E, topk, x_dtype="bf16", weights="plain"):
 
 def moe_forward_workspace_size(T, H, I, E, topk, block_m=0):
     return int(lib.moe_forward_workspace_size(T, H, I, E, topk, block_m))
+
+
+def moe_forward_wait_flag_offset(T, H, I, E, topk, block_m=0, x_dtype="bf16", weights="plain"):
+    """Byte offset, in moe_forward's workspace, of the int32 flag that a
+    persistent launch sets when one of its waits hit the spin limit."""
+    off = int(lib.moe_forward_wait_flag_offset(T, H, I, E, topk, block_m, DTYPE[x_dtype],
+                                               WEIGHTS[weights]))
+    _check("moe_forward_wait_flag_offset", off if off < 0 else 0)
+    return off
+
+
+def moe_grouped_ffn_wait_flag_offset(max_padded, block_m):
+    """The same flag's byte offset in moe_grouped_ffn's workspace."""
+    off = int(lib.moe_grouped_ffn_wait_flag_offset(max_padded, block_m))
+    _check("moe_grouped_ffn_wait_flag_offset", off if off < 0 else 0)
+    return off
+
+
+def moe_set_wait_spin_limit(spins):
+    """Polls before a persistent launch's wait gives up (0: the default)."""
+    _check("moe_set_wait_spin_limit", lib.moe_set_wait_spin_limit(spins))
+
+
+def wait_flag(workspace, offset):
+    """The flag at `offset` of a uint8 workspace tensor, read after the
+    stream's work has completed (this synchronises)."""
+    return int(workspace[offset:offset + 4].view(_torch().int32).item())
 
 
 def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe.h"   // include/ is on the include path
 #include "launch.hpp"
 
@@ -17,6 +19,15 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Spin limit of the persistent launch's waits, set by moe_set_wait_spin_limit
+// (0: the default).
+std::atomic<int32_t> g_wait_spin_limit{0};
+
+int wait_spin_limit() {
+  const int32_t v = g_wait_spin_limit.load(std::memory_order_relaxed);
+  return v > 0 ? v : moe::kFusedSpinLimit;
+}
 
 // Shape and option checks of the routing step (pointers are checked by the caller).
 int check_route_shape(int64_t T, int32_t E, int32_t topk, int32_t G, int32_t Kg, int32_t scoring) {
@@ -340,6 +351,7 @@ int moe_grouped_ffn(const void* x, int64_t T, int32_t H, int32_t topk, const voi
       base + round_up(sizeof(int32_t) * (size_t)moe::fused_counters(nblk_max), 256));
   f.blk_start = bs;
   f.nblk_max = (int)nblk_max;
+  f.spin_limit = wait_spin_limit();
   hipStream_t s = as_stream(stream);
   hipError_t err = moe::launch_ffn_prep(expert_ids, num_tokens_post_padded, block_m, E, nblk_max,
                                         bs, f.ctr, s);
@@ -352,6 +364,30 @@ int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype,
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return -1;
   if (!valid_layout(w_layout)) return -1;
   return choose_block_m(T, E, topk, x_dtype, w_layout);
+}
+
+int64_t moe_forward_wait_flag_offset(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                     int32_t block_m, int32_t x_dtype, int32_t w_layout) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
+  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
+  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype, w_layout);
+  if (L.small || L.block_m < 64 || x_dtype != MOE_DTYPE_BF16) return MOE_ERR_CONFIG;
+  return (int64_t)L.ctr +
+         (int64_t)sizeof(int32_t) * moe::fused_wait_flag(L.max_padded / L.block_m);
+}
+
+int64_t moe_grouped_ffn_wait_flag_offset(int64_t max_padded, int32_t block_m) {
+  if (max_padded < 0) return MOE_ERR_SHAPE;
+  if (block_m != 64 && block_m != 128 && block_m != 256) return MOE_ERR_CONFIG;
+  return (int64_t)sizeof(int32_t) * moe::fused_wait_flag(max_padded / block_m);
+}
+
+int moe_set_wait_spin_limit(int32_t spins) {
+  if (spins < 0) return MOE_ERR_CONFIG;
+  g_wait_spin_limit.store(spins, std::memory_order_relaxed);
+  return MOE_OK;
 }
 
 size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
@@ -441,6 +477,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   if (fused) {
     moe::FusedArgs f{};
     f.g1 = g1; f.g2 = g2; f.ctr = ctr; f.nblk_max = (int)nblk_max;
+    f.spin_limit = wait_spin_limit();
     f.blk_start = reinterpret_cast<const int32_t*>(base + L.bstart);
     st = hip_status(moe::launch_moe_ffn_fused(f, s));
   } else {

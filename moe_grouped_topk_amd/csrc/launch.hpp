@@ -90,8 +90,13 @@ struct FusedArgs {
   int32_t* ctr;
   const int32_t* blk_start;
   int nblk_max;
+  int spin_limit;   // polls of a down tile's wait before it gives up and sets the flag
 };
+// Default spin limit of the fused launch's waits: about a second of polling.
+constexpr int kFusedSpinLimit = 1 << 20;
 int fused_counters(int64_t nblk_max);
+// Index of the fused launch's wait-failure flag among its counters.
+int64_t fused_wait_flag(int64_t nblk_max);
 hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream);
 // Counters and blk_start of a fused launch from expert_ids and the total
 // alone (one small kernel): ctr gets fused_counters(nblk_max) zeros.

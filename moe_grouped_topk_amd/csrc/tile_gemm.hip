@@ -1050,9 +1050,9 @@ moe_gemm_dma_kernel(MoeGemmArgs a) {
 // Counters, zeroed before the launch (fused_counters(nblk_max) ints):
 //   [0, 8) gate_up queue heads, [8, 16) down queue heads,
 //   [16, 16 + nblk_max) gate_up tiles finished per token block,
-//   [16 + nblk_max] set to 1 if a wait ran into its spin limit (a fault of
-//   the launch: down tiles then read h early).
-constexpr int kFusedSpinLimit = 1 << 20;   // about a second of polling
+//   [16 + nblk_max] (fused_wait_flag) set to 1 if a wait ran into its spin
+//   limit (f.spin_limit polls): the down tile then reads h early and the
+//   launch's output is wrong, but every workgroup still ends.
 constexpr int kFusedMaxExperts = 1024;
 
 // Token-block ranges of the queues: qb[q] .. qb[q + 1] for q < kNumXcd.  The
@@ -1237,7 +1237,7 @@ moe_ffn_fused_kernel(FusedArgs f) {
         int spins = 0;
         while (__hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt1) {
           __builtin_amdgcn_s_sleep(8);
-          if (++spins == kFusedSpinLimit) {
+          if (++spins >= f.spin_limit) {
             __hip_atomic_store(done + f.nblk_max, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
@@ -1533,6 +1533,7 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
 }
 
 int fused_counters(int64_t nblk_max) { return (int)(2 * kNumXcd + nblk_max + 1); }
+int64_t fused_wait_flag(int64_t nblk_max) { return 2 * kNumXcd + nblk_max; }
 
 // Set-up of a fused launch from the alignment outputs alone: zero the
 // counters and find each expert's first block.  Blocks are in ascending

@@ -51,12 +51,17 @@ def _compare(moe, d, cfg, bm, layout, ws=None):
     if layout == "packed":
         w1, w2 = moe.moe_pack_weights(w1, "silu_mul"), moe.moe_pack_weights(w2, "none")
     h_ref, y_ref = _two_launches(moe, x, w1, w2, K, s, e, tot, bm, w, P)
+    if ws is None:
+        ws = torch.empty(moe.moe_grouped_ffn_workspace_size(s.numel(), E, bm), dtype=torch.uint8,
+                         device=x.device)
     h = torch.zeros_like(h_ref)
     h, y = moe.moe_grouped_ffn(x, w1, w2, K, s, e, tot, bm, w, h=h, workspace=ws)
     torch.cuda.synchronize()
     rows = torch.from_numpy(_valid_rows(s, tot, P)).to(x.device)
     assert torch.equal(h[rows], h_ref[rows])
     assert torch.equal(y, y_ref)
+    # no wait of the launch ran into its spin limit
+    assert moe.wait_flag(ws, moe.moe_grouped_ffn_wait_flag_offset(s.numel(), bm)) == 0
     return w, ids, y
 
 
@@ -111,3 +116,30 @@ def test_ffn_prefill_matches_oracle(moe, dev):
     err = max_abs_rel(out.cpu().numpy()[rows].astype(np.float64), ref)
     print("ffn prefill sampled err=%.3e" % err)
     assert err <= BAR_BF16
+
+
+def test_ffn_wait_gives_up_at_spin_limit(moe, dev):
+    """Failure handling, forced from the host: with a spin limit of one poll,
+    down tiles that find their token block's gate_up tiles unfinished stop
+    waiting and set the workspace flag, and every kernel still ends (h is
+    then read early; the output is not checked).  With the default limit
+    restored the same call on the same workspace is exact again and the flag
+    reads 0.  Shape: few token blocks with 16 gate_up tiles each (K = 2048
+    per tile), so all tiles are in flight at once and down tiles must wait."""
+    cfg = _cfg(512, 2048, 2048, 8, 1, sub=6)
+    d = layer_inputs(cfg, dev)
+    bm = 64
+    w, ids = moe.moe_route(d["gating"], 1)
+    s, e, tot = moe.moe_align_block_size(ids, cfg.E, bm)
+    ws = torch.empty(moe.moe_grouped_ffn_workspace_size(s.numel(), cfg.E, bm),
+                     dtype=torch.uint8, device=dev)
+    off = moe.moe_grouped_ffn_wait_flag_offset(s.numel(), bm)
+    moe.moe_set_wait_spin_limit(1)
+    try:
+        moe.moe_grouped_ffn(d["x"], d["w1"], d["w2"], 1, s, e, tot, bm, w, workspace=ws)
+        torch.cuda.synchronize()
+        flagged = moe.wait_flag(ws, off)
+    finally:
+        moe.moe_set_wait_spin_limit(0)
+    assert flagged == 1
+    _compare(moe, d, cfg, bm, "plain", ws=ws)

@@ -140,9 +140,11 @@ def test_decode_layer_sampled(moe, dev, name):
     err = max_abs_rel(o[rows], ref)
     print("%s sampled err=%.3e" % (name, err))
     assert err <= BAR_BF16
-    # both weight-streaming and tile kernels, plain and packed weights, agree
-    out_t, _, _ = _run(moe, cfg, d, 64, dev)
-    assert max_abs_rel(_out_host(out_t)[rows], ref) <= BAR_BF16
+    assert moe.moe_forward_block_m(cfg.T, cfg.E, cfg.topk) == 64   # the tile kernels
+    # the weight-streaming kernel (block_m 16, plain weights) and the tile
+    # kernels on packed weights agree with the oracle too
+    out_s, _, _ = _run(moe, cfg, d, 16, dev)
+    assert max_abs_rel(_out_host(out_s)[rows], ref) <= BAR_BF16
     out_p, _, ids_p = _run(moe, cfg, d, 0, dev, "packed")
     assert (ids_p == ids).all()
     assert max_abs_rel(_out_host(out_p)[rows], ref) <= BAR_BF16
@@ -171,6 +173,9 @@ def test_layer_reuses_workspace(moe, dev, block_m):
             err = max_abs_rel(_out_host(out), ref)
             print("reuse T=%d %s block_m %d err=%.3e" % (c.T, layout, block_m, err))
             assert err <= BAR_BF16
+            off = moe.moe_forward_wait_flag_offset(c.T, c.H, c.I, c.E, c.topk, block_m, "bf16",
+                                                   layout)
+            assert moe.wait_flag(ws, off) == 0
 
 
 # ---- small layers: routing, then one launch for the GEMMs and the sum ----

@@ -322,3 +322,39 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_wait_flag_offsets(mod):
+    """The persistent launch's wait flag lies inside the caller's workspace,
+    4-byte aligned, past the launch's queue heads and per-block counters; the
+    calls reject layers that run no persistent launch."""
+    d = _defines()
+    # moe_grouped_ffn: counters first (16 queue heads, one count per block), then the flag
+    assert mod.moe_grouped_ffn_wait_flag_offset(1024, 128) == 4 * (16 + 8)
+    assert mod.moe_grouped_ffn_wait_flag_offset(0, 64) == 4 * 16
+    for bm in (64, 128, 256):
+        mp = mod.moe_align_max_padded(32768, 128, bm)
+        off = mod.moe_grouped_ffn_wait_flag_offset(mp, bm)
+        assert off % 4 == 0 and off + 4 <= mod.moe_grouped_ffn_workspace_size(mp, 128, bm)
+    assert mod.lib.moe_grouped_ffn_wait_flag_offset(1024, 32) == d["MOE_ERR_CONFIG"]
+    assert mod.lib.moe_grouped_ffn_wait_flag_offset(-1, 64) == d["MOE_ERR_SHAPE"]
+    # moe_forward: the prefill and decode shapes with bf16 x, both layouts
+    for (T, H, I, E, K) in [(4096, 2048, 768, 128, 8), (16, 7168, 2048, 256, 8)]:
+        for bm in (0, 64, 128, 256):
+            for weights in ("plain", "packed"):
+                off = mod.moe_forward_wait_flag_offset(T, H, I, E, K, bm, "bf16", weights)
+                assert off % 4 == 0 and 0 < off
+                assert off + 4 <= mod.moe_forward_workspace_size(T, H, I, E, K, bm)
+    with pytest.raises(mod.MoeError):      # f32 x: two separate GEMM launches
+        mod.moe_forward_wait_flag_offset(4096, 2048, 768, 128, 8, 0, "f32")
+    with pytest.raises(mod.MoeError):      # weight-streaming block sizes
+        mod.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 16)
+    with pytest.raises(mod.MoeError):      # the tiny layer runs as one small launch
+        mod.moe_forward_wait_flag_offset(64, 128, 256, 8, 2, 0, "bf16", "plain")
+    assert mod.moe_forward_wait_flag_offset(64, 128, 256, 8, 2, 64, "bf16", "plain") > 0
+    assert mod.lib.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 48, 1, 0) == \
+        d["MOE_ERR_CONFIG"]
+    assert mod.lib.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 0, 7, 0) == \
+        d["MOE_ERR_DTYPE"]
+    assert mod.lib.moe_set_wait_spin_limit(-1) == d["MOE_ERR_CONFIG"]
+    assert mod.lib.moe_set_wait_spin_limit(0) == 0

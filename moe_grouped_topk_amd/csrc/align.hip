@@ -307,8 +307,10 @@ __global__ void __launch_bounds__(kCountThreads)
 align_count_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int chunk,
                    int32_t* __restrict__ hist, int32_t* __restrict__ zero, int nzero) {
   extern __shared__ int cnt[];
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nzero; i += kCountThreads) zero[i] = 0;
+  // nzero is a multiple of 4 and zero 16-byte aligned: all workgroups clear it
+  for (int i = blockIdx.x * kCountThreads + threadIdx.x; i < nzero / 4;
+       i += gridDim.x * kCountThreads)
+    reinterpret_cast<int4*>(zero)[i] = make_int4(0, 0, 0, 0);
   for (int e = threadIdx.x; e < E; e += kCountThreads) cnt[e] = 0;
   __syncthreads();
   const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
@@ -503,6 +505,8 @@ size_t align_ws_bytes(int64_t P, int E) {
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
                            hipStream_t stream, int32_t* zero, int nzero, int32_t* blk_start) {
+  if (zero && ((nzero & 3) != 0 || (reinterpret_cast<uintptr_t>(zero) & 15) != 0))
+    return hipErrorInvalidValue;
   const int64_t chunk = align_ws_chunk(P);
   const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
   hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,

@@ -137,7 +137,9 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
   L.hist = take(moe::align_ws_bytes(P, E));
-  L.ctr = take(sizeof(int32_t) * (size_t)moe::fused_counters(L.max_padded / L.block_m));
+  // the persistent launch's counters, rounded up to whole 16-byte pieces (the
+  // alignment zeroes them with 16-byte stores)
+  L.ctr = take(sizeof(int32_t) * round_up((size_t)moe::fused_counters(L.max_padded / L.block_m), 4));
   L.bstart = take(sizeof(int32_t) * ((size_t)E + 1));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
@@ -453,7 +455,7 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   const int64_t nblk_max = L.max_padded / L.block_m;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
                              reinterpret_cast<int32_t*>(base + L.hist), s, fused ? ctr : nullptr,
-                             moe::fused_counters(nblk_max),
+                             (int)round_up((size_t)moe::fused_counters(nblk_max), 4),
                              fused ? reinterpret_cast<int32_t*>(base + L.bstart) : nullptr);
   if (err != hipSuccess) return MOE_ERR_HIP;
 

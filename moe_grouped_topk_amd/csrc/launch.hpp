@@ -19,8 +19,9 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
 // with a workspace of align_ws_bytes(P, E) bytes for the counts.
 size_t align_ws_bytes(int64_t P, int E);
 // Optional: zero / nzero ints set to 0 on the way (counters of a later
-// launch); blk_start [E + 1] receives each expert's first block (its padded
-// segment start / B) and, last, the total number of blocks.
+// launch; zero 16-byte aligned, nzero a multiple of 4); blk_start [E + 1]
+// receives each expert's first block (its padded segment start / B) and,
+// last, the total number of blocks.
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
                            hipStream_t stream, int32_t* zero = nullptr, int nzero = 0,

@@ -143,3 +143,58 @@ def test_ffn_wait_gives_up_at_spin_limit(moe, dev):
         moe.moe_set_wait_spin_limit(0)
     assert flagged == 1
     _compare(moe, d, cfg, bm, "plain", ws=ws)
+
+
+def _sum_k_bf16(y, T, K):
+    """Host sum of each token's K pair rows in k order, float32 from 0, then
+    round to bf16 (the top-k reduce's arithmetic, written out)."""
+    yf = y.float().cpu().view(T, K, -1)
+    acc = torch.zeros_like(yf[:, 0])
+    for k in range(K):
+        acc += yf[:, k]
+    return acc.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["prefill", "decode16", "ragged64", "ragged128", "one_token"])
+def test_forward_is_k_order_sum_of_ffn_rows(moe, dev, case):
+    """moe_forward with bf16 x and block_m 64 / 128 (persistent launch, then the
+    top-k reduce) is bit-identical to the pair rows of moe_grouped_ffn on the
+    same routing and alignment, summed per token in k order in float32 and
+    rounded to bf16 on the host: for both weight layouts, at the prefill and
+    decode sizes, with H not a multiple of the 256-column tile, and with most
+    experts empty (one token)."""
+    if case in ("prefill", "decode16"):
+        cfg = synth.CONFIGS[case]
+    elif case == "one_token":
+        cfg = _cfg(1, 4096, 512, 32, 8, sub=7)
+    else:
+        cfg = _cfg(333, 272, 160, 40, 6, sub=8 if case == "ragged64" else 9, groups=8,
+                   topk_group=3)
+    bm = 128 if case in ("prefill", "ragged128") else 64
+    d = layer_inputs(cfg, dev)
+    T, K, E = cfg.T, cfg.topk, cfg.E
+    layouts = ["packed"] if case == "decode16" else ["plain", "packed"]
+    for layout in layouts:
+        w1, w2 = d["w1"], d["w2"]
+        if layout == "packed":
+            w1, w2 = moe.moe_pack_weights(w1, "silu_mul"), moe.moe_pack_weights(w2, "none")
+        w, ids = moe.moe_route(d["gating"], K, cfg.groups, cfg.topk_group, "softmax",
+                               cfg.renormalize, cfg.scale)
+        s, e, tot = moe.moe_align_block_size(ids, E, bm)
+        _, y = moe.moe_grouped_ffn(d["x"], w1, w2, K, s, e, tot, bm, w)
+        ref = _sum_k_bf16(y, T, K)
+        del y
+        ws = torch.full((moe.moe_forward_workspace_size(T, cfg.H, cfg.I, E, K, bm),), 0x33,
+                        dtype=torch.uint8, device=dev)
+        ids2 = torch.empty_like(ids)
+        out = moe.moe_forward(d["x"], d["gating"], w1, w2, K, cfg.groups, cfg.topk_group,
+                              "softmax", cfg.renormalize, cfg.scale, block_m=bm,
+                              topk_ids_out=ids2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids2, ids)
+        o = out.cpu()
+        ndiff = int((o.view(torch.int16) != ref.view(torch.int16)).sum())
+        print("%s %s block_m %d: %d of %d outputs differ" % (case, layout, bm, ndiff, o.numel()))
+        assert ndiff == 0
+        off = moe.moe_forward_wait_flag_offset(T, cfg.H, cfg.I, E, K, bm, "bf16", layout)
+        assert moe.wait_flag(ws, off) == 0

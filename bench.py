@@ -403,7 +403,7 @@ def main():
                     help="also copy 1 GiB device-to-device 3 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(collectives are out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -246,3 +246,35 @@ def test_small_layer_repeatable_on_garbage_workspace(moe, dev):
                                        *oracle.grouped_topk(d["gating_host"], cfg.topk))
     assert max_abs_rel(outs[0].numpy(), ref) <= BAR_BF16
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("scoring,renorm,scale", [("sigmoid", True, 1.0), ("sigmoid", False, 2.5),
+                                                  ("softmax", False, 1.5)])
+@pytest.mark.parametrize("block_m", [0, 128])
+def test_layer_routing_variants(moe, dev, scoring, renorm, scale, block_m):
+    """The whole layer with the other routing variants (sigmoid scores, no
+    renormalisation, a scale): moe_forward's own routing is checked against
+    the oracle's (near-tie rule), and its output against the oracle layer run
+    with the routing it accepted, in full, on both weight layouts."""
+    from synth.configs import Config
+    cfg = Config(14, "variants", T=300, H=256, I=384, E=64, topk=6, groups=8, topk_group=3,
+                 x_dtype="bf16", w_std=0.05, scale=scale, renormalize=renorm,
+                 extra={"sub": ["sigmoid", "softmax"].index(scoring) * 2 + int(renorm)})
+    d = layer_inputs(cfg, dev)
+    for layout in ("plain", "packed"):
+        w1, w2 = _packed(moe, d) if layout == "packed" else (d["w1"], d["w2"])
+        w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=dev)
+        ids = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=dev)
+        out = moe.moe_forward(d["x"], d["gating"], w1, w2, cfg.topk, cfg.groups, cfg.topk_group,
+                              scoring, renorm, scale, block_m=block_m, topk_weights_out=w,
+                              topk_ids_out=ids)
+        torch.cuda.synchronize()
+        wn, idn = w.cpu().numpy(), ids.cpu().numpy()
+        check_routing(wn, idn, d["gating_host"], cfg.topk, renorm, cfg.groups, cfg.topk_group,
+                      scoring, scale)
+        ref = oracle.moe_layer_expert_loop(d["x_host"], d["w1_host"], d["w2_host"],
+                                           wn.astype(np.float64), idn)
+        err = max_abs_rel(_out_host(out), ref)
+        print("%s renorm=%s scale=%.1f block_m %d %s err=%.3e" % (scoring, renorm, scale, block_m,
+                                                                 layout, err))
+        assert err <= BAR_BF16

@@ -278,3 +278,26 @@ def test_layer_routing_variants(moe, dev, scoring, renorm, scale, block_m):
         print("%s renorm=%s scale=%.1f block_m %d %s err=%.3e" % (scoring, renorm, scale, block_m,
                                                                  layout, err))
         assert err <= BAR_BF16
+
+
+def test_layers_with_zero_tokens(moe, dev):
+    """T = 0: both layer calls return an empty output without launching,
+    for bf16 and f32 tokens and both weight layouts."""
+    E, H, I, K = 16, 256, 384, 4
+    g = torch.empty((0, E), dtype=torch.float32, device=dev)
+    w1 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=dev)
+    w2 = torch.zeros((E, H, I), dtype=torch.bfloat16, device=dev)
+    packed = (moe.moe_pack_weights(w1, "silu_mul"), moe.moe_pack_weights(w2, "none"))
+    for dtype in (torch.bfloat16, torch.float32):
+        x = torch.empty((0, H), dtype=dtype, device=dev)
+        for ws in ((w1, w2), packed) if dtype == torch.bfloat16 else ((w1, w2),):
+            out = moe.moe_forward(x, g, ws[0], ws[1], K)
+            assert out.shape == (0, H) and out.dtype == dtype
+    q1 = torch.zeros((E, 2 * I, H), dtype=torch.int8, device=dev)
+    q2 = torch.zeros((E, H, I), dtype=torch.int8, device=dev)
+    s1 = torch.ones((E, 2 * I), dtype=torch.float32, device=dev)
+    s2 = torch.ones((E, H), dtype=torch.float32, device=dev)
+    out = moe.moe_forward_w8a8(torch.empty((0, H), dtype=torch.bfloat16, device=dev), g, q1, s1,
+                               q2, s2, K)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H)

@@ -198,3 +198,34 @@ def test_forward_is_k_order_sum_of_ffn_rows(moe, dev, case):
         assert ndiff == 0
         off = moe.moe_forward_wait_flag_offset(T, cfg.H, cfg.I, E, K, bm, "bf16", layout)
         assert moe.wait_flag(ws, off) == 0
+
+
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.float16])
+@pytest.mark.parametrize("bm", [64, 128])
+def test_ffn_other_output_dtypes(moe, dev, y_dtype, bm):
+    """y in float32 or float16 (the persistent launch's other down-tile
+    epilogues): bit-identical to two moe_grouped_gemm launches writing the
+    same dtype, on both weight layouts, with H not a multiple of 256."""
+    cfg = _cfg(600, 272, 384, 16, 4, sub=10)
+    d = layer_inputs(cfg, dev)
+    K, E = cfg.topk, cfg.E
+    w, ids = moe.moe_route(d["gating"], K)
+    P = ids.numel()
+    s, e, tot = moe.moe_align_block_size(ids, E, bm)
+    for layout in ("plain", "packed"):
+        w1, w2 = d["w1"], d["w2"]
+        if layout == "packed":
+            w1, w2 = moe.moe_pack_weights(w1, "silu_mul"), moe.moe_pack_weights(w2, "none")
+        h = torch.zeros((s.numel(), cfg.I), dtype=torch.bfloat16, device=dev)
+        moe.moe_grouped_gemm(d["x"], w1, s, e, tot, bm, P, a_rows="pair", a_row_div=K,
+                             epilogue="silu_mul", C=h, c_rows="sorted")
+        y_ref = moe.moe_grouped_gemm(h, w2, s, e, tot, bm, P, a_rows="sorted", topk_weights=w,
+                                     c_dtype=y_dtype, c_rows="pair")
+        ws = torch.empty(moe.moe_grouped_ffn_workspace_size(s.numel(), E, bm), dtype=torch.uint8,
+                         device=dev)
+        _, y = moe.moe_grouped_ffn(d["x"], w1, w2, K, s, e, tot, bm, w, y_dtype=y_dtype,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        assert y.dtype == y_dtype
+        assert torch.equal(y, y_ref), layout
+        assert moe.wait_flag(ws, moe.moe_grouped_ffn_wait_flag_offset(s.numel(), bm)) == 0

@@ -39,8 +39,10 @@ def moe_align_block_size(topk_ids, num_experts, block_m):
 
 
 def align_max_padded(num_pairs, num_experts, block_m):
-    """Largest total the padding can reach: every non-empty expert adds at
-    most block_m - 1 placeholders, and at most min(E, pairs) experts are
-    non-empty; rounded up to a whole block."""
+    """Upper bound of the padded total: every non-empty expert adds at most
+    block_m - 1 placeholders, and at most min(E, pairs) experts are
+    non-empty; rounded up to a whole block.  It is reached when E >= pairs
+    (every pair alone) or when pairs - E is a multiple of block_m (every
+    expert holds 1 mod block_m pairs); otherwise the true maximum is lower."""
     bound = num_pairs + min(num_experts, num_pairs) * (block_m - 1)
     return -(-bound // block_m) * block_m

@@ -3,32 +3,32 @@
 
 import numpy as np
 
-from .gemm import silu_and_mul
+from .gemm import silu, silu_and_mul
 from .routing import grouped_topk
 
 
 def moe_layer_expert_loop(x, w1, w2, topk_weights, topk_ids):
-    """[MSG] "参考后端" (TorchMoeBackend): for every expert that some pair
-    chose, gather the tokens routed to it, run silu_and_mul(x_t @ w1[e]^T)
-    @ w2[e]^T, multiply by the routing weight, and add the rows back into
-    their tokens.  x [T, H], w1 [E, 2I, H] (gate rows first), w2 [E, H, I].
-    Returns out [T, H] float64."""
+    """The layer's definition, evaluated one expert at a time.
+
+    [MSG] "参考后端" defines the layer output of token t as
+        out[t] = sum_k w[t, k] * W2[e] ( silu(W1[e][:I] x_t) * (W1[e][I:] x_t) ),
+    e = topk_ids[t, k], and evaluates it per expert.  Here every expert that
+    occurs in topk_ids maps the rows of all the (t, k) slots that chose it in
+    one matrix product, the slot results are kept in a [T, topk, H] array,
+    and each token's slots are summed at the end.  x [T, H], w1 [E, 2I, H]
+    (gate rows first), w2 [E, H, I].  Returns out [T, H] float64."""
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids)
-    T, topk = ids.shape
-    flat_ids = ids.reshape(-1)
-    token_idx = np.repeat(np.arange(T), topk)
-    flat_w = np.asarray(topk_weights, dtype=np.float64).reshape(-1)
-    out = np.zeros((T, x.shape[1]), dtype=np.float64)
-    for e in np.unique(flat_ids):
-        sel = np.flatnonzero(flat_ids == e)
-        tokens = token_idx[sel]
-        w1e = np.asarray(w1[int(e)], dtype=np.float64)
-        w2e = np.asarray(w2[int(e)], dtype=np.float64)
-        h = silu_and_mul(x[tokens] @ w1e.T)
-        y = (h @ w2e.T) * flat_w[sel][:, None]
-        np.add.at(out, tokens, y)
-    return out
+    wts = np.asarray(topk_weights, dtype=np.float64)
+    slots = np.zeros(ids.shape + (x.shape[1],), dtype=np.float64)
+    for e in sorted(set(int(v) for v in ids.ravel())):
+        tok, slot = np.nonzero(ids == e)            # the slots routed to e
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        inter = w1e.shape[0] // 2
+        act = silu(x[tok] @ w1e[:inter].T) * (x[tok] @ w1e[inter:].T)
+        down = act @ np.asarray(w2[e], dtype=np.float64).T
+        slots[tok, slot] = wts[tok, slot][:, None] * down
+    return slots.sum(axis=1)
 
 
 def moe_layer_token_loop(x, w1, w2, topk_weights, topk_ids):

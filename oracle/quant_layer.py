@@ -49,30 +49,27 @@ def _int_dot(aq, bq):
 
 
 def moe_layer_w8a8_expert_loop(x, w1q, s1, w2q, s2, topk_weights, topk_ids):
-    """The layer above, looping over experts as [MSG] "参考后端" does.
+    """The layer above, evaluated one expert at a time: every expert that
+    occurs in topk_ids maps the rows of the (t, k) slots that chose it in one
+    exact integer product per GEMM, the scaled slot results are kept in a
+    [T, topk, H] array and each token's slots are summed at the end.
     x [T, H] (float values), w1q [E, 2I, H] int8 with s1 [E, 2I],
     w2q [E, H, I] int8 with s2 [E, H], topk_weights / topk_ids [T, topk].
     Returns out [T, H] float64."""
     ids = np.asarray(topk_ids)
-    T, topk = ids.shape
+    wts = np.asarray(topk_weights, dtype=np.float64)
     xq, sx = quantize_rows_f32(x)
     sx = sx.astype(np.float64)
-    flat_ids = ids.reshape(-1)
-    token_idx = np.repeat(np.arange(T), topk)
-    flat_w = np.asarray(topk_weights, dtype=np.float64).reshape(-1)
-    out = np.zeros((T, np.asarray(x).shape[1]), dtype=np.float64)
-    for e in np.unique(flat_ids):
-        e = int(e)
-        sel = np.flatnonzero(flat_ids == e)
-        tokens = token_idx[sel]
-        gu = _int_dot(xq[tokens], w1q[e]) * sx[tokens][:, None] * \
-            np.asarray(s1[e], dtype=np.float64)[None, :]
-        h = silu_and_mul(gu)
-        hq, sh = quantize_rows_f32(h)
-        y = _int_dot(hq, w2q[e]) * sh.astype(np.float64)[:, None] * \
-            np.asarray(s2[e], dtype=np.float64)[None, :] * flat_w[sel][:, None]
-        np.add.at(out, tokens, y)
-    return out
+    slots = np.zeros(ids.shape + (np.asarray(x).shape[1],), dtype=np.float64)
+    for e in sorted(set(int(v) for v in ids.ravel())):
+        tok, slot = np.nonzero(ids == e)            # the slots routed to e
+        acc1 = _int_dot(xq[tok], w1q[e])            # exact integer sums
+        gate_up = acc1 * sx[tok, None] * np.asarray(s1[e], dtype=np.float64)[None, :]
+        hq, sh = quantize_rows_f32(silu_and_mul(gate_up))
+        acc2 = _int_dot(hq, w2q[e])
+        scale = sh.astype(np.float64)[:, None] * np.asarray(s2[e], dtype=np.float64)[None, :]
+        slots[tok, slot] = wts[tok, slot][:, None] * scale * acc2
+    return slots.sum(axis=1)
 
 
 def moe_layer_w8a8_token_loop(x, w1q, s1, w2q, s2, topk_weights, topk_ids):

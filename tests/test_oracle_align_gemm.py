@@ -59,24 +59,64 @@ def test_align_invariants_random(seed, B):
     _check_align_invariants(ids, E, B)
 
 
-def test_align_matches_vectorised_form():
-    """Cross-formulation: the page's vectorised procedure (bincount, padded
-    counts, segment starts, stable argsort) against the expert loop."""
+def test_align_matches_rank_count():
+    """Cross-formulation written from the definition, pair by pair: pair i of
+    expert e lands at (sum over experts e' < e of count(e') rounded up to a
+    multiple of B) + (number of pairs j < i with the same expert); every
+    other entry is a placeholder, and block b's expert is the expert whose
+    padded segment covers position b * B."""
     rng = np.random.default_rng(3)
-    E, B = 13, 8
-    ids = rng.integers(0, E, size=(57, 3))
-    flat = ids.reshape(-1)
-    P = flat.size
-    counts = np.bincount(flat, minlength=E)
-    padded = (counts + B - 1) // B * B
-    seg = np.cumsum(padded) - padded
-    order = np.argsort(flat, kind="stable")
-    rank = np.arange(P) - (np.cumsum(counts) - counts)[flat[order]]
-    ref = np.full(int(padded.sum()), P)
-    ref[seg[flat[order]] + rank] = order
-    ref_e = np.repeat(np.arange(E), padded // B)
-    s, e, total = oracle.moe_align_block_size(ids, E, B)
-    assert s.tolist() == ref.tolist() and e.tolist() == ref_e.tolist()
+    for E, B, T, K in [(13, 8, 57, 3), (5, 1, 9, 2), (40, 16, 31, 4), (3, 64, 100, 1)]:
+        ids = rng.integers(0, E, size=(T, K))
+        flat = [int(v) for v in ids.reshape(-1)]
+        P = len(flat)
+        count = [flat.count(e) for e in range(E)]
+        padded = [-(-c // B) * B for c in count]
+        start = [sum(padded[:e]) for e in range(E)]
+        total = sum(padded)
+        ref = [P] * total
+        for i, e in enumerate(flat):
+            ref[start[e] + sum(1 for j in range(i) if flat[j] == e)] = i
+        ref_e = [next(e for e in range(E) if start[e] <= b * B < start[e] + padded[e])
+                 for b in range(total // B)]
+        s, eids, got_total = oracle.moe_align_block_size(ids, E, B)
+        assert got_total == total and s.tolist() == ref and eids.tolist() == ref_e
+
+
+def test_align_max_padded_values():
+    """Hand-computed values of the padded-length bound P + min(E, P)(B - 1),
+    rounded up to a whole block."""
+    cases = [  # (pairs, experts, block, bound)
+        (0, 8, 4, 0),          # nothing to place
+        (5, 8, 4, 20),         # five singleton experts, each padded to 4
+        (5, 2, 4, 12),         # 5 + 2 * 3 = 11, rounded up to 12
+        (128, 8, 16, 256),     # tiny layer: 128 + 8 * 15 = 248, rounded up to 256
+        (32768, 128, 128, 49024),   # prefill: 32768 + 128 * 127 = 49024
+        (128, 256, 64, 8192),  # decode T = 16: every pair may sit alone
+        (1, 1, 1, 1),
+        (7, 3, 1, 7),          # block 1: no padding at all
+    ]
+    for P, E, B, want in cases:
+        assert oracle.align_max_padded(P, E, B) == want, (P, E, B)
+
+
+def test_align_max_padded_brute_force():
+    """Against every assignment of P pairs to E experts on tiny sizes: the
+    bound is never exceeded, and it is reached whenever it can be (E >= P,
+    or P - E a multiple of B, which lets every used expert hold 1 mod B)."""
+    import itertools
+    for P in range(0, 6):
+        for E in range(1, 5):
+            for B in (1, 2, 3, 4):
+                best = 0
+                for assign in itertools.product(range(E), repeat=P):
+                    _, _, total = oracle.moe_align_block_size(
+                        np.array(assign, dtype=np.int64).reshape(-1, 1), E, B)
+                    best = max(best, total)
+                bound = oracle.align_max_padded(P, E, B)
+                assert best <= bound
+                if E >= P or (P - E) % B == 0:
+                    assert best == bound, (P, E, B, best, bound)
 
 
 def test_align_empty_and_single():

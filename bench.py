@@ -69,6 +69,69 @@ class Timer:
         return float(np.mean(ms)), float(np.median(ms))
 
 
+FLUSH_BYTES = 512 << 20        # larger than the 256 MB Infinity Cache and every L2
+
+
+def flushed_events(torch, fn, reps, flush):
+    """Mean and median of fn, each call event-timed after a write of the
+    whole flush buffer (outside the timed region), so no call finds the
+    previous call's data in the Infinity Cache or an L2."""
+    start = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(i & 0x7f)
+        start[i].record()
+        fn()
+        end[i].record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(start, end)]
+    return dict(mean_ms=float(np.mean(ms)), median_ms=float(np.median(ms)), reps=reps)
+
+
+def calibrate(torch, dev, timer):
+    """Ceilings measured on this GPU, for context: hipBLASLt bf16 GEMMs (a
+    dense 8192^3 and the prefill gate_up as one batched GEMM of 128 experts x
+    256 tokens x 1536 x 2048) and a 1 GiB device copy.  Run before the timed
+    layer, they also bring the GPU clock up."""
+    res = {}
+    a = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
+    c = torch.empty((8192, 8192), device=dev, dtype=torch.bfloat16)
+    for _ in range(20):
+        torch.matmul(a, b, out=c)
+    mean, med = timer.run(lambda: torch.matmul(a, b, out=c), 50)
+    res["hipblaslt_dense_8192"] = dict(ms=med, tflops=2.0 * 8192 ** 3 / med * 1e-9)
+    del a, b, c
+    xa = torch.randn((128, 256, 2048), device=dev, dtype=torch.bfloat16)
+    wb = torch.randn((128, 2048, 1536), device=dev, dtype=torch.bfloat16)
+    cb = torch.empty((128, 256, 1536), device=dev, dtype=torch.bfloat16)
+    for _ in range(20):
+        torch.bmm(xa, wb, out=cb)
+    mean, med = timer.run(lambda: torch.bmm(xa, wb, out=cb), 50)
+    res["hipblaslt_batched_gate_up"] = dict(ms=med, tflops=2.0 * 128 * 256 * 2048 * 1536 / med * 1e-9)
+    del xa, wb, cb
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    mean, med = timer.run(lambda: dst.copy_(src), 20)
+    res["device_copy_1gib"] = dict(ms=med, gbs=2.0 * (1 << 30) / med * 1e-6)
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def wall_steps(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -140,6 +203,14 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     ms = wall_steps(torch, step, steps, warmup)
     flops = 6.0 * T * K * H * I
     res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops, pack_weights_ms=pack_ms)
+    bm_used = moe.moe_forward_block_m(T, E, K, "bf16", "packed")
+    flag_off = moe.moe_forward_wait_flag_offset(T, H, I, E, K, bm_used, "bf16", "packed")
+    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    fl = flushed_events(torch, step, max(steps, 10), flush)
+    fl["tflops"] = flops / fl["mean_ms"] * 1e-9
+    res["flushed"] = fl
+    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
 
     def step_plain():
         moe.moe_forward(x, g, w1_plain, w2_plain, K, out=out, workspace=ws)
@@ -192,6 +263,12 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
             fn()
         mean, med = timer.run(fn, reps)
         br[name] = dict(mean_ms=mean, median_ms=med)
+    fflag = moe.moe_grouped_ffn_wait_flag_offset(cap, bm)
+    assert moe.wait_flag(fws, fflag) == 0, "a wait of the persistent launch gave up"
+    br["ffn_gate_up_and_down"]["flushed"] = flushed_events(
+        torch, parts["ffn_gate_up_and_down"], reps, flush)
+    assert moe.wait_flag(fws, fflag) == 0, "a wait of the persistent launch gave up"
+    del flush
     gemm1_flops = 2.0 * P * H * 2 * I
     gemm2_flops = 2.0 * P * I * H
     br["ffn_gate_up_and_down"]["tflops"] = (gemm1_flops + gemm2_flops) / \
@@ -228,6 +305,8 @@ def bench_decode(torch, moe, dev, name, steps, warmup, timer):
                         out=out, topk_ids_out=ids, workspace=ws)
 
     ms = wall_steps(torch, lambda: run(w1, w2), steps, warmup)
+    flag_off = moe.moe_forward_wait_flag_offset(T, H, I, E, K, 0, "bf16", "packed")
+    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
     n_exp = touched_experts(ids.cpu().numpy())
     per_expert = (2 * I * H + H * I) * 2
     nbytes = n_exp * per_expert + 2 * T * H * 2
@@ -285,6 +364,9 @@ def bench_int8(torch, moe, dev, steps, warmup, timer):
 
     ms = wall_steps(torch, step, steps, warmup)
     mean, med = timer.run(step, max(steps, 10))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    fl = flushed_events(torch, step, max(steps, 10), flush)
+    del flush
     ms_plain = wall_steps(torch, lambda: moe.gmm_int8(xq_d, wq, sx_d, sw, off_d, output=Y),
                           steps, warmup)
     nz = int((sizes > 0).sum())
@@ -296,6 +378,8 @@ def bench_int8(torch, moe, dev, steps, warmup, timer):
                 frac_hbm=nbytes / ms * 1e-6 / PEAK_HBM_GBS,
                 frac_int8=ops / ms * 1e-9 / PEAK_INT8_TOPS, bytes=nbytes, ops=ops,
                 weights="packed", plain_weights=dict(ms=ms_plain, gbs=nbytes / ms_plain * 1e-6),
+                flushed=dict(fl, gbs=nbytes / fl["mean_ms"] * 1e-6,
+                             frac_hbm=nbytes / fl["mean_ms"] * 1e-6 / PEAK_HBM_GBS),
                 group_sizes_min_max=[int(sizes.min()), int(sizes.max())])
 
 
@@ -370,7 +454,7 @@ def cpu_baseline(torch, prefill_inputs, target_s=12.0):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return dict(value=flops / dt * 1e-12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                seconds_per_pass=dt, passes=reps,
+                cpu_model=cpu_model(), seconds_per_pass=dt, passes=reps,
                 sample="%d pass(es) over the first %d of %d tokens of the prefill layer (route + "
                        "expert-loop layer, float64 NumPy; weights pre-decoded)" % (reps, S, cfg.T))
 
@@ -429,6 +513,8 @@ def main():
                           "warmup": args.warmup, "result": res}), flush=True)
         return
 
+    log("calibration (hipBLASLt GEMMs, device copy)")
+    calib = calibrate(torch, dev, timer)
     log("prefill layer")
     pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
     ffn = pre["breakdown"]["ffn_gate_up_and_down"]
@@ -442,7 +528,8 @@ def main():
                            "its set-up kernel)",
                     block_m=pre["block_m"],
                     flops_per_launch=pre["ffn_flops"], mean_ms=ffn["mean_ms"])
-    components = {"prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
+    components = {"calibration": calib, "prefill_flushed": pre["flushed"],
+                  "prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}
     if args.copy_calibration:
         copy_calibration(torch, dev)

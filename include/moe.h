@@ -25,9 +25,16 @@
  *   - Arguments are validated on the host before anything is enqueued.  On an
  *     error nothing is launched and a negative MOE_ERR_* code is returned;
  *     MOE_ERR_HIP reports a failed launch (hipGetLastError).  No C++
- *     exception crosses this boundary.  Calls are reentrant and hold no
- *     global state; calls that write the same buffers must be ordered by the
- *     caller (same stream, or events).
+ *     exception crosses this boundary.  Calls are reentrant; calls that
+ *     write the same buffers must be ordered by the caller (same stream, or
+ *     events).
+ *   - Process-wide state, all of it set once and never freed:
+ *       * each kernel's dynamic-LDS limit is raised on its first launch;
+ *       * each device's compute-unit count is queried once and cached (it
+ *         sizes the persistent launch; concurrent first calls store the
+ *         same value);
+ *       * the persistent launch's spin limit (moe_set_wait_spin_limit), a
+ *         process-global setting that only tests of the failure path change.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

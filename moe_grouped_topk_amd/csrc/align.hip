@@ -266,7 +266,6 @@ align_expert_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
   cursor = __shfl(cursor, 0, kWave);
   if (mine) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll 4
     for (int base = r0; base < r1; base += kWave) {
       const int i = base + lane;
       const bool hit = i < r1 && id_at(i) == e;

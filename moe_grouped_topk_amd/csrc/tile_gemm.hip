@@ -274,7 +274,11 @@ __device__ __forceinline__ int tile_tid() {
 // its conservative waits on them; the loop waits itself (vmcnt), and each
 // wait is followed by a workgroup barrier so that every wave's loads of the
 // stage have landed before any wave reads it.  The barrier's "memory" clobber
-// keeps the compiler from moving LDS reads across it.
+// keeps the compiler from moving LDS reads across it.  M0 (the LDS address)
+// is an input operand of the asm, so the compiler writes it and knows the
+// asm leaves it unchanged.  An SALU write of M0 needs one wait state before
+// an LDS-DMA load reads it; the compiler's hazard pass cannot see into the
+// asm, so the asm starts with that wait state (s_nop 0).
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -282,8 +286,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 __device__ __forceinline__ void dma16(uint32_t m0, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0), "v"(g) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(m0) : "memory");
 }
 
 // The same load with the non-temporal hint (nt), for packed weight pieces
@@ -293,15 +296,13 @@ __device__ __forceinline__ void dma16(uint32_t m0, const void* g) {
 // other tiles then miss L2 (the prefill layer ran 23% slower with the hint on
 // every packed load), and rows read as half lines are slower with it.
 __device__ __forceinline__ void dma16_nt(uint32_t m0, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :: "s"(m0), "v"(g) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" :: "v"(g), "{m0}"(m0) : "memory");
 }
 
 // The same load at agent scope (sc1): it sees stores that other XCDs made
 // with agent-scope coherent stores, which their L2 may not have written back.
 __device__ __forceinline__ void dma16_coh(uint32_t m0, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
-               :: "s"(m0), "v"(g) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" :: "v"(g), "{m0}"(m0) : "memory");
 }
 
 template <int N>

@@ -33,7 +33,7 @@ from .routing import (softmax_scores, sigmoid_scores, grouped_topk,
                       select_experts)
 from .align import moe_align_block_size, align_max_padded
 from .gemm import grouped_gemm_sorted, index_fused_gemm, silu, silu_and_mul
-from .layer import (moe_layer_expert_loop, moe_layer_token_loop,
+from .layer import (moe_layer_expert_loop, moe_layer_pair_rows, moe_layer_token_loop,
                     moe_forward, dense_swiglu)
 from .gmm import gmm, gmm_int8, quantize_weight_per_channel, quantize_per_token
 from .quant_layer import (quantize_rows_f32, moe_layer_w8a8_expert_loop,
@@ -44,7 +44,7 @@ __all__ = [
     "softmax_scores", "sigmoid_scores", "grouped_topk", "select_experts",
     "moe_align_block_size", "align_max_padded",
     "grouped_gemm_sorted", "index_fused_gemm", "silu", "silu_and_mul",
-    "moe_layer_expert_loop", "moe_layer_token_loop", "moe_forward",
+    "moe_layer_expert_loop", "moe_layer_pair_rows", "moe_layer_token_loop", "moe_forward",
     "dense_swiglu", "gmm", "gmm_int8", "quantize_weight_per_channel",
     "quantize_per_token", "bf16_bits_to_f64", "quantize_rows_f32",
     "moe_layer_w8a8_expert_loop", "moe_layer_w8a8_token_loop",

@@ -7,16 +7,17 @@ from .gemm import silu, silu_and_mul
 from .routing import grouped_topk
 
 
-def moe_layer_expert_loop(x, w1, w2, topk_weights, topk_ids):
-    """The layer's definition, evaluated one expert at a time.
+def moe_layer_pair_rows(x, w1, w2, topk_weights, topk_ids):
+    """The routing-weighted output of every (token, slot) pair, evaluated one
+    expert at a time.
 
     [MSG] "参考后端" defines the layer output of token t as
         out[t] = sum_k w[t, k] * W2[e] ( silu(W1[e][:I] x_t) * (W1[e][I:] x_t) ),
     e = topk_ids[t, k], and evaluates it per expert.  Here every expert that
     occurs in topk_ids maps the rows of all the (t, k) slots that chose it in
-    one matrix product, the slot results are kept in a [T, topk, H] array,
-    and each token's slots are summed at the end.  x [T, H], w1 [E, 2I, H]
-    (gate rows first), w2 [E, H, I].  Returns out [T, H] float64."""
+    one matrix product.  x [T, H], w1 [E, 2I, H] (gate rows first),
+    w2 [E, H, I].  Returns the terms of that sum, [T, topk, H] float64
+    (pair p = t * topk + k is row p of its [T * topk, H] view)."""
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids)
     wts = np.asarray(topk_weights, dtype=np.float64)
@@ -28,7 +29,14 @@ def moe_layer_expert_loop(x, w1, w2, topk_weights, topk_ids):
         act = silu(x[tok] @ w1e[:inter].T) * (x[tok] @ w1e[inter:].T)
         down = act @ np.asarray(w2[e], dtype=np.float64).T
         slots[tok, slot] = wts[tok, slot][:, None] * down
-    return slots.sum(axis=1)
+    return slots
+
+
+def moe_layer_expert_loop(x, w1, w2, topk_weights, topk_ids):
+    """The layer output: each token's pair terms (moe_layer_pair_rows,
+    computed one expert at a time) summed over its slots.  Returns
+    out [T, H] float64."""
+    return moe_layer_pair_rows(x, w1, w2, topk_weights, topk_ids).sum(axis=1)
 
 
 def moe_layer_token_loop(x, w1, w2, topk_weights, topk_ids):

@@ -1,6 +1,10 @@
-"""GPU parity of the whole layer, moe_forward, against the oracle: tiny
-layer in full, prefill and decode layers at full size on sampled tokens
-(each output row depends only on its own token).  Bar: max-abs-rel 2e-2."""
+"""GPU parity of the whole layer, moe_forward, against the oracle, every
+output row: the tiny layer, the prefill layer (T=4096, H=2048, I=768, E=128,
+top-8) and the decode layers (T=16 and 64, H=7168, I=2048, E=256, grouped
+top-8) at full size, in the launch configuration the benchmark times and in
+the other kernel variants.  Bar: max-abs-rel 2e-2."""
+
+import time
 
 import numpy as np
 import pytest
@@ -109,46 +113,64 @@ def prefill_inputs(dev):
     return layer_inputs(synth.CONFIGS["prefill"], dev)
 
 
-@pytest.mark.parametrize("layout", ["plain", "packed"])
-def test_prefill_layer_sampled(moe, dev, prefill_inputs, layout):
+# Oracle outputs of whole layers, keyed by config; recomputed only if a later
+# run accepted different near-tie ids.
+_ORACLE_ALL = {}
+
+
+def _oracle_all(cfg, d, w, ids):
+    hit = _ORACLE_ALL.get(cfg.name)
+    if hit is None or not (hit[0] == ids).all():
+        t0 = time.time()
+        ref = _oracle_rows(cfg, d, np.arange(cfg.T), w, ids)
+        print("oracle %s, all %d rows: %.1f s" % (cfg.name, cfg.T, time.time() - t0), flush=True)
+        _ORACLE_ALL[cfg.name] = hit = (ids.copy(), ref)
+    return hit[1]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layout", ["packed", "plain"])
+def test_prefill_layer_full(moe, dev, prefill_inputs, layout):
+    """Every one of the 4096 output rows against the oracle, in the
+    benchmark's configuration (packed weights, automatic block size) and on
+    plain weights."""
     cfg = synth.CONFIGS["prefill"]
     d = prefill_inputs
     out, w, ids = _run(moe, cfg, d, 0, dev, layout)
     check_routing(w, ids, d["gating_host"], cfg.topk, True, 1, 1, "softmax", 1.0)
     o = _out_host(out)
     assert np.isfinite(o).all()
-    rows = np.random.default_rng(3).choice(cfg.T, 48, replace=False)
-    rows = np.concatenate([rows, [0, cfg.T - 1]])
-    ref = _oracle_rows(cfg, d, rows, w, ids)
-    err = max_abs_rel(o[rows], ref)
-    print("prefill sampled err=%.3e" % err)
+    err = max_abs_rel(o, _oracle_all(cfg, d, w, ids))
+    print("prefill %s, all rows: err=%.3e" % (layout, err))
     assert err <= BAR_BF16
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["decode16", "decode64"])
-def test_decode_layer_sampled(moe, dev, name):
+def test_decode_layer_full(moe, dev, name):
+    """Every output row of the decode layers against the oracle (touched
+    experts decoded one at a time): the tile kernels on plain weights (the
+    automatic block size), the weight-streaming kernel (block_m 16) and the
+    tile kernels on packed weights (the benchmark's configuration)."""
     cfg = synth.CONFIGS[name]
     d = layer_inputs(cfg, dev)
     out, w, ids = _run(moe, cfg, d, 0, dev)
     check_routing(w, ids, d["gating_host"], cfg.topk, True, cfg.groups, cfg.topk_group,
                   "softmax", cfg.scale)
     np.testing.assert_allclose(w.sum(1), cfg.scale, rtol=1e-5)
-    o = _out_host(out)
-    assert np.isfinite(o).all()
-    rows = np.array([0, 5, cfg.T - 1])
-    ref = _oracle_rows(cfg, d, rows, w, ids)
-    err = max_abs_rel(o[rows], ref)
-    print("%s sampled err=%.3e" % (name, err))
-    assert err <= BAR_BF16
     assert moe.moe_forward_block_m(cfg.T, cfg.E, cfg.topk) == 64   # the tile kernels
-    # the weight-streaming kernel (block_m 16, plain weights) and the tile
-    # kernels on packed weights agree with the oracle too
-    out_s, _, _ = _run(moe, cfg, d, 16, dev)
-    assert max_abs_rel(_out_host(out_s)[rows], ref) <= BAR_BF16
-    out_p, _, ids_p = _run(moe, cfg, d, 0, dev, "packed")
-    assert (ids_p == ids).all()
-    assert max_abs_rel(_out_host(out_p)[rows], ref) <= BAR_BF16
+    ref = _oracle_all(cfg, d, w, ids)
+    outs = {"tile, plain": out}
+    outs["stream, block_m 16"], _, ids_s = _run(moe, cfg, d, 16, dev)
+    outs["tile, packed"], _, ids_p = _run(moe, cfg, d, 0, dev, "packed")
+    assert (ids_s == ids).all() and (ids_p == ids).all()
     del d["w1_packed"], d["w2_packed"]
+    for k, o in outs.items():
+        oh = _out_host(o)
+        assert np.isfinite(oh).all()
+        err = max_abs_rel(oh, ref)
+        print("%s %s, all rows: err=%.3e" % (name, k, err))
+        assert err <= BAR_BF16, k
 
 
 @pytest.mark.parametrize("block_m", [64, 128, 256])

@@ -63,9 +63,8 @@ def test_int8_edge_groups(moe, dev, sizes, layout):
 
 @pytest.mark.parametrize("layout", ["plain", "packed"])
 def test_int8_more_tiles_than_one_round(moe, dev, layout):
-    """About 600 tiles of 256 x 128: the first round of resident workgroups
-    and the second launch for the remaining tiles together write every
-    output once."""
+    """About 600 tiles of 256 x 128, more than one round of resident
+    workgroups: every output is written once and matches the oracle."""
     rng = np.random.default_rng(77)
     sizes = rng.integers(0, 500, size=40)
     sizes[[3, 17]] = 0

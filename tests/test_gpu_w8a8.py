@@ -117,8 +117,12 @@ def _device_quantize(w):
     return q, s
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["prefill", "decode16"])
-def test_w8a8_layer_sampled(moe, dev, name):
+def test_w8a8_layer_full(moe, dev, name):
+    """Every output row of the int8 layer at the prefill and decode (T=16)
+    shapes, packed weights, against the oracle's int8 layer run on the
+    routing the GPU accepted (itself checked against the oracle's)."""
     cfg = synth.CONFIGS[name]
     d = layer_inputs(cfg, dev)
     w1q, s1 = _device_quantize(d["w1"])
@@ -138,10 +142,9 @@ def test_w8a8_layer_sampled(moe, dev, name):
                   "softmax", cfg.scale)
     o = out.float().cpu().numpy()
     assert np.isfinite(o).all()
-    rows = np.array([0, 5, T // 2, T - 1])
     ref = oracle.moe_layer_w8a8_expert_loop(
-        d["x_host"][rows], _Int8Experts(w1q), _Int8Experts(s1), _Int8Experts(w2q),
-        _Int8Experts(s2), wn[rows].astype(np.float64), idn[rows])
-    err = max_abs_rel(o[rows], ref)
-    print("w8a8 %s sampled err=%.3e" % (name, err))
+        d["x_host"], _Int8Experts(w1q), _Int8Experts(s1), _Int8Experts(w2q),
+        _Int8Experts(s2), wn.astype(np.float64), idn)
+    err = max_abs_rel(o, ref)
+    print("w8a8 %s, all rows: err=%.3e" % (name, err))
     assert err <= BAR_INT8

@@ -204,6 +204,20 @@ def test_expert_loop_equals_token_loop():
     np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
 
 
+def test_pair_rows_are_single_slot_layers():
+    """Slot k of the pair rows is the token loop run with that slot alone;
+    the expert loop is their sum over slots."""
+    x, w1, w2, g = _rand_layer(5, K=3)
+    w, ids = oracle.grouped_topk(g, 3, True, 1, 1)
+    rows = oracle.moe_layer_pair_rows(x, w1, w2, w, ids)
+    assert rows.shape == (x.shape[0], 3, x.shape[1])
+    for k in range(3):
+        one = oracle.moe_layer_token_loop(x, w1, w2, w[:, k:k + 1], ids[:, k:k + 1])
+        np.testing.assert_allclose(rows[:, k], one, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(rows.sum(axis=1), oracle.moe_layer_expert_loop(x, w1, w2, w, ids),
+                               atol=0, rtol=0)
+
+
 def test_identical_experts_reduce_to_dense():
     """If every expert holds the same weights the renormalised layer is the
     dense SwiGLU MLP, whatever the routing; with a scale it is scaled."""

@@ -321,6 +321,31 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
                 float* topk_weights_out, int32_t* topk_ids_out, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* moe_forward_noalloc: moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as moe_forward,
+ * without ws / ws_bytes: the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per device, part of the library's code object,
+ * held from the library's first use on a device until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * call) and runs the same kernels as moe_forward.
+ *   MOE_ERR_WORKSPACE  the layer needs more than MOE_NOALLOC_SCRATCH_BYTES
+ *                      (moe_forward_workspace_size gives the need; 96 MiB
+ *                      covers, e.g., T = 64 tokens at H = 7168, I = 2048,
+ *                      E = 256, top-8);
+ *   MOE_ERR_HIP        the scratch address could not be obtained.
+ * Every call on a device shares that device's one array and leaves its
+ * contents behind: calls that overlap on one device (other streams, other
+ * host threads) race and must be serialised by the caller.  The persistent
+ * launch's wait flag (below) lands in the scratch and is not reported. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+MOE_API int moe_forward_noalloc(const void* x, int32_t x_dtype, const float* gating,
+                const void* w1, const void* w2, int32_t w_layout, int64_t T, int32_t H, int32_t I,
+                int32_t E, int32_t topk, int32_t num_expert_group,
+                int32_t topk_group, int32_t scoring, int32_t renormalize,
+                float routed_scaling_factor, int32_t block_m, void* out,
+                float* topk_weights_out, int32_t* topk_ids_out, void* stream);
+
 /* ---- wait diagnostics of the persistent launch ---------------------------
  * In the persistent gate_up + down launch (moe_grouped_ffn, and moe_forward
  * with bf16 x and block_m >= 64) a down tile polls a per-block counter until

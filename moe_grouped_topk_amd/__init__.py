@@ -20,7 +20,7 @@ __all__ = [
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
     "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
     "moe_forward_wait_flag_offset", "moe_grouped_ffn_wait_flag_offset", "moe_set_wait_spin_limit",
-    "wait_flag",
+    "wait_flag", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -76,6 +76,9 @@ def _load():
     L.moe_forward.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
                               i32, f32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, f32, i32, vp, vp, vp, vp]
+    L.moe_forward_noalloc.restype = ctypes.c_int
     L.moe_forward_wait_flag_offset.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
     L.moe_forward_wait_flag_offset.restype = i64
     L.moe_grouped_ffn_wait_flag_offset.argtypes = [i64, i32]
@@ -374,6 +377,33 @@ def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,
         _ptr(topk_weights_out, torch.float32, "topk_weights_out"),
         _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20     # MOE_NOALLOC_SCRATCH_BYTES of moe.h
+
+
+def moe_forward_noalloc(x, gating, w1, w2, topk, out, num_expert_group=1, topk_group=1,
+                        scoring="softmax", renormalize=True, routed_scaling_factor=1.0,
+                        block_m=0, topk_weights_out=None, topk_ids_out=None, stream=None):
+    """moe_forward on the library's static per-device scratch: nothing is
+    allocated, here or in the library, so `out` [T, H] (x's dtype) must be
+    given.  Calls that overlap on one device race on the scratch."""
+    torch = _torch()
+    T, H = x.shape
+    w1_ptr, l1, (E, twoI, _) = _weights(w1, "silu_mul", "w1")
+    w2_ptr, l2, _ = _weights(w2, "none", "w2")
+    if l1 != l2:
+        raise ValueError("w1 and w2 must both be plain or both packed")
+    if out is None:
+        raise ValueError("moe_forward_noalloc needs the output tensor")
+    _check("moe_forward_noalloc", lib.moe_forward_noalloc(
+        _ptr(x, None, "x"), _dtype_code(x), _ptr(gating, torch.float32, "gating"),
+        w1_ptr, w2_ptr, l1, T, H, twoI // 2, E, topk,
+        num_expert_group, topk_group, SCORING[scoring], int(bool(renormalize)),
+        float(routed_scaling_factor), block_m, _ptr(out, x.dtype, "out"),
+        _ptr(topk_weights_out, torch.float32, "topk_weights_out"),
+        _ptr(topk_ids_out, torch.int32, "topk_ids_out"), _stream(stream)))
     return out
 
 

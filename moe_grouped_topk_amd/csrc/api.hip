@@ -10,6 +10,9 @@
 #include "moe.h"   // include/ is on the include path
 #include "launch.hpp"
 
+// Workspace of moe_forward_noalloc (see scratch_address below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -27,6 +30,26 @@ std::atomic<int32_t> g_wait_spin_limit{0};
 int wait_spin_limit() {
   const int32_t v = g_wait_spin_limit.load(std::memory_order_relaxed);
   return v > 0 ? v : moe::kFusedSpinLimit;
+}
+
+// Workspace of moe_forward_noalloc: a static device array, one copy per
+// device, held until the process ends.  Its name is a host-side stand-in in
+// host code; the device address comes from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array; null if HIP fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);   // racing first calls store the same
+  return p;
 }
 
 // Shape and option checks of the routing step (pointers are checked by the caller).
@@ -406,12 +429,18 @@ size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, in
   return most;
 }
 
-int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void* w1, const void* w2,
-                int32_t w_layout, int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
-                int32_t num_expert_group, int32_t topk_group, int32_t scoring,
-                int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
-                float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
-                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward's work on a caller's workspace (ws, ws_bytes), or, with
+// use_scratch set, on this device's static scratch array (ws is ignored).
+int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void* w1,
+                 const void* w2, int32_t w_layout, int64_t T, int32_t H, int32_t I, int32_t E,
+                 int32_t topk, int32_t num_expert_group, int32_t topk_group, int32_t scoring,
+                 int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
+                 float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
+                 bool use_scratch, void* stream) {
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
   if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
@@ -424,6 +453,12 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   if (!x || !gating || !w1 || !w2 || !out) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_SHAPE;
   const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype, w_layout);
+  if (use_scratch) {
+    if (L.bytes > kScratchBytes) return MOE_ERR_WORKSPACE;
+    ws = scratch_address();
+    ws_bytes = kScratchBytes;
+    if (!ws) return MOE_ERR_HIP;
+  }
   if (!ws || ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
   if (L.max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
@@ -488,6 +523,32 @@ int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void*
   }
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void* x, int32_t x_dtype, const float* gating, const void* w1, const void* w2,
+                int32_t w_layout, int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                int32_t num_expert_group, int32_t topk_group, int32_t scoring,
+                int32_t renormalize, float routed_scaling_factor, int32_t block_m, void* out,
+                float* topk_weights_out, int32_t* topk_ids_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  return forward_impl(x, x_dtype, gating, w1, w2, w_layout, T, H, I, E, topk, num_expert_group,
+                      topk_group, scoring, renormalize, routed_scaling_factor, block_m, out,
+                      topk_weights_out, topk_ids_out, ws, ws_bytes, false, stream);
+}
+
+int moe_forward_noalloc(const void* x, int32_t x_dtype, const float* gating, const void* w1,
+                        const void* w2, int32_t w_layout, int64_t T, int32_t H, int32_t I,
+                        int32_t E, int32_t topk, int32_t num_expert_group, int32_t topk_group,
+                        int32_t scoring, int32_t renormalize, float routed_scaling_factor,
+                        int32_t block_m, void* out, float* topk_weights_out,
+                        int32_t* topk_ids_out, void* stream) {
+  return forward_impl(x, x_dtype, gating, w1, w2, w_layout, T, H, I, E, topk, num_expert_group,
+                      topk_group, scoring, renormalize, routed_scaling_factor, block_m, out,
+                      topk_weights_out, topk_ids_out, nullptr, 0, true, stream);
 }
 
 int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,

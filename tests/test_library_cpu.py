@@ -225,6 +225,33 @@ def test_forward_validation(mod):
     assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
 
 
+def test_forward_noalloc_validation(mod):
+    """The allocation-free layer call validates like moe_forward, and rejects
+    a layer whose workspace exceeds the static scratch before touching HIP."""
+    L, d = mod.lib, _defines()
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+MOE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mod.NOALLOC_SCRATCH_BYTES
+    f = ctypes.c_void_p(256)
+    args = [f, 1, f, f, f, 0, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, None]
+    assert L.moe_forward_noalloc(*args[:1], 5, *args[2:]) == d["MOE_ERR_DTYPE"]
+    a = list(args); a[7] = 100      # H % 16
+    assert L.moe_forward_noalloc(*a) == d["MOE_ERR_SHAPE"]
+    a = list(args); a[16] = 24      # block_m
+    assert L.moe_forward_noalloc(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[0] = None
+    assert L.moe_forward_noalloc(*a) == d["MOE_ERR_NULL"]
+    a = list(args); a[6] = 0        # no tokens: nothing to do
+    assert L.moe_forward_noalloc(*a) == d["MOE_OK"]
+    # the prefill layer needs about 328 MiB of workspace: more than the scratch
+    big = [4096, 2048, 768, 128, 8]
+    assert mod.moe_forward_workspace_size(*big) > mod.NOALLOC_SCRATCH_BYTES
+    a = list(args); a[6:11] = big
+    assert L.moe_forward_noalloc(*a) == d["MOE_ERR_WORKSPACE"]
+    # decode at T = 64 (H = 7168, I = 2048, E = 256, top-8) fits
+    assert mod.moe_forward_workspace_size(64, 7168, 2048, 256, 8) <= mod.NOALLOC_SCRATCH_BYTES
+
+
 def test_packed_weights_size_and_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)

@@ -2,9 +2,8 @@
 
 A step is one moe_forward of the prefill-shaped layer (T=4096, H=2048,
 I=768, E=128, top-8 softmax with renormalisation): routing, alignment, the
-gate_up GEMM with SiLU*up and the down GEMM with the routing weight (one
-persistent launch), and the top-k reduce, on seeded synthetic inputs
-already resident in HBM.  The
+gate_up GEMM with SiLU*up, the down GEMM with the routing weight, and the
+top-k reduce, on seeded synthetic inputs already resident in HBM.  The
 expert weights are in the packed tile layout (moe_pack_weights, done once
 before timing, as at model load; its time is reported).  The headline value
 is that step's throughput in TFLOP/s (6*T*topk*H*I algorithmic FLOPs,
@@ -36,10 +35,11 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
-# HBM bytes per launch of the fused gate_up + down kernel, from rocprofv3 FETCH_SIZE /
-# WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill layer).  Only
-# valid for that kernel configuration; null for any other block size or once the kernel changes.
-FFN_TRAFFIC = {"block_m": 128, "bytes": 1.929e9 + 0.188e9}
+# HBM bytes per launch of the gate_up GEMM (the layer's dominant kernel), from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill
+# layer).  Only valid for that kernel configuration; None for any other block size or once the
+# kernel has changed since the counters were taken.
+GATE_UP_TRAFFIC = {"block_m": 128, "bytes": None}
 
 
 def log(msg):
@@ -203,14 +203,10 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     ms = wall_steps(torch, step, steps, warmup)
     flops = 6.0 * T * K * H * I
     res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops, pack_weights_ms=pack_ms)
-    bm_used = moe.moe_forward_block_m(T, E, K, "bf16", "packed")
-    flag_off = moe.moe_forward_wait_flag_offset(T, H, I, E, K, bm_used, "bf16", "packed")
-    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     fl = flushed_events(torch, step, max(steps, 10), flush)
     fl["tflops"] = flops / fl["mean_ms"] * 1e-9
     res["flushed"] = fl
-    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
 
     def step_plain():
         moe.moe_forward(x, g, w1_plain, w2_plain, K, out=out, workspace=ws)
@@ -229,9 +225,9 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
         del q1, q2, ws8
 
     # Per-kernel breakdown: the launches moe_forward makes (route, the
-    # two-kernel alignment, both GEMMs in one persistent launch), each timed
-    # with HIP events on the stream they run on; the top-k reduce is the rest
-    # of the step.  The two GEMMs as separate launches are timed for reference.
+    # two-kernel alignment, gate_up with SiLU*up, down with the routing
+    # weight), each timed with HIP events on the stream they run on; the
+    # top-k reduce is the rest of the step.
     P = T * K
     bm = moe.moe_forward_block_m(T, E, K, "bf16", "packed")   # the block size used here
     w_t, ids_t = moe.moe_route(g, K)
@@ -240,20 +236,16 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     cap = sorted_ids.numel()
     h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((P, H), dtype=torch.bfloat16, device=dev)   # y in x's dtype
-    fws = torch.empty(moe.moe_grouped_ffn_workspace_size(cap, E, bm), dtype=torch.uint8,
-                      device=dev)
     torch.cuda.synchronize()
     reps = max(steps, 10)
     parts = {
         "route": lambda: moe.moe_route(g, K, topk_weights=w_t, topk_ids=ids_t),
         "align": lambda: moe.moe_align_block_size(ids_t, E, bm, sorted_ids, eids, total,
                                                   workspace=aws),
-        "ffn_gate_up_and_down": lambda: moe.moe_grouped_ffn(
-            x, w1, w2, K, sorted_ids, eids, total, bm, w_t, h=h, y=y, workspace=fws),
-        "separate_gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
+        "gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
             x, w1, sorted_ids, eids, total, bm, P, a_rows="pair", a_row_div=K,
             epilogue="silu_mul", C=h, c_rows="sorted"),
-        "separate_gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
+        "gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
             h, w2, sorted_ids, eids, total, bm, P, a_rows="sorted", topk_weights=w_t,
             C=y, c_rows="pair"),
     }
@@ -263,24 +255,19 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
             fn()
         mean, med = timer.run(fn, reps)
         br[name] = dict(mean_ms=mean, median_ms=med)
-    fflag = moe.moe_grouped_ffn_wait_flag_offset(cap, bm)
-    assert moe.wait_flag(fws, fflag) == 0, "a wait of the persistent launch gave up"
-    br["ffn_gate_up_and_down"]["flushed"] = flushed_events(
-        torch, parts["ffn_gate_up_and_down"], reps, flush)
-    assert moe.wait_flag(fws, fflag) == 0, "a wait of the persistent launch gave up"
+    br["gemm1_gate_up_silu"]["flushed"] = flushed_events(
+        torch, parts["gemm1_gate_up_silu"], reps, flush)
     del flush
     gemm1_flops = 2.0 * P * H * 2 * I
     gemm2_flops = 2.0 * P * I * H
-    br["ffn_gate_up_and_down"]["tflops"] = (gemm1_flops + gemm2_flops) / \
-        br["ffn_gate_up_and_down"]["mean_ms"] * 1e-9
-    br["separate_gemm1_gate_up_silu"]["tflops"] = \
-        gemm1_flops / br["separate_gemm1_gate_up_silu"]["mean_ms"] * 1e-9
-    br["separate_gemm2_down_weighted"]["tflops"] = \
-        gemm2_flops / br["separate_gemm2_down_weighted"]["mean_ms"] * 1e-9
+    br["gemm1_gate_up_silu"]["tflops"] = \
+        gemm1_flops / br["gemm1_gate_up_silu"]["mean_ms"] * 1e-9
+    br["gemm2_down_weighted"]["tflops"] = \
+        gemm2_flops / br["gemm2_down_weighted"]["mean_ms"] * 1e-9
     br["remainder_reduce_and_gaps_ms"] = ms - sum(
-        br[k]["mean_ms"] for k in ("route", "align", "ffn_gate_up_and_down"))
+        br[k]["mean_ms"] for k in ("route", "align", "gemm1_gate_up_silu", "gemm2_down_weighted"))
     res["breakdown"] = br
-    res["ffn_flops"] = gemm1_flops + gemm2_flops
+    res["gemm1_flops"] = gemm1_flops
     res["block_m"] = bm
     res["inputs"] = (x_host, g_host, w1_plain, w2_plain)
     return res
@@ -305,8 +292,6 @@ def bench_decode(torch, moe, dev, name, steps, warmup, timer):
                         out=out, topk_ids_out=ids, workspace=ws)
 
     ms = wall_steps(torch, lambda: run(w1, w2), steps, warmup)
-    flag_off = moe.moe_forward_wait_flag_offset(T, H, I, E, K, 0, "bf16", "packed")
-    assert moe.wait_flag(ws, flag_off) == 0, "a wait of the persistent launch gave up"
     n_exp = touched_experts(ids.cpu().numpy())
     per_expert = (2 * I * H + H * I) * 2
     nbytes = n_exp * per_expert + 2 * T * H * 2
@@ -517,17 +502,16 @@ def main():
     calib = calibrate(torch, dev, timer)
     log("prefill layer")
     pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
-    ffn = pre["breakdown"]["ffn_gate_up_and_down"]
-    roofline = dict(bound="mfma", achieved=ffn["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=ffn["tflops"] / PEAK_BF16_TFLOPS,
-                    traffic=(FFN_TRAFFIC["bytes"] if pre["block_m"] == FFN_TRAFFIC["block_m"]
+    g1 = pre["breakdown"]["gemm1_gate_up_silu"]
+    roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=g1["tflops"] / PEAK_BF16_TFLOPS,
+                    traffic=(GATE_UP_TRAFFIC["bytes"] if pre["block_m"] == GATE_UP_TRAFFIC["block_m"]
                              else None),
                     traffic_unit="bytes per launch",
-                    kernel="moe_ffn_fused_kernel (gate_up with SiLU*up, then down with the "
-                           "routing weight, one persistent launch, packed weights; timed with "
-                           "its set-up kernel)",
+                    kernel="moe_gemm_dma_kernel, gate_up with the SiLU*up epilogue (the layer's "
+                           "dominant kernel), packed weights",
                     block_m=pre["block_m"],
-                    flops_per_launch=pre["ffn_flops"], mean_ms=ffn["mean_ms"])
+                    flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
     components = {"calibration": calib, "prefill_flushed": pre["flushed"],
                   "prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}

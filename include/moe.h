@@ -30,11 +30,8 @@
  *     events).
  *   - Process-wide state, all of it set once and never freed:
  *       * each kernel's dynamic-LDS limit is raised on its first launch;
- *       * each device's compute-unit count is queried once and cached (it
- *         sizes the persistent launch; concurrent first calls store the
- *         same value);
- *       * the persistent launch's spin limit (moe_set_wait_spin_limit), a
- *         process-global setting that only tests of the failure path change.
+ *       * the static scratch of moe_forward_noalloc (one array per device,
+ *         its address looked up once per device).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -234,55 +231,14 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
                      const float* topk_weights, int32_t epilogue, void* C,
                      int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream);
 
-/* ---- both GEMMs in one launch ------------------------------------------
- * moe_grouped_ffn: the two fused_moe_kernel calls of [MSG] fused MoE
- * (FusedMoeBackend.forward: gate_up with silu_and_mul, then down with the
- * routing weight), as one persistent launch for bf16 tokens.  With
- * moe_grouped_gemm's notation, for every valid entry p at sorted position s
- * of a block of expert e:
- *     h[s] = silu(x[p / topk] . W1[e][0:I]^T) * (x[p / topk] . W1[e][I:2I]^T)
- *     y[p] = topk_weights[p] * (h[s] . W2[e]^T)
- * i.e. moe_grouped_gemm(x, MOE_ROWS_PAIR, topk, w1, EPILOGUE_SILU_MUL -> h,
- * MOE_ROWS_SORTED) followed by moe_grouped_gemm(h, MOE_ROWS_SORTED, w2,
- * topk_weights -> y, MOE_ROWS_PAIR), with the same tiles and arithmetic (the
- * results are bit-identical).  A down tile starts as soon as every gate_up
- * tile of its token block has written its part of h, so the two GEMMs
- * overlap instead of each ending with a partly idle device.
- *
- *   x        [T, H] bf16.
- *   w1, w2   [E, 2I, H] and [E, H, I] bf16, both plain or both packed
- *            (w_layout; w1 packed with MOE_EPILOGUE_SILU_MUL, w2 with
- *            MOE_EPILOGUE_NONE).
- *   sorted_token_ids / expert_ids / num_tokens_post_padded: as written by
- *            moe_align_block_size for the T * topk pairs with the same
- *            block_m; max_padded is the capacity of sorted_token_ids.
- *   topk_weights  [T * topk] f32, pair order.
- *   h        [max_padded, I] bf16 out (placeholder rows are not written).
- *   y        [T * topk, H] out in y_dtype (F32, BF16 or F16).
- *   block_m  64, 128 or 256.
- *   ws       at least moe_grouped_ffn_workspace_size(max_padded, E,
- *            block_m) bytes, 256-byte aligned; its contents need not be
- *            initialised (a small set-up kernel runs first).
- * Calls that share a workspace must not overlap in time.
- * Requirements: H % 16 == 0, I % 16 == 0, E <= MOE_MAX_EXPERTS, x, w1, w2,
- * h and y 16-byte aligned.  T = 0 is a no-op.
- */
-MOE_API size_t moe_grouped_ffn_workspace_size(int64_t max_padded, int32_t E, int32_t block_m);
-
-MOE_API int moe_grouped_ffn(const void* x, int64_t T, int32_t H, int32_t topk, const void* w1,
-                            const void* w2, int32_t w_layout, int32_t E, int32_t I,
-                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                            const int32_t* num_tokens_post_padded, int64_t max_padded,
-                            int32_t block_m, const float* topk_weights, void* h, void* y,
-                            int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
-
 /* ---- whole layer -------------------------------------------------------
  * moe_forward: [MSG] fused MoE, FusedMoeBackend.forward, with routing per
  * moe_route: route -> align -> gate_up GEMM with silu(gate)*up in its
  * epilogue (intermediate h kept in sorted order, bf16) -> down GEMM times
  * the routing weight -> per-token sum over the topk slots, written in x's
  * dtype.  out[t] = sum_k w[t,k] * W2[e] (silu(W1g[e] x[t]) * (W1u[e] x[t])).
- * With bf16 x and block_m >= 64 the two GEMMs run as in moe_grouped_ffn.
+ * The GEMMs are two moe_grouped_gemm launches (gate_up into h in sorted
+ * order, then down into per-pair rows y) and the sum is a third launch.
  *
  *   x        [T, H] bf16 or f32 (x_dtype); out [T, H] in the same dtype.
  *   gating   [T, E] f32 logits.
@@ -336,8 +292,7 @@ MOE_API int moe_forward(const void* x, int32_t x_dtype, const float* gating,
  *   MOE_ERR_HIP        the scratch address could not be obtained.
  * Every call on a device shares that device's one array and leaves its
  * contents behind: calls that overlap on one device (other streams, other
- * host threads) race and must be serialised by the caller.  The persistent
- * launch's wait flag (below) lands in the scratch and is not reported. */
+ * host threads) race and must be serialised by the caller. */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 MOE_API int moe_forward_noalloc(const void* x, int32_t x_dtype, const float* gating,
                 const void* w1, const void* w2, int32_t w_layout, int64_t T, int32_t H, int32_t I,
@@ -345,39 +300,6 @@ MOE_API int moe_forward_noalloc(const void* x, int32_t x_dtype, const float* gat
                 int32_t topk_group, int32_t scoring, int32_t renormalize,
                 float routed_scaling_factor, int32_t block_m, void* out,
                 float* topk_weights_out, int32_t* topk_ids_out, void* stream);
-
-/* ---- wait diagnostics of the persistent launch ---------------------------
- * In the persistent gate_up + down launch (moe_grouped_ffn, and moe_forward
- * with bf16 x and block_m >= 64) a down tile polls a per-block counter until
- * every gate_up tile of its token block has stored its part of h.  Each poll
- * loop is bounded: after the spin limit (about a second by default) the tile
- * stops waiting, sets a flag and reads h as it is, so a broken launch still
- * ends instead of hanging the GPU; the output of such a launch is wrong.  By
- * construction every gate_up tile a down tile waits for is already running,
- * so the limit is a safety net, not part of normal operation.
- * The flag is one int32 in the caller's workspace, zeroed at the start of
- * every launch and set to 1 by a wait that hit the limit; it keeps its value
- * until the next call on that workspace.  Reading it is up to the caller
- * (after the launch has completed, e.g. a stream sync).
- *
- * moe_forward_wait_flag_offset: byte offset of the flag in moe_forward's
- *   workspace for these arguments (the same ones as moe_forward's; block_m 0
- *   = the automatic choice).  MOE_ERR_CONFIG if this layer runs no
- *   persistent launch (f32 x, block_m 16/32, or the one-launch small layer),
- *   other negative MOE_ERR_* codes for invalid arguments.
- * moe_grouped_ffn_wait_flag_offset: the same for moe_grouped_ffn's
- *   workspace (max_padded and block_m as passed to it).
- * moe_set_wait_spin_limit: polls before a wait gives up, for every later
- *   launch in this process (0 restores the default).  A hook for tests of
- *   the failure path: a tiny limit makes waits give up early, so the flag
- *   is set while every kernel still ends normally.  MOE_ERR_CONFIG if
- *   spins < 0.  Not synchronised with launches already enqueued.
- */
-MOE_API int64_t moe_forward_wait_flag_offset(int64_t T, int32_t H, int32_t I, int32_t E,
-                                             int32_t topk, int32_t block_m, int32_t x_dtype,
-                                             int32_t w_layout);
-MOE_API int64_t moe_grouped_ffn_wait_flag_offset(int64_t max_padded, int32_t block_m);
-MOE_API int moe_set_wait_spin_limit(int32_t spins);
 
 /* ---- INT8 activations and the INT8 fused layer ------------------------
  * moe_quantize_rows: symmetric per-row int8 quantisation, [GMM] 3.2 (per

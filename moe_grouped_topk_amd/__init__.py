@@ -15,12 +15,10 @@ import os
 __all__ = [
     "MoeError", "LIB_PATH", "lib", "moe_status_string", "moe_route",
     "moe_align_max_padded", "moe_align_workspace_size", "moe_align_block_size", "moe_grouped_gemm",
-    "moe_grouped_ffn_workspace_size", "moe_grouped_ffn",
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
     "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
-    "moe_forward_wait_flag_offset", "moe_grouped_ffn_wait_flag_offset", "moe_set_wait_spin_limit",
-    "wait_flag", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -64,11 +62,6 @@ def _load():
     L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
                                    i32, i64, vp, i32, vp, i32, i64, i32, vp]
     L.moe_grouped_gemm.restype = ctypes.c_int
-    L.moe_grouped_ffn_workspace_size.argtypes = [i64, i32, i32]
-    L.moe_grouped_ffn_workspace_size.restype = sz
-    L.moe_grouped_ffn.argtypes = [vp, i64, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, i64, i32,
-                                  vp, vp, vp, i32, vp, sz, vp]
-    L.moe_grouped_ffn.restype = ctypes.c_int
     L.moe_forward_block_m.argtypes = [i64, i32, i32, i32, i32]
     L.moe_forward_block_m.restype = i32
     L.moe_forward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
@@ -79,12 +72,6 @@ def _load():
     L.moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32,
                                       i32, i32, f32, i32, vp, vp, vp, vp]
     L.moe_forward_noalloc.restype = ctypes.c_int
-    L.moe_forward_wait_flag_offset.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
-    L.moe_forward_wait_flag_offset.restype = i64
-    L.moe_grouped_ffn_wait_flag_offset.argtypes = [i64, i32]
-    L.moe_grouped_ffn_wait_flag_offset.restype = i64
-    L.moe_set_wait_spin_limit.argtypes = [i32]
-    L.moe_set_wait_spin_limit.restype = ctypes.c_int
     L.gmm_int8.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.moe_quantize_rows.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     L.moe_quantize_rows.restype = ctypes.c_int
@@ -274,46 +261,6 @@ def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded,
     return C
 
 
-def moe_grouped_ffn_workspace_size(max_padded, E, block_m):
-    return int(lib.moe_grouped_ffn_workspace_size(max_padded, E, block_m))
-
-
-def moe_grouped_ffn(x, w1, w2, topk, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                    block_m, topk_weights, h=None, y=None, y_dtype=None, workspace=None,
-                    stream=None):
-    """Both GEMMs of the layer in one launch: x [T, H] bf16, w1 [E, 2I, H] and
-    w2 [E, H, I] bf16 (both plain or both PackedWeights), the alignment of the
-    T * topk pairs with this block_m, topk_weights [T, topk] f32.  Returns
-    (h [max_padded, I] bf16 in sorted order, y [T * topk, H] weighted, pair
-    order, of y_dtype (default x's dtype))."""
-    torch = _torch()
-    T, H = x.shape
-    w1_ptr, l1, (E, twoI, _) = _weights(w1, "silu_mul", "w1")
-    w2_ptr, l2, _ = _weights(w2, "none", "w2")
-    if l1 != l2:
-        raise ValueError("w1 and w2 must both be plain or both packed")
-    I = twoI // 2
-    max_padded = sorted_token_ids.numel()
-    if expert_ids.numel() < max_padded // block_m:
-        raise ValueError("expert_ids is smaller than sorted_token_ids / block_m")
-    if h is None:
-        h = torch.empty((max_padded, I), dtype=torch.bfloat16, device=x.device)
-    if y is None:
-        y = torch.empty((T * topk, H), dtype=y_dtype or x.dtype, device=x.device)
-    need = moe_grouped_ffn_workspace_size(max_padded, E, block_m)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _check("moe_grouped_ffn", lib.moe_grouped_ffn(
-        _ptr(x, torch.bfloat16, "x"), T, H, topk, w1_ptr, w2_ptr, l1, E, I,
-        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
-        _ptr(expert_ids, torch.int32, "expert_ids"),
-        _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
-        max_padded, block_m, _ptr(topk_weights, torch.float32, "topk_weights"),
-        _ptr(h, torch.bfloat16, "h"), _ptr(y, None, "y"), _dtype_code(y),
-        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
-    return h, y
-
-
 def moe_forward_block_m(T, E, topk, x_dtype="bf16", weights="plain"):
     """Block size moe_forward picks for block_m=0."""
     return int(lib.moe_forward_block_m(T, E, topk, DTYPE[x_dtype], WEIGHTS[weights]))
@@ -321,33 +268,6 @@ def moe_forward_block_m(T, E, topk, x_dtype="bf16", weights="plain"):
 
 def moe_forward_workspace_size(T, H, I, E, topk, block_m=0):
     return int(lib.moe_forward_workspace_size(T, H, I, E, topk, block_m))
-
-
-def moe_forward_wait_flag_offset(T, H, I, E, topk, block_m=0, x_dtype="bf16", weights="plain"):
-    """Byte offset, in moe_forward's workspace, of the int32 flag that a
-    persistent launch sets when one of its waits hit the spin limit."""
-    off = int(lib.moe_forward_wait_flag_offset(T, H, I, E, topk, block_m, DTYPE[x_dtype],
-                                               WEIGHTS[weights]))
-    _check("moe_forward_wait_flag_offset", off if off < 0 else 0)
-    return off
-
-
-def moe_grouped_ffn_wait_flag_offset(max_padded, block_m):
-    """The same flag's byte offset in moe_grouped_ffn's workspace."""
-    off = int(lib.moe_grouped_ffn_wait_flag_offset(max_padded, block_m))
-    _check("moe_grouped_ffn_wait_flag_offset", off if off < 0 else 0)
-    return off
-
-
-def moe_set_wait_spin_limit(spins):
-    """Polls before a persistent launch's wait gives up (0: the default)."""
-    _check("moe_set_wait_spin_limit", lib.moe_set_wait_spin_limit(spins))
-
-
-def wait_flag(workspace, offset):
-    """The flag at `offset` of a uint8 workspace tensor, read after the
-    stream's work has completed (this synchronises)."""
-    return int(workspace[offset:offset + 4].view(_torch().int32).item())
 
 
 def moe_forward(x, gating, w1, w2, topk, num_expert_group=1, topk_group=1,

@@ -304,12 +304,8 @@ constexpr int kPlaceWaves = kPlaceThreads / kWave;
 
 __global__ void __launch_bounds__(kCountThreads)
 align_count_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int chunk,
-                   int32_t* __restrict__ hist, int32_t* __restrict__ zero, int nzero) {
+                   int32_t* __restrict__ hist) {
   extern __shared__ int cnt[];
-  // nzero is a multiple of 4 and zero 16-byte aligned: all workgroups clear it
-  for (int i = blockIdx.x * kCountThreads + threadIdx.x; i < nzero / 4;
-       i += gridDim.x * kCountThreads)
-    reinterpret_cast<int4*>(zero)[i] = make_int4(0, 0, 0, 0);
   for (int e = threadIdx.x; e < E; e += kCountThreads) cnt[e] = 0;
   __syncthreads();
   const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
@@ -360,7 +356,7 @@ __global__ void __launch_bounds__(kPlaceThreads)
 align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, int chunk, int nchunk,
                    const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
                    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out,
-                   int max_padded, int32_t* __restrict__ blk_start) {
+                   int max_padded) {
   extern __shared__ int smem[];
   int* seg = smem;                               // [E + 1] segment starts
   int* cur = seg + (E + 1);                      // [kPlaceWaves][E] per-wave cursors
@@ -486,8 +482,6 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
   for (int s = total + first; s < max_padded; s += stride) sorted_ids[s] = P;
   for (int b = total / B + first; b < max_padded / B; b += stride) expert_ids[b] = -1;
   if (c == 0 && tid == 0) *total_out = total;
-  if (c == 0 && blk_start)
-    for (int e = tid; e <= E; e += kPlaceThreads) blk_start[e] = seg[e] / B;
 }
 
 int64_t align_ws_chunk(int64_t P) {
@@ -503,13 +497,11 @@ size_t align_ws_bytes(int64_t P, int E) {
 
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
-                           hipStream_t stream, int32_t* zero, int nzero, int32_t* blk_start) {
-  if (zero && ((nzero & 3) != 0 || (reinterpret_cast<uintptr_t>(zero) & 15) != 0))
-    return hipErrorInvalidValue;
+                           hipStream_t stream) {
   const int64_t chunk = align_ws_chunk(P);
   const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
   hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
-                     stream, topk_ids, (int)P, E, (int)chunk, hist, zero, zero ? nzero : 0);
+                     stream, topk_ids, (int)P, E, (int)chunk, hist);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
@@ -520,7 +512,7 @@ hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int
   }
   hipLaunchKernelGGL(align_place_kernel, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
                      (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
-                     (int)max_padded, blk_start);
+                     (int)max_padded);
   return hipGetLastError();
 }
 

@@ -23,15 +23,6 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Spin limit of the persistent launch's waits, set by moe_set_wait_spin_limit
-// (0: the default).
-std::atomic<int32_t> g_wait_spin_limit{0};
-
-int wait_spin_limit() {
-  const int32_t v = g_wait_spin_limit.load(std::memory_order_relaxed);
-  return v > 0 ? v : moe::kFusedSpinLimit;
-}
-
 // Workspace of moe_forward_noalloc: a static device array, one copy per
 // device, held until the process ends.  Its name is a host-side stand-in in
 // host code; the device address comes from hipGetSymbolAddress, looked up once
@@ -133,7 +124,7 @@ int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t 
 bool valid_layout(int32_t l) { return l == MOE_WEIGHTS_PLAIN || l == MOE_WEIGHTS_PACKED; }
 
 struct ForwardLayout {
-  size_t w, ids, sorted, eids, total, hist, ctr, bstart, h, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, h, y, bytes;
   int64_t max_padded;
   int block_m;
   bool small;   // the layer after routing runs as one launch (small_layer.hip)
@@ -160,10 +151,6 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.eids = take(sizeof(int32_t) * (size_t)(L.max_padded / L.block_m));
   L.total = take(sizeof(int32_t));
   L.hist = take(moe::align_ws_bytes(P, E));
-  // the persistent launch's counters, rounded up to whole 16-byte pieces (the
-  // alignment zeroes them with 16-byte stores)
-  L.ctr = take(sizeof(int32_t) * round_up((size_t)moe::fused_counters(L.max_padded / L.block_m), 4));
-  L.bstart = take(sizeof(int32_t) * ((size_t)E + 1));
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.small = use_small_layer(T, H, I, E, topk, block_m, w_layout);
@@ -322,97 +309,11 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   return enqueue_gemm(a, as_stream(stream));
 }
 
-size_t moe_grouped_ffn_workspace_size(int64_t max_padded, int32_t E, int32_t block_m) {
-  if (max_padded < 0 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
-  if (block_m != 64 && block_m != 128 && block_m != 256) return 0;
-  return round_up(sizeof(int32_t) * (size_t)moe::fused_counters(max_padded / block_m), 256) +
-         sizeof(int32_t) * ((size_t)E + 1);
-}
-
-int moe_grouped_ffn(const void* x, int64_t T, int32_t H, int32_t topk, const void* w1,
-                    const void* w2, int32_t w_layout, int32_t E, int32_t I,
-                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                    const int32_t* num_tokens_post_padded, int64_t max_padded, int32_t block_m,
-                    const float* topk_weights, void* h, void* y, int32_t y_dtype, void* ws,
-                    size_t ws_bytes, void* stream) {
-  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
-  if (block_m != 64 && block_m != 128 && block_m != 256) return MOE_ERR_CONFIG;
-  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F16)
-    return MOE_ERR_DTYPE;
-  if (T < 0 || topk < 1 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
-  if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0) return MOE_ERR_SHAPE;
-  if (T * (int64_t)topk >= INT32_MAX) return MOE_ERR_SHAPE;
-  if (max_padded < 0 || max_padded % block_m != 0) return MOE_ERR_SHAPE;
-  if (T == 0 || max_padded == 0) return MOE_OK;
-  if (!x || !w1 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
-      !topk_weights || !h || !y)
-    return MOE_ERR_NULL;
-  const size_t need = moe_grouped_ffn_workspace_size(max_padded, E, block_m);
-  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-    return MOE_ERR_WORKSPACE;
-  const int64_t P = T * topk;
-  moe::FusedArgs f{};
-  moe::MoeGemmArgs& g1 = f.g1;
-  g1.A = x; g1.a_dtype = MOE_DTYPE_BF16; g1.lda = H; g1.a_rows = MOE_ROWS_PAIR; g1.a_row_div = topk;
-  g1.B = w1; g1.b_packed = w_layout == MOE_WEIGHTS_PACKED; g1.E = E; g1.N = 2 * (int64_t)I;
-  g1.K = H; g1.sorted_ids = sorted_token_ids; g1.expert_ids = expert_ids;
-  g1.total = num_tokens_post_padded; g1.max_padded = max_padded; g1.block_m = block_m;
-  g1.num_valid = P; g1.topk_weights = nullptr; g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h;
-  g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I; g1.c_rows = MOE_ROWS_SORTED;
-  int st = check_gemm(g1);
-  if (st != MOE_OK) return st;
-  moe::MoeGemmArgs& g2 = f.g2;
-  g2 = g1;
-  g2.A = h; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1;
-  g2.B = w2; g2.N = H; g2.K = I; g2.topk_weights = topk_weights;
-  g2.epilogue = MOE_EPILOGUE_NONE; g2.C = y; g2.c_dtype = y_dtype; g2.ldc = H;
-  g2.c_rows = MOE_ROWS_PAIR;
-  st = check_gemm(g2);
-  if (st != MOE_OK) return st;
-  const int64_t nblk_max = max_padded / block_m;
-  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-  f.ctr = reinterpret_cast<int32_t*>(base);
-  int32_t* bs = reinterpret_cast<int32_t*>(
-      base + round_up(sizeof(int32_t) * (size_t)moe::fused_counters(nblk_max), 256));
-  f.blk_start = bs;
-  f.nblk_max = (int)nblk_max;
-  f.spin_limit = wait_spin_limit();
-  hipStream_t s = as_stream(stream);
-  hipError_t err = moe::launch_ffn_prep(expert_ids, num_tokens_post_padded, block_m, E, nblk_max,
-                                        bs, f.ctr, s);
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_moe_ffn_fused(f, s));
-}
-
 int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
   if (T < 0 || E < 1 || topk < 1) return -1;
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return -1;
   if (!valid_layout(w_layout)) return -1;
   return choose_block_m(T, E, topk, x_dtype, w_layout);
-}
-
-int64_t moe_forward_wait_flag_offset(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
-                                     int32_t block_m, int32_t x_dtype, int32_t w_layout) {
-  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return MOE_ERR_SHAPE;
-  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
-  if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
-  if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
-  const ForwardLayout L = forward_layout(T, H, I, E, topk, block_m, x_dtype, w_layout);
-  if (L.small || L.block_m < 64 || x_dtype != MOE_DTYPE_BF16) return MOE_ERR_CONFIG;
-  return (int64_t)L.ctr +
-         (int64_t)sizeof(int32_t) * moe::fused_wait_flag(L.max_padded / L.block_m);
-}
-
-int64_t moe_grouped_ffn_wait_flag_offset(int64_t max_padded, int32_t block_m) {
-  if (max_padded < 0) return MOE_ERR_SHAPE;
-  if (block_m != 64 && block_m != 128 && block_m != 256) return MOE_ERR_CONFIG;
-  return (int64_t)sizeof(int32_t) * moe::fused_wait_flag(max_padded / block_m);
-}
-
-int moe_set_wait_spin_limit(int32_t spins) {
-  if (spins < 0) return MOE_ERR_CONFIG;
-  g_wait_spin_limit.store(spins, std::memory_order_relaxed);
-  return MOE_OK;
 }
 
 size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
@@ -473,7 +374,6 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
   void* y = base + L.y;   // per-pair down-projection rows, in x's dtype
   hipStream_t s = as_stream(stream);
   const int64_t P = T * topk;
-  int32_t* ctr = reinterpret_cast<int32_t*>(base + L.ctr);
 
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
@@ -484,14 +384,8 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
     a.w1 = w1; a.w2 = w2; a.out = out; a.T = T; a.H = H; a.I = I; a.topk = topk;
     return hip_status(moe::launch_small_layer(a, s));
   }
-  // the tile path runs both GEMMs in one persistent launch, whose counters
-  // the alignment zeroes
-  const bool fused = L.block_m >= 64 && x_dtype == MOE_DTYPE_BF16;
-  const int64_t nblk_max = L.max_padded / L.block_m;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
-                             reinterpret_cast<int32_t*>(base + L.hist), s, fused ? ctr : nullptr,
-                             (int)round_up((size_t)moe::fused_counters(nblk_max), 4),
-                             fused ? reinterpret_cast<int32_t*>(base + L.bstart) : nullptr);
+                             reinterpret_cast<int32_t*>(base + L.hist), s);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
   moe::MoeGemmArgs g1{};
@@ -511,16 +405,8 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
   st = check_gemm(g2);
   if (st != MOE_OK) return st;
 
-  if (fused) {
-    moe::FusedArgs f{};
-    f.g1 = g1; f.g2 = g2; f.ctr = ctr; f.nblk_max = (int)nblk_max;
-    f.spin_limit = wait_spin_limit();
-    f.blk_start = reinterpret_cast<const int32_t*>(base + L.bstart);
-    st = hip_status(moe::launch_moe_ffn_fused(f, s));
-  } else {
-    st = enqueue_gemm(g1, s);
-    if (st == MOE_OK) st = enqueue_gemm(g2, s);
-  }
+  st = enqueue_gemm(g1, s);
+  if (st == MOE_OK) st = enqueue_gemm(g2, s);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }

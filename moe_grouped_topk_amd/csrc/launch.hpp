@@ -18,14 +18,9 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
 // The same alignment in two kernels (per-chunk counts, then placement),
 // with a workspace of align_ws_bytes(P, E) bytes for the counts.
 size_t align_ws_bytes(int64_t P, int E);
-// Optional: zero / nzero ints set to 0 on the way (counters of a later
-// launch; zero 16-byte aligned, nzero a multiple of 4); blk_start [E + 1]
-// receives each expert's first block (its padded segment start / B) and,
-// last, the total number of blocks.
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
-                           hipStream_t stream, int32_t* zero = nullptr, int nzero = 0,
-                           int32_t* blk_start = nullptr);
+                           hipStream_t stream);
 
 // Packed expert weights (see moe_pack_weights in moe.h): tiles of 256 rows,
 // K stages of 64 bytes, one 16 KiB block per (expert, tile, stage).
@@ -80,29 +75,6 @@ hipError_t launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t stream);
 // y_dtype / out_dtype: 0 f32, 1 bf16 (out also 2 f16).
 hipError_t launch_topk_reduce(const void* y, int y_dtype, int64_t T, int topk, int64_t H,
                               void* out, int out_dtype, hipStream_t stream);
-
-// Both GEMMs of the layer in one persistent launch: g1 = gate_up (bf16
-// tokens, SiLU epilogue, bf16 h in sorted order), g2 = down (h in sorted
-// order).  ctr: fused_counters(nblk_max) ints, zero at launch;
-// nblk_max = max_padded / block_m; blk_start: [E + 1] first block of each
-// expert, then the number of blocks (from launch_align_ws); E <= 1024.
-struct FusedArgs {
-  MoeGemmArgs g1, g2;
-  int32_t* ctr;
-  const int32_t* blk_start;
-  int nblk_max;
-  int spin_limit;   // polls of a down tile's wait before it gives up and sets the flag
-};
-// Default spin limit of the fused launch's waits: about a second of polling.
-constexpr int kFusedSpinLimit = 1 << 20;
-int fused_counters(int64_t nblk_max);
-// Index of the fused launch's wait-failure flag among its counters.
-int64_t fused_wait_flag(int64_t nblk_max);
-hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream);
-// Counters and blk_start of a fused launch from expert_ids and the total
-// alone (one small kernel): ctr gets fused_counters(nblk_max) zeros.
-hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int block_m, int E,
-                           int64_t nblk_max, int32_t* blk_start, int32_t* ctr, hipStream_t stream);
 
 // The layer after routing in one launch, for small problems
 // (small_layer.hip): one workgroup per token.  H and I multiples of 8.

@@ -18,7 +18,7 @@
 //    gathered tensor never exists in HBM.  Placeholder rows are masked at
 //    the store.
 //  * Main path (bf16 and int8 operands, moe_gemm_dma_kernel,
-//    moe_ffn_fused_kernel, gmm_i8_tile_kernel): BN = 256 weight rows x BM =
+//    gmm_i8_tile_kernel): BN = 256 weight rows x BM =
 //    64/128/256 tokens per tile, loaded with direct-to-LDS loads
 //    (global_load_lds_dwordx4) into an NSTAGE ring of 64-byte K stages, with
 //    no staging registers.  Weights may come pre-packed (moe_pack_weights) so
@@ -26,9 +26,6 @@
 //    workgroups per CU at BM 64/128: one workgroup's MFMAs run while the
 //    other waits for its loads.  Epilogues stage 16-bit output through LDS
 //    and store whole 16-byte pieces of each output row.
-//  * moe_ffn_fused_kernel runs gate_up and down of a layer in one persistent
-//    launch fed by per-XCD work queues; h crosses XCDs through agent-scope
-//    stores and loads (described where the kernel is defined).
 //  * float32 tokens (moe_gemm_tile_kernel): 4 waves in a 2 x 2 grid, global
 //    -> registers (rounded to bf16) -> LDS with 128-byte K stages, LDS rows
 //    padded to 144 bytes so every group of 8 lanes reading 16 bytes hits 8
@@ -246,10 +243,9 @@ __device__ __forceinline__ void mainloop(uint8_t* smem, const Src<C>& src, int64
   }
 }
 
-// threadIdx.x behind an empty asm.  The tile code derives its lane-dependent
-// values from this, so the persistent kernel recomputes them for every tile
-// instead of the compiler hoisting them out of its loop, where they would
-// hold registers across the whole K loop.
+// threadIdx.x behind an empty asm: lane-dependent values derived from it are
+// computed where they are used rather than hoisted by the compiler, where
+// they would hold registers across the whole K loop.
 __device__ __forceinline__ int tile_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
@@ -297,12 +293,6 @@ __device__ __forceinline__ void dma16(uint32_t m0, const void* g) {
 // every packed load), and rows read as half lines are slower with it.
 __device__ __forceinline__ void dma16_nt(uint32_t m0, const void* g) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" :: "v"(g), "{m0}"(m0) : "memory");
-}
-
-// The same load at agent scope (sc1): it sees stores that other XCDs made
-// with agent-scope coherent stores, which their L2 may not have written back.
-__device__ __forceinline__ void dma16_coh(uint32_t m0, const void* g) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" :: "v"(g), "{m0}"(m0) : "memory");
 }
 
 template <int N>
@@ -373,20 +363,11 @@ struct DmaCfg {
 //   (the valid rows of a tile come first); the others are neither read from
 //   LDS nor multiplied.  Every wave still issues its loads and meets every
 //   barrier.
-struct NoHook {
-  __device__ void operator()() const {}
-};
-
-//   COH: token rows are read with agent-scope loads (dma16_coh).
-//   issued_all(): called once the last stage's loads have been issued; a
-//   memory operation it issues is newer than every load the remaining waits
-//   count, so it never holds them up.
-template <class C, int KIND, int NCB, bool COH = false, class Hook = NoHook>
+template <class C, int KIND, int NCB>
 __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                              uint32_t pk_mask, int64_t kbytes,
                                              const int (&wrow)[C::RB], int tcol0,
-                                             typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
-                                             Hook issued_all = Hook()) {
+                                             typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const uint32_t sbase = lds_addr(smem);
   const int chunk_pos = lane & 3;
@@ -403,8 +384,7 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
                               ? (int64_t)kt * kPackBlockBytes
                               : (koff + c * 16 < kbytes ? koff + c * 16 : 0);   // past K: row start
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + (uint32_t)((wave * C::NI + j) * 1024));
-      if (COH && wave * C::NI + j >= C::BN / 16) dma16_coh(m0, rowp[j] + off);
-      else if (C::NT && (pk_mask & kPkStream) && ((pk_mask >> j) & 1u)) dma16_nt(m0, rowp[j] + off);
+      if (C::NT && (pk_mask & kPkStream) && ((pk_mask >> j) & 1u)) dma16_nt(m0, rowp[j] + off);
       else dma16(m0, rowp[j] + off);
     }
   };
@@ -461,7 +441,6 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
   // Stage s goes to LDS buffer s % NSTAGE; all NSTAGE buffers start loading.
   const int pre = nk < C::NSTAGE ? nk : C::NSTAGE;
   for (int kt = 0; kt < pre; ++kt) issue(kt);
-  if (pre == nk) issued_all();
   u32x4_t a0[C::RB], b0[C::CB], a1[C::RB], b1[C::CB];
   publish(0, pre - 1);
   load_frags(0, 0, a0, b0);
@@ -472,10 +451,7 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
       const int last = (kt + C::NSTAGE - 1 < nk - 1) ? kt + C::NSTAGE - 1 : nk - 1;
       publish(kt + 1, last - (kt + 1));
       // every wave has finished reading stage kt: refill its buffer
-      if (kt + C::NSTAGE < nk) {
-        issue(kt + C::NSTAGE);
-        if (kt + C::NSTAGE == nk - 1) issued_all();
-      }
+      if (kt + C::NSTAGE < nk) issue(kt + C::NSTAGE);
       load_frags(kt + 1, 0, a0, b0);
     }
     mfmas(a1, b1);
@@ -484,29 +460,24 @@ __device__ __forceinline__ void mainloop_dma(uint8_t* smem, const uint8_t* const
 
 // Runs the K loop specialised for this wave's number of live column blocks
 // (wave-uniform), so the loop itself has no per-block branches.
-template <class C, int KIND, bool COH = false, class Hook = NoHook>
+template <class C, int KIND>
 __device__ __forceinline__ void mainloop_dma_live(uint8_t* smem, const uint8_t* const (&rowp)[C::NI],
                                                   uint32_t pk_mask, int64_t kbytes,
                                                   const int (&wrow)[C::RB], int tcol0,
                                                   int valid_rows,
-                                                  typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB],
-                                                  Hook issued_all = Hook()) {
+                                                  typename Mma<KIND>::acc_t (&acc)[C::RB][C::CB]) {
   int ncb = (valid_rows - tcol0 + 31) / 32;
   ncb = __builtin_amdgcn_readfirstlane(ncb < 0 ? 0 : (ncb > C::CB ? C::CB : ncb));
   pk_mask = __builtin_amdgcn_readfirstlane(pk_mask);
   if constexpr (C::CB >= 4) {
-    if (ncb == 4) return mainloop_dma<C, KIND, 4, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
-                                                 issued_all);
-    if (ncb == 3) return mainloop_dma<C, KIND, 3, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
-                                                 issued_all);
+    if (ncb == 4) return mainloop_dma<C, KIND, 4>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+    if (ncb == 3) return mainloop_dma<C, KIND, 3>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
   }
   if constexpr (C::CB >= 2) {
-    if (ncb == 2) return mainloop_dma<C, KIND, 2, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
-                                                 issued_all);
+    if (ncb == 2) return mainloop_dma<C, KIND, 2>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
   }
-  if (ncb == 1) return mainloop_dma<C, KIND, 1, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc,
-                                                 issued_all);
-  mainloop_dma<C, KIND, 0, COH>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc, issued_all);
+  if (ncb == 1) return mainloop_dma<C, KIND, 1>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
+  mainloop_dma<C, KIND, 0>(smem, rowp, pk_mask, kbytes, wrow, tcol0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -705,15 +676,12 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
   }
 }
 
-// DRAIN: every thread also waits for all its earlier memory operations (the
-// previous tile's stores) before the barrier, in the shadow of these loads.
-template <int BM, bool DRAIN = false>
+template <int BM>
 __device__ __forceinline__ void load_rowinfo(const MoeGemmArgs& a, const MoeTile& t, int* rowinfo) {
   for (int r = tile_tid(); r < BM; r += blockDim.x) {
     const int p = a.sorted_ids[t.s0 + r];
     rowinfo[r] = (p >= 0 && p < a.num_valid) ? p : -1;
   }
-  if (DRAIN) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
 
@@ -788,19 +756,12 @@ __global__ void __launch_bounds__(C::THREADS) moe_gemm_tile_kernel(MoeGemmArgs a
   moe_epilogue<S::RB, S::CB, EPI, CDT, 0>(a, t, rowinfo, wrow, tcol0, acc);
 }
 
-// 16 bytes with one agent-scope (sc1) store.
-__device__ __forceinline__ void store16_coh(void* dst, const u32x4_t& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(dst), "v"(v) : "memory");
-}
-
 // SiLU epilogue with bf16 output that stages the tile in LDS and writes
-// whole 256-byte row segments (COH: with agent-scope stores, which go
-// through to memory; written straight from the MFMA layout each store
-// instruction would touch 32 rows with 16 bytes each, and agent-scope
-// stores would then move partial lines).  Reuses the K ring, which every
-// wave has finished reading at the first barrier.  wr / ar: this thread's
+// whole 256-byte row segments (written straight from the MFMA layout each
+// store instruction would touch 32 rows with 16 bytes each).  Reuses the K
+// ring, which every wave has finished reading at the first barrier.  wr / ar: this thread's
 // row weight and (int8) row scale (threads < BM), read before the K loop.
-template <class C, bool COH, int KIND>
+template <class C, int KIND>
 __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const MoeTile& t,
                                                      const int* rowinfo,
                                                      const int (&wrow)[C::RB], int tcol0,
@@ -859,8 +820,7 @@ __device__ __forceinline__ void silu_epilogue_staged(const MoeGemmArgs& a, const
     if (p < 0 || p >= a.num_valid || col >= Nout) continue;
     const int64_t crow = (a.c_rows == 0) ? (int64_t)p : t.s0 + r;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
-    if constexpr (COH) store16_coh(Cb + (crow * a.ldc + col) * 2, v);
-    else *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) = v;
+    *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) = v;
   }
 }
 
@@ -930,14 +890,10 @@ __device__ __forceinline__ void plain_epilogue_staged(const MoeGemmArgs& a, cons
 }
 
 // One tile with the direct-to-LDS loop (rowinfo already loaded): operand
-// addresses, K loop (issued_all() once its last loads are issued),
-// after_loop(), epilogue.  COH_A: token rows are read with agent-scope loads;
-// COH_C: the SiLU output is written with agent-scope stores.
-template <class C, int EPI, int CDT, int KIND, bool COH_A = false, bool COH_C = false,
-          class Hook1 = NoHook, class Hook2 = NoHook>
+// addresses, K loop, epilogue.
+template <class C, int EPI, int CDT, int KIND>
 __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile& t, uint8_t* smem,
-                                             const int* rowinfo, Hook1 issued_all = Hook1(),
-                                             Hook2 after_loop = Hook2()) {
+                                             const int* rowinfo) {
   constexpr int BN = C::BN, BM = C::BM;
 
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
@@ -947,11 +903,21 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
   const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)t.e * a.N * wrow_bytes;
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
   const int64_t arow_bytes = a.lda * eb;
-  // packed weights: this tile's blocks; BN == kPackRows and the tile's
-  // columns are the packed tile's (checked by the launcher)
+  // packed weights: a tile of BN rows is SUB = BN / kPackRows consecutive
+  // packed tiles.  The LDS rows keep the plain order (with the SiLU epilogue
+  // the BN/2 gate rows, then the BN/2 up rows), so piece q of the stage
+  // (LDS rows 16q .. 16q+15) comes from packed tile nt * SUB + s, rows pr ..:
+  //   SiLU:  gate row R < BN/2      -> s = R / 128, pr = R % 128;
+  //          up row R >= BN/2       -> s = (R - BN/2) / 128, pr = 128 + (R - BN/2) % 128;
+  //   plain: s = R / 256, pr = R % 256.
+  // A packed tile past the matrix (its rows are never stored) reads the
+  // tile's first packed tile instead.  Row and packed row agree mod 16, so
+  // the pre-swizzled chunk order is the one the LDS rows expect.
+  constexpr int SUB = BN / kPackRows;
+  const int64_t kst = packed_kstages(a.K, eb);
+  const int64_t ptiles = packed_tiles(a.N, EPI);
   const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
-                      ((int64_t)t.e * packed_tiles(a.N, EPI) + t.nt) *
-                          packed_kstages(a.K, eb) * kPackBlockBytes;
+                      ((int64_t)t.e * ptiles + (int64_t)t.nt * SUB) * kst * kPackBlockBytes;
   const uint8_t* rowp[C::NI];
   uint32_t pk_mask = 0;
 #pragma unroll
@@ -960,7 +926,18 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
     const int r = q * 16 + (lane >> 2);
     if (q < BN / 16) {
       if (a.b_packed) {
-        rowp[j] = Bp + q * 1024 + lane * 16;
+        const int R = q * 16;
+        int sub, pr;
+        if (EPI) {
+          const int Rg = R < BN / 2 ? R : R - BN / 2;
+          sub = Rg / (kPackRows / 2);
+          pr = (R < BN / 2 ? 0 : kPackRows / 2) + Rg % (kPackRows / 2);
+        } else {
+          sub = R / kPackRows;
+          pr = R % kPackRows;
+        }
+        if ((int64_t)t.nt * SUB + sub >= ptiles) sub = 0;
+        rowp[j] = Bp + (int64_t)sub * kst * kPackBlockBytes + pr * 64 + lane * 16;
         pk_mask |= 1u << j;
       } else {
         const int64_t g = moe_weight_row<BN, EPI>(a, t.c0, r);
@@ -987,7 +964,6 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
                                 BM * (BN * 2 + 16) + 2 * BM * 4 <= C::kBytes && BM <= C::THREADS;
   constexpr bool kStagedSilu = EPI == 1 && CDT == 1 &&
                                BM * (BN + 16) + 2 * BM * 4 <= C::kBytes && BM <= C::THREADS;
-  static_assert(!COH_C || kStagedSilu, "coherent stores: staged bf16 SiLU output");
   // this thread's row weight and (int8) row scale, read while the K loop runs
   float wr = 1.0f, ar = 1.0f;
   if constexpr (kStagedPlain || kStagedSilu) {
@@ -1000,11 +976,10 @@ __device__ __forceinline__ void run_dma_tile(const MoeGemmArgs& a, const MoeTile
       }
     }
   }
-  mainloop_dma_live<C, KIND, COH_A>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
-                                    live_rows<BM>(rowinfo, a.num_valid), acc, issued_all);
-  after_loop();
+  mainloop_dma_live<C, KIND>(smem, rowp, pk_mask, wrow_bytes, wrow, tcol0,
+                             live_rows<BM>(rowinfo, a.num_valid), acc);
   if constexpr (kStagedSilu) {
-    silu_epilogue_staged<C, COH_C, KIND>(a, t, rowinfo, wrow, tcol0, acc, smem, wr, ar);
+    silu_epilogue_staged<C, KIND>(a, t, rowinfo, wrow, tcol0, acc, smem, wr, ar);
   } else if constexpr (kStagedPlain) {
     plain_epilogue_staged<C, CDT, KIND>(a, t, rowinfo, wrow, tcol0, acc, smem, wr, ar);
   } else {
@@ -1025,229 +1000,6 @@ moe_gemm_dma_kernel(MoeGemmArgs a) {
   if (!moe_tile<C::BN, C::BM, EPI>(a, t, s_win)) return;
   load_rowinfo<C::BM>(a, t, rowinfo);   // one global round trip, then LDS
   run_dma_tile<C, EPI, CDT, KIND>(a, t, smem, rowinfo);
-}
-
-// ---------------------------------------------------------------------------
-// Both GEMMs of the layer in one persistent launch (bf16 tokens, direct-to-LDS
-// tiles).  Each workgroup takes tasks from work queues until all are done:
-//   gate_up tiles (g1, SiLU epilogue): h is written with agent-scope stores;
-//   down tiles (g2): each first waits until every gate_up tile of its token
-//     block has written its part of h, then reads h with agent-scope loads
-//     (h was written by other XCDs, whose L2 may still hold it dirty).
-// The token blocks are cut into one contiguous range per XCD, at expert
-// boundaries where that keeps the ranges balanced (queue_blocks).  Queue q
-// holds the gate_up tiles and, separately, the down tiles of range q, each in
-// expert-local n-tile-major order (fused_tile), so tiles that share a weight
-// slice run together on one XCD and share its L2.  A workgroup drains its own
-// XCD's gate_up queue, then its down queue (whose first blocks finished
-// first), then takes gate_up tiles, then down tiles, from the other queues.
-// Down tiles of a queue are taken only once its gate_up queue is empty: every
-// gate_up tile a down tile waits for has then been taken by a running
-// workgroup that waits for nothing, so every wait ends.  The next claim on
-// the own queue is issued once a tile's last loads are issued and used after
-// its epilogue, and a gate_up tile is counted for its block once its stores
-// have completed, in the shadow of the next tile's row-info loads, so
-// neither costs a round trip of its own.
-// Counters, zeroed before the launch (fused_counters(nblk_max) ints):
-//   [0, 8) gate_up queue heads, [8, 16) down queue heads,
-//   [16, 16 + nblk_max) gate_up tiles finished per token block,
-//   [16 + nblk_max] (fused_wait_flag) set to 1 if a wait ran into its spin
-//   limit (f.spin_limit polls): the down tile then reads h early and the
-//   launch's output is wrong, but every workgroup still ends.
-constexpr int kFusedMaxExperts = 1024;
-
-// Token-block ranges of the queues: qb[q] .. qb[q + 1] for q < kNumXcd.  The
-// cut near q * nblk / 8 moves up to the next expert start when that is at
-// most nblk / 32 blocks away, else it splits the expert.  bs: [E + 1] first
-// block of each expert, then the number of blocks.
-__device__ __forceinline__ void queue_blocks(const int* bs, int E, int* qb) {
-  const int nblk = bs[E];
-  qb[0] = 0;
-  qb[kNumXcd] = nblk;
-  for (int q = 1; q < kNumXcd; ++q) {
-    const int target = (int)((int64_t)q * nblk / kNumXcd);
-    int lo = 0, hi = E;                        // the first e with bs[e] >= target
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (bs[mid] >= target) hi = mid; else lo = mid + 1;
-    }
-    const int slack = nblk / 32 > 1 ? nblk / 32 : 1;
-    qb[q] = bs[lo] - target <= slack ? bs[lo] : target;
-  }
-}
-
-// Tile v of queue range [b0, b1) (ntile tiles per block).  Inside the range
-// the tiles of each expert (clipped to the range) are numbered n-tile-major,
-// so the tiles of one weight slice are neighbours.  Every thread finds the
-// expert by a binary search of its own (no barrier).
-template <int BN, int BM, int EPI>
-__device__ __forceinline__ void fused_tile(const MoeGemmArgs& a, int v, int b0, int b1,
-                                           const int* bs, int E, MoeTile& t) {
-  const int ntile = moe_ntiles<BN, EPI>(a);
-  const int bm = b0 + v / ntile;             // block-major block
-  int lo = 0, hi = E;                        // the last e with bs[e] <= bm (empty experts skipped)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (bs[mid] <= bm) lo = mid; else hi = mid;
-  }
-  const int first = bs[lo] > b0 ? bs[lo] : b0;
-  const int end = bs[lo + 1] < b1 ? bs[lo + 1] : b1;
-  const int local = v - (first - b0) * ntile;
-  t.e = lo;
-  t.nt = local / (end - first);
-  t.blk = first + local % (end - first);
-  t.s0 = (int64_t)t.blk * BM;
-  t.c0 = (int64_t)t.nt * (EPI ? BN / 2 : BN);
-  t.solo = bs[lo + 1] - bs[lo] == 1;
-}
-
-__device__ __forceinline__ int xcc_id() {
-  uint32_t v;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
-  return (int)(v & (kNumXcd - 1));
-}
-
-typedef const __attribute__((address_space(4))) FusedArgs* KArgPtr;
-
-__device__ __forceinline__ KArgPtr opaque(KArgPtr p) {
-  asm volatile("" : "+s"(p));
-  return p;
-}
-
-// Two workgroups of 8 waves per CU need at most 128 VGPRs: ask for
-// OCC * waves / 4 waves per SIMD.
-template <class C, int CDT>
-__global__ void __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256)
-moe_ffn_fused_kernel(FusedArgs f) {
-  const KArgPtr kargs = (KArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int BN = C::BN, BM = C::BM;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int rowinfo[BM];
-  __shared__ int s_task;
-  // thread 0's bookkeeping, kept in LDS rather than in registers of every lane
-  __shared__ int s_own;       // the own queue's phase being drained (2: both empty)
-  __shared__ int s_pre;       // head returned by the claim issued during the last tile
-  __shared__ int s_pending;   // block of the last gate_up tile, not yet counted
-  __shared__ int s_bs[kFusedMaxExperts + 1];
-  __shared__ int s_qb[kNumXcd + 1];
-  const int E = f.g1.E;
-  for (int e = tile_tid(); e <= E; e += C::THREADS) s_bs[e] = f.blk_start[e];
-  __syncthreads();
-  if (tile_tid() == 0) queue_blocks(s_bs, E, s_qb);
-  __syncthreads();
-  const int nt1 = moe_ntiles<BN, 1>(f.g1), nt2 = moe_ntiles<BN, 0>(f.g2);
-  const int xcd = xcc_id();
-  int* const heads = f.ctr;                   // [phase][queue]
-  int* const done = f.ctr + 2 * kNumXcd;
-  const int lane = tile_tid() & 63;
-  // tasks of queue q in phase p
-  auto count = [&](int p, int q) { return (s_qb[q + 1] - s_qb[q]) * (p ? nt2 : nt1); };
-  if (tile_tid() == 0) { s_own = 0; s_pre = -1; s_pending = -1; }
-  auto count_pending = [&]() {
-    if (tile_tid() == 0 && s_pending >= 0) {
-      __hip_atomic_fetch_add(done + s_pending, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_pending = -1;
-    }
-  };
-
-  for (;;) {
-    if (tile_tid() < 64) {   // wave 0 claims the next task: v | q << 24 | p << 27
-      int task = -1;
-      if (lane == 0) {
-        // the claim issued during the last tile, then the own queue's phases
-        int own = s_own, pre = s_pre;
-        while (own < 2) {
-          const int v = pre >= 0 ? pre
-                                 : __hip_atomic_fetch_add(heads + kNumXcd * own + xcd, 1,
-                                                          __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-          pre = -1;
-          if (v < count(own, xcd)) { task = v | (xcd << 24) | (own << 27); break; }
-          ++own;
-        }
-        s_own = own;
-        s_pre = -1;
-      }
-      task = __shfl(task, 0, 64);
-      while (task < 0) {
-        // steal: read all heads at once; gate_up tiles of any queue first, then
-        // down tiles of queues whose gate_up tiles have all been taken
-        const int q = lane & (kNumXcd - 1), p = (lane >> 3) & 1;
-        const int head = lane < 2 * kNumXcd
-                             ? __hip_atomic_load(heads + kNumXcd * p + q, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : 0;
-        const bool left = lane < 2 * kNumXcd && head < count(p, q);
-        const uint32_t m = (uint32_t)__ballot(left);
-        const uint32_t m0 = m & 0xffu, m1 = (m >> 8) & ~m0 & 0xffu;
-        const uint32_t mm = m0 ? m0 : m1;
-        if (mm == 0) break;
-        const uint32_t rot = ((mm >> xcd) | (mm << (kNumXcd - xcd))) & ((1u << kNumXcd) - 1);
-        const int qc = (xcd + __builtin_ctz(rot)) & (kNumXcd - 1), pc = m0 ? 0 : 1;
-        int v = 0;
-        if (lane == 0)
-          v = __hip_atomic_fetch_add(heads + kNumXcd * pc + qc, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        v = __shfl(v, 0, 64);
-        if (v < count(pc, qc)) task = v | (qc << 24) | (pc << 27);
-      }
-      if (lane == 0) s_task = task;
-    }
-    __syncthreads();
-    const int task = __builtin_amdgcn_readfirstlane(s_task);
-    if (task < 0) {
-      // once every wave's stores have completed, count the last gate_up tile
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      count_pending();
-      return;
-    }
-    const int phase = (task >> 27) & 1, tq = (task >> 24) & (kNumXcd - 1), v = task & 0xffffff;
-    const int b0 = s_qb[tq], b1 = s_qb[tq + 1];
-    // the next claim on the own queue goes out once this tile's last loads
-    // are issued; its latency hides behind the end of the K loop
-    auto claim_ahead = [&]() {
-      if (tile_tid() == 0 && s_own < 2)
-        s_pre = __hip_atomic_fetch_add(heads + kNumXcd * s_own + xcd, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // The GEMM arguments are re-read from the kernel-argument segment for
-    // every tile (the empty asm hides that they never change): kept live
-    // across the loop they would not fit the scalar registers.
-    const KArgPtr kp = opaque(kargs);
-    MoeTile t;
-    if (phase == 0) {
-      const MoeGemmArgs g1 = *(const MoeGemmArgs*)&kp->g1;
-      fused_tile<BN, BM, 1>(g1, v, b0, b1, s_bs, E, t);
-      // the last tile's stores complete in the shadow of the row-info loads;
-      // then the last gate_up tile is counted for its block
-      load_rowinfo<BM, true>(g1, t, rowinfo);
-      count_pending();
-      run_dma_tile<C, 1, 1, 0, false, true>(g1, t, smem, rowinfo, claim_ahead);
-      if (tile_tid() == 0) s_pending = t.blk;
-    } else {
-      const MoeGemmArgs g2 = *(const MoeGemmArgs*)&kp->g2;
-      fused_tile<BN, BM, 0>(g2, v, b0, b1, s_bs, E, t);
-      // the block's count is read in the same round trip as the row info
-      int cnt = nt1;
-      if (tile_tid() == 0)
-        cnt = __hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      load_rowinfo<BM, true>(g2, t, rowinfo);
-      count_pending();
-      if (tile_tid() == 0 && cnt < nt1) {
-        int spins = 0;
-        while (__hip_atomic_load(done + t.blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt1) {
-          __builtin_amdgcn_s_sleep(8);
-          if (++spins >= f.spin_limit) {
-            __hip_atomic_store(done + f.nblk_max, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      run_dma_tile<C, 0, CDT, 0, true, false>(g2, t, smem, rowinfo, claim_ahead);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1480,6 +1232,9 @@ template <int BM> struct TileFor;
 #define MOE_T128_WN 4
 #define MOE_T128_WM 2
 #endif
+#ifndef MOE_T128_BN
+#define MOE_T128_BN 256
+#endif
 // 256 x 64 tiles (decode and small experts): 4 waves, a 3-stage ring (60 KiB)
 // and two workgroups per CU: more weight bytes in flight per CU than one
 // workgroup with a 4-stage ring (measured 1-4% faster on the decode layers).
@@ -1494,7 +1249,7 @@ template <> struct TileFor<64> {
   typedef Cfg<256, 64, 2, 2, MOE_TILE_NBUF> Regs;
 };
 template <> struct TileFor<128> {
-  typedef DmaCfg<256, 128, MOE_T128_NSTAGE, MOE_T128_WN, MOE_T128_WM, MOE_T128_OCC> Dma;
+  typedef DmaCfg<MOE_T128_BN, 128, MOE_T128_NSTAGE, MOE_T128_WN, MOE_T128_WM, MOE_T128_OCC> Dma;
   typedef Cfg<256, 128, 2, 2, MOE_TILE_NBUF> Regs;
 };
 template <> struct TileFor<256> {
@@ -1504,7 +1259,7 @@ template <> struct TileFor<256> {
 template <int BM>
 hipError_t launch_tile_bm(const MoeGemmArgs& a, hipStream_t s) {
   typedef typename TileFor<BM>::Dma D;
-  static_assert(D::BN == kPackRows, "packed weights are cut into tiles of the kernel's BN rows");
+  static_assert(D::BN % kPackRows == 0, "a tile is a whole number of packed tiles");
   if (a.b_packed && a.a_dtype == 0) return hipErrorInvalidValue;   // rejected by the ABI layer
   if (a.a_dtype == 3) {   // int8 tokens and weights; f32 or bf16 output
     if (a.c_dtype == 0)
@@ -1530,109 +1285,6 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
     case 64: return launch_tile_bm<64>(a, stream);
     case 128: return launch_tile_bm<128>(a, stream);
     default: return launch_tile_bm<256>(a, stream);
-  }
-}
-
-int fused_counters(int64_t nblk_max) { return (int)(2 * kNumXcd + nblk_max + 1); }
-int64_t fused_wait_flag(int64_t nblk_max) { return 2 * kNumXcd + nblk_max; }
-
-// Set-up of a fused launch from the alignment outputs alone: zero the
-// counters and find each expert's first block.  Blocks are in ascending
-// expert order, so a suffix minimum over the experts' first blocks gives an
-// expert without blocks the start of the next expert that has some (what the
-// fused kernel's binary search expects); bs[E] = the number of blocks.
-constexpr int kPrepThreads = 1024;
-static_assert(kPrepThreads >= kFusedMaxExperts, "one thread per expert");
-
-__global__ void __launch_bounds__(kPrepThreads)
-ffn_prep_kernel(const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ total, int B,
-                int E, int nblk_max, int32_t* __restrict__ bs, int32_t* __restrict__ ctr,
-                int nctr) {
-  __shared__ int start[kFusedMaxExperts];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nctr; i += kPrepThreads) ctr[i] = 0;
-  int nblk = *total / B;
-  nblk = nblk < nblk_max ? nblk : nblk_max;
-  if (tid < E) start[tid] = nblk;
-  __syncthreads();
-  for (int b = tid; b < nblk; b += kPrepThreads) {
-    const int e = expert_ids[b];
-    if (e >= 0 && e < E && (b == 0 || expert_ids[b - 1] != e)) start[e] = b;
-  }
-  __syncthreads();
-  for (int off = 1; off < E; off <<= 1) {
-    const int v = (tid < E && tid + off < E) ? min(start[tid], start[tid + off]) : 0;
-    __syncthreads();
-    if (tid < E && tid + off < E) start[tid] = v;
-    __syncthreads();
-  }
-  if (tid < E) bs[tid] = start[tid];
-  if (tid == 0) bs[E] = nblk;
-}
-
-hipError_t launch_ffn_prep(const int32_t* expert_ids, const int32_t* total, int block_m, int E,
-                           int64_t nblk_max, int32_t* blk_start, int32_t* ctr, hipStream_t stream) {
-  if (E < 1 || E > kFusedMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ffn_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_ids, total,
-                     block_m, E, (int)nblk_max, blk_start, ctr, fused_counters(nblk_max));
-  return hipGetLastError();
-}
-
-namespace {
-
-// CUs of the current device, queried once per device (calls from several
-// host threads may race to fill the cache; they store the same value).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-template <int BM, int CDT>
-hipError_t launch_fused_t(const FusedArgs& f, hipStream_t s) {
-  typedef typename TileFor<BM>::Dma C;
-  auto k = moe_ffn_fused_kernel<C, CDT>;
-  constexpr size_t lds = C::kBytes;
-  const hipError_t st = ensure_lds(k, lds);
-  if (st != hipSuccess) return st;
-  // one workgroup per slot: more would only find the queues empty
-  int64_t tasks = (f.g1.max_padded / BM) *
-                  ((f.g1.N / 2 + C::BN / 2 - 1) / (C::BN / 2) + (f.g2.N + C::BN - 1) / C::BN);
-  int64_t grid = (int64_t)device_cus() * C::OCC;
-  if (tasks < grid) grid = tasks;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(C::THREADS), lds, s, f);
-  return hipGetLastError();
-}
-
-template <int BM>
-hipError_t launch_fused_bm(const FusedArgs& f, hipStream_t s) {
-  switch (f.g2.c_dtype) {
-    case 0: return launch_fused_t<BM, 0>(f, s);
-    case 1: return launch_fused_t<BM, 1>(f, s);
-    default: return launch_fused_t<BM, 2>(f, s);
-  }
-}
-
-}  // namespace
-
-hipError_t launch_moe_ffn_fused(const FusedArgs& f, hipStream_t stream) {
-  if (f.g1.a_dtype != 1 || f.g2.a_dtype != 1 || f.g1.c_dtype != 1 || !f.g1.epilogue ||
-      f.g1.topk_weights || f.g2.epilogue || f.g1.block_m != f.g2.block_m || !f.ctr ||
-      !f.blk_start || f.g1.E > kFusedMaxExperts)
-    return hipErrorInvalidValue;   // the ABI layer only builds valid pairs
-  switch (f.g1.block_m) {
-    case 64: return launch_fused_bm<64>(f, stream);
-    case 128: return launch_fused_bm<128>(f, stream);
-    case 256: return launch_fused_bm<256>(f, stream);
-    default: return hipErrorInvalidValue;
   }
 }
 

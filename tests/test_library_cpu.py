@@ -169,38 +169,6 @@ def test_gemm_validation(mod):
     assert call(bl=1, a_dtype=0) == d["MOE_ERR_CONFIG"]          # packed needs bf16 A
 
 
-def test_grouped_ffn_workspace_and_validation(mod):
-    L, d = mod.lib, _defines()
-    f = ctypes.c_void_p(256)
-    # counters (16 + blocks + 1 ints, padded to 256 bytes), then E + 1 expert starts
-    assert mod.moe_grouped_ffn_workspace_size(49024, 128, 128) == 1792 + 4 * 129
-    assert mod.moe_grouped_ffn_workspace_size(512, 8, 32) == 0          # not a tile block size
-    assert mod.moe_grouped_ffn_workspace_size(512, 2048, 64) == 0       # too many experts
-    ws_need = mod.moe_grouped_ffn_workspace_size(512, 8, 64)
-    base = dict(x=f, T=64, H=128, topk=2, w1=f, w2=f, wl=0, E=8, I=256, s=f, e=f, tot=f,
-                maxp=512, bm=64, w=f, h=f, y=f, yd=1, ws=f, wsb=ws_need)
-
-    def call(**kw):
-        a = dict(base, **kw)
-        return L.moe_grouped_ffn(a["x"], a["T"], a["H"], a["topk"], a["w1"], a["w2"], a["wl"],
-                                 a["E"], a["I"], a["s"], a["e"], a["tot"], a["maxp"], a["bm"],
-                                 a["w"], a["h"], a["y"], a["yd"], a["ws"], a["wsb"], None)
-    assert call(x=None) == d["MOE_ERR_NULL"]
-    assert call(w=None) == d["MOE_ERR_NULL"]
-    assert call(bm=32) == d["MOE_ERR_CONFIG"]          # tile block sizes only
-    assert call(wl=2) == d["MOE_ERR_CONFIG"]
-    assert call(yd=3) == d["MOE_ERR_DTYPE"]
-    assert call(H=100) == d["MOE_ERR_SHAPE"]
-    assert call(I=40) == d["MOE_ERR_SHAPE"]
-    assert call(maxp=500) == d["MOE_ERR_SHAPE"]        # not a multiple of block_m
-    assert call(E=2048) == d["MOE_ERR_SHAPE"]
-    assert call(ws=None) == d["MOE_ERR_WORKSPACE"]
-    assert call(wsb=ws_need - 4) == d["MOE_ERR_WORKSPACE"]
-    assert call(ws=ctypes.c_void_p(512 + 64)) == d["MOE_ERR_WORKSPACE"]   # alignment
-    assert call(h=ctypes.c_void_p(264)) == d["MOE_ERR_SHAPE"]             # misaligned h
-    assert call(T=0) == 0                                                  # no-op
-
-
 def test_forward_validation(mod):
     L, d = mod.lib, _defines()
     f = ctypes.c_void_p(256)
@@ -349,39 +317,3 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
-
-
-def test_wait_flag_offsets(mod):
-    """The persistent launch's wait flag lies inside the caller's workspace,
-    4-byte aligned, past the launch's queue heads and per-block counters; the
-    calls reject layers that run no persistent launch."""
-    d = _defines()
-    # moe_grouped_ffn: counters first (16 queue heads, one count per block), then the flag
-    assert mod.moe_grouped_ffn_wait_flag_offset(1024, 128) == 4 * (16 + 8)
-    assert mod.moe_grouped_ffn_wait_flag_offset(0, 64) == 4 * 16
-    for bm in (64, 128, 256):
-        mp = mod.moe_align_max_padded(32768, 128, bm)
-        off = mod.moe_grouped_ffn_wait_flag_offset(mp, bm)
-        assert off % 4 == 0 and off + 4 <= mod.moe_grouped_ffn_workspace_size(mp, 128, bm)
-    assert mod.lib.moe_grouped_ffn_wait_flag_offset(1024, 32) == d["MOE_ERR_CONFIG"]
-    assert mod.lib.moe_grouped_ffn_wait_flag_offset(-1, 64) == d["MOE_ERR_SHAPE"]
-    # moe_forward: the prefill and decode shapes with bf16 x, both layouts
-    for (T, H, I, E, K) in [(4096, 2048, 768, 128, 8), (16, 7168, 2048, 256, 8)]:
-        for bm in (0, 64, 128, 256):
-            for weights in ("plain", "packed"):
-                off = mod.moe_forward_wait_flag_offset(T, H, I, E, K, bm, "bf16", weights)
-                assert off % 4 == 0 and 0 < off
-                assert off + 4 <= mod.moe_forward_workspace_size(T, H, I, E, K, bm)
-    with pytest.raises(mod.MoeError):      # f32 x: two separate GEMM launches
-        mod.moe_forward_wait_flag_offset(4096, 2048, 768, 128, 8, 0, "f32")
-    with pytest.raises(mod.MoeError):      # weight-streaming block sizes
-        mod.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 16)
-    with pytest.raises(mod.MoeError):      # the tiny layer runs as one small launch
-        mod.moe_forward_wait_flag_offset(64, 128, 256, 8, 2, 0, "bf16", "plain")
-    assert mod.moe_forward_wait_flag_offset(64, 128, 256, 8, 2, 64, "bf16", "plain") > 0
-    assert mod.lib.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 48, 1, 0) == \
-        d["MOE_ERR_CONFIG"]
-    assert mod.lib.moe_forward_wait_flag_offset(16, 7168, 2048, 256, 8, 0, 7, 0) == \
-        d["MOE_ERR_DTYPE"]
-    assert mod.lib.moe_set_wait_spin_limit(-1) == d["MOE_ERR_CONFIG"]
-    assert mod.lib.moe_set_wait_spin_limit(0) == 0

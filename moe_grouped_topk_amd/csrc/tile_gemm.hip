@@ -35,8 +35,6 @@
 //    contiguous run of tiles, so an expert's weight slab and its gathered
 //    rows are shared in one XCD's L2.
 
-#include <atomic>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1014,28 +1012,18 @@ moe_gemm_dma_kernel(MoeGemmArgs a) {
 typedef DmaCfg<256, MOE_GMM_BM, MOE_GMM_NSTAGE, MOE_GMM_WN, MOE_GMM_WM, MOE_GMM_OCC, true> GmmCfg;
 static_assert(GmmCfg::BN == kPackRows, "packed int8 weights are cut into tiles of BN rows");
 
-// OCC workgroups per CU: ask for OCC * waves / 4 waves per SIMD.
-__global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC * GmmCfg::THREADS / 256)
-gmm_i8_tile_kernel(GmmI8Args a) {
-  typedef GmmCfg C;
-  typedef C S;
-  constexpr int BN = C::BN, BM = C::BM, NT = C::THREADS;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int tprefix[kMaxGmmExperts + 1];   // m-tiles before expert e
-  __shared__ int scan_buf[NT];
-  __shared__ int rowinfo[BM];
+typedef i32x16_t GmmAcc[GmmCfg::RB][GmmCfg::CB];
 
-  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % C::WN, wm = wave / C::WN;
-  const int E = a.E;
-  const int M = (int)a.M;
-  const int ntile = (int)((a.N + BN - 1) / BN);
+// m-tiles before each expert, tprefix[e] (e <= E), from the clamped offsets.
+// Every thread takes part (barriers); scan_buf: THREADS ints of LDS.
+__device__ __forceinline__ int gmm_row_of(const GmmI8Args& a, int e) {
+  const int v = a.offsets[e], M = (int)a.M;
+  return v < 0 ? 0 : (v > M ? M : v);
+}
 
-  // m-tile counts per expert from the (clamped) offsets, then a scan.
-  auto lo_of = [&](int e) {
-    int v = a.offsets[e];
-    return v < 0 ? 0 : (v > M ? M : v);
-  };
+__device__ __forceinline__ void gmm_tile_prefix(const GmmI8Args& a, int* tprefix, int* scan_buf) {
+  constexpr int BM = GmmCfg::BM, NT = GmmCfg::THREADS;
+  const int tid = tile_tid(), E = a.E;
   const int per = (E + NT - 1) / NT;   // <= 4
   int cnt[4] = {0, 0, 0, 0};
   int local = 0;
@@ -1043,8 +1031,8 @@ gmm_i8_tile_kernel(GmmI8Args a) {
   for (int j = 0; j < 4; ++j) {
     const int e = tid * per + j;
     if (j < per && e < E) {
-      const int lo = lo_of(e);
-      int hi = lo_of(e + 1);
+      const int lo = gmm_row_of(a, e);
+      int hi = gmm_row_of(a, e + 1);
       hi = hi < lo ? lo : hi;
       cnt[j] = (hi - lo + BM - 1) / BM;
       local += cnt[j];
@@ -1058,46 +1046,64 @@ gmm_i8_tile_kernel(GmmI8Args a) {
     scan_buf[tid] += add;
     __syncthreads();
   }
-  {
-    int run = scan_buf[tid] - local;
+  int run = scan_buf[tid] - local;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid * per + j;
-      if (j < per && e < E) {
-        tprefix[e] = run;
-        run += cnt[j];
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per + j;
+    if (j < per && e < E) {
+      tprefix[e] = run;
+      run += cnt[j];
     }
-    if (tid == NT - 1) tprefix[E] = scan_buf[tid];
   }
+  if (tid == NT - 1) tprefix[E] = scan_buf[tid];
   __syncthreads();
-  const int total_mt = tprefix[E];
-  const int live = total_mt * ntile;
-  if ((int)blockIdx.x >= live) return;
-  const int L = xcd_remap((int)blockIdx.x, live);
-  // Expert: largest e with tprefix[e] * ntile <= L.
-  int lo = 0, hi = E;   // invariant: tprefix[lo]*ntile <= L < tprefix[hi]*ntile
+}
+
+// Tile L of the GMM (0 <= L < tprefix[E] * ntile): its expert, and inside
+// the expert the m-tiles of one n-tile adjacent (they share the weight slice).
+struct GmmTile {
+  int e, mcount, nt, mt, row_lo, row_hi, row0;
+  int64_t n0;
+};
+
+__device__ __forceinline__ GmmTile gmm_tile_at(const GmmI8Args& a, const int* tprefix, int ntile,
+                                               int L) {
+  GmmTile t;
+  int lo = 0, hi = a.E;   // the largest e with tprefix[e] * ntile <= L
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (tprefix[mid] * ntile <= L) lo = mid; else hi = mid;
   }
-  const int e = lo;
-  const int mcount = tprefix[e + 1] - tprefix[e];
-  const int lin = L - tprefix[e] * ntile;
-  const int nt = lin / mcount, mt = lin % mcount;   // m-tiles of one n-tile adjacent
-  const int row_lo = lo_of(e);
-  int row_hi = lo_of(e + 1);
-  row_hi = row_hi < row_lo ? row_lo : row_hi;
-  const int row0 = row_lo + mt * BM;
-  const int64_t n0 = (int64_t)nt * BN;
+  t.e = lo;
+  t.mcount = tprefix[lo + 1] - tprefix[lo];
+  const int lin = L - tprefix[lo] * ntile;
+  t.nt = lin / t.mcount;
+  t.mt = lin % t.mcount;
+  t.row_lo = gmm_row_of(a, lo);
+  const int rh = gmm_row_of(a, lo + 1);
+  t.row_hi = rh < t.row_lo ? t.row_lo : rh;
+  t.row0 = t.row_lo + t.mt * GmmCfg::BM;
+  t.n0 = (int64_t)t.nt * GmmCfg::BN;
+  return t;
+}
 
-  if (tid < BM) rowinfo[tid] = (row0 + tid < row_hi) ? row0 + tid : -1;
+// K stages [k0, k1) of tile t into acc (which it does not clear); kst =
+// stages of the whole K.  Writes rowinfo (barrier inside); *ar: this
+// thread's row scale (threads < BM), read while the loop runs.
+__device__ __forceinline__ void gmm_tile_mainloop(const GmmI8Args& a, const GmmTile& t, int k0,
+                                                  int k1, int kst, uint8_t* smem, int* rowinfo,
+                                                  GmmAcc& acc, float* ar) {
+  typedef GmmCfg C;
+  constexpr int BN = C::BN, BM = C::BM;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  if (tid < BM) rowinfo[tid] = (t.row0 + tid < t.row_hi) ? t.row0 + tid : -1;
   __syncthreads();
-
-  const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W) + (int64_t)e * a.N * a.K;
-  // packed weights: this n-tile's blocks (tiles of kPackRows == BN rows)
+  const int64_t kshift = (int64_t)k0 * C::ROWB;        // bytes of K before stage k0
+  const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W) + (int64_t)t.e * a.N * a.K + kshift;
+  // packed weights: this n-tile's blocks (tiles of kPackRows == BN rows), from stage k0
   const uint8_t* Wp = reinterpret_cast<const uint8_t*>(a.W) +
-                      ((int64_t)e * packed_tiles(a.N, 0) + nt) * packed_kstages(a.K, 1) *
+                      (((int64_t)t.e * packed_tiles(a.N, 0) + t.nt) * packed_kstages(a.K, 1) + k0) *
                           kPackBlockBytes;
   const uint8_t* rowp[C::NI];
   uint32_t pk_mask = 0;
@@ -1109,78 +1115,120 @@ gmm_i8_tile_kernel(GmmI8Args a) {
       rowp[j] = Wp + q * 1024 + lane * 16;
       pk_mask |= 1u << j;
     } else if (r < BN) {
-      const int64_t n = n0 + r;
+      const int64_t n = t.n0 + r;
       rowp[j] = Wb + (n < a.N ? n : 0) * a.K;
     } else {
       const int m = rowinfo[r - BN];
-      rowp[j] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)(m < 0 ? row_lo : m) * a.K;
+      rowp[j] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)(m < 0 ? t.row_lo : m) * a.K +
+                kshift;
     }
   }
-  if (mcount == 1 && pk_mask) pk_mask |= kPkStream;   // the only tile of this weight slice
-
+  // the only reader of this weight slice streams it with the non-temporal hint
+  if (t.mcount == 1 && k0 == 0 && k1 == kst && pk_mask) pk_mask |= kPkStream;
   constexpr int WROWS = BN / C::WN;
-  int wrow[S::RB];
+  int wrow[C::RB];
 #pragma unroll
-  for (int rb = 0; rb < S::RB; ++rb) wrow[rb] = wn * WROWS + rb * 32;
+  for (int rb = 0; rb < C::RB; ++rb) wrow[rb] = wn * WROWS + rb * 32;
   const int tcol0 = wm * (BM / C::WM);
+  const int live_m = t.row_hi - t.row0 < BM ? t.row_hi - t.row0 : BM;
+  if (tid < BM && rowinfo[tid] >= 0) *ar = a.sx[rowinfo[tid]];
+  // the last stage of K may be partial; earlier cut points are whole stages
+  const int64_t kbytes = k1 == kst ? a.K - kshift : (int64_t)(k1 - k0) * C::ROWB;
+  mainloop_dma_live<C, 1>(smem, rowp, pk_mask, kbytes, wrow, tcol0, live_m, acc);
+}
 
-  i32x16_t acc[S::RB][S::CB];
-#pragma unroll
-  for (int rb = 0; rb < S::RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < S::CB; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
-
-  const int live_m = row_hi - row0 < BM ? row_hi - row0 : BM;
-  // this thread's row scale (threads < BM), read while the K loop runs
-  float ar = 0.0f;
-  if (tid < BM && rowinfo[tid] >= 0) ar = a.sx[rowinfo[tid]];
-  mainloop_dma_live<C, 1>(smem, rowp, pk_mask, a.K, wrow, tcol0, live_m, acc);
-
-  // Epilogue through LDS: the fp16 tile in [token row][column] order in the
-  // drained K ring, then each row's BN columns as whole 16-byte pieces
-  // (straight from the MFMA layout each store would cover 32 rows x 8 bytes).
+// Epilogue through LDS: the fp16 tile in [token row][column] order in the
+// drained K ring, then each row's BN columns as whole 16-byte pieces
+// (straight from the MFMA layout each store would cover 32 rows x 8 bytes).
+// When the whole tile does not fit the ring it goes in passes of one wave
+// row (BM / WM token rows) each.
+__device__ __forceinline__ void gmm_tile_epilogue(const GmmI8Args& a, const GmmTile& t,
+                                                  const int* rowinfo, const GmmAcc& acc,
+                                                  uint8_t* smem, float ar) {
+  typedef GmmCfg C;
+  constexpr int BN = C::BN, BM = C::BM, NT = C::THREADS;
   constexpr int PITCH = BN * 2 + 16, LPR = BN * 2 / 16, RPP = NT / LPR;
-  static_assert(BM * PITCH + BM * 4 <= C::kBytes && NT % LPR == 0 && BM % RPP == 0 && BM <= NT,
+  constexpr bool kWhole = BM * PITCH + BM * 4 <= C::kBytes;
+  constexpr int PR = kWhole ? BM : BM / C::WM;   // rows staged per pass
+  static_assert(PR * PITCH + BM * 4 <= C::kBytes && NT % LPR == 0 && PR % RPP == 0 && BM <= NT,
                 "staged GMM epilogue shape");
-  float* s_a = reinterpret_cast<float*>(smem + BM * PITCH);
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  constexpr int WROWS = BN / C::WN;
+  const int tcol0 = wm * (BM / C::WM);
+  float* s_a = reinterpret_cast<float*>(smem + PR * PITCH);
   __syncthreads();                            // every wave has left the K ring
   if (tid < BM) s_a[tid] = ar;
   __syncthreads();
   const int rsub = 4 * (lane >> 5);
-  const float* swe = a.sw + (int64_t)e * a.N;
-#pragma unroll
-  for (int cb = 0; cb < S::CB; ++cb) {
-    const int trow = tcol0 + cb * 32 + (lane & 31);
-    const float sx = s_a[trow];
-    uint8_t* dst = smem + trow * PITCH;
-#pragma unroll
-    for (int rb = 0; rb < S::RB; ++rb) {
-      const i32x16_t v = acc[rb][cb];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = wrow[rb] + 8 * g + rsub;
-        const int64_t n = n0 + col;
-        const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(swe + (n < a.N ? n : 0));   // past N: never stored
-        *reinterpret_cast<uint2*>(dst + col * 2) =
-            make_uint2(pack_f16x2((float)v[4 * g] * sx * sw[0], (float)v[4 * g + 1] * sx * sw[1]),
-                       pack_f16x2((float)v[4 * g + 2] * sx * sw[2], (float)v[4 * g + 3] * sx * sw[3]));
-      }
-    }
-  }
-  __syncthreads();
+  const float* swe = a.sw + (int64_t)t.e * a.N;
   uint8_t* Yb = reinterpret_cast<uint8_t*>(a.Y);
   const int ch = tid % LPR;
-  const int64_t col = n0 + ch * 8;            // 8 columns; N is a multiple of 16
+  const int64_t col = t.n0 + ch * 8;          // 8 columns; N is a multiple of 16
 #pragma unroll
-  for (int r0 = 0; r0 < BM; r0 += RPP) {
-    const int r = r0 + tid / LPR;
-    const int m = rowinfo[r];
-    if (m < 0 || col >= a.N) continue;
-    *reinterpret_cast<u32x4_t*>(Yb + ((int64_t)m * a.N + col) * 2) =
-        *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+  for (int p = 0; p < BM / PR; ++p) {
+    if (kWhole || wm == p) {                  // this pass's rows: [p * PR, p * PR + PR)
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb) {
+        const int trow = tcol0 + cb * 32 + (lane & 31);
+        const float sx = s_a[trow];
+        uint8_t* dst = smem + (trow - p * PR) * PITCH;
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+          const i32x16_t v = acc[rb][cb];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wn * WROWS + rb * 32 + 8 * g + rsub;
+            const int64_t n = t.n0 + c;
+            const f32x4_t sw = *reinterpret_cast<const f32x4_t*>(swe + (n < a.N ? n : 0));   // past N: never stored
+            *reinterpret_cast<uint2*>(dst + c * 2) = make_uint2(
+                pack_f16x2((float)v[4 * g] * sx * sw[0], (float)v[4 * g + 1] * sx * sw[1]),
+                pack_f16x2((float)v[4 * g + 2] * sx * sw[2], (float)v[4 * g + 3] * sx * sw[3]));
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r0 = 0; r0 < PR; r0 += RPP) {
+      const int r = r0 + tid / LPR;
+      const int m = rowinfo[p * PR + r];
+      if (m < 0 || col >= a.N) continue;
+      *reinterpret_cast<u32x4_t*>(Yb + ((int64_t)m * a.N + col) * 2) =
+          *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+    }
+    if (p + 1 < BM / PR) __syncthreads();     // the next pass overwrites the staged rows
   }
+}
+
+__device__ __forceinline__ void gmm_acc_clear(GmmAcc& acc) {
+#pragma unroll
+  for (int rb = 0; rb < GmmCfg::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < GmmCfg::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+}
+
+// One tile per workgroup (a grid of every possible tile; the surplus exits).
+// OCC workgroups per CU: ask for OCC * waves / 4 waves per SIMD.
+__global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC * GmmCfg::THREADS / 256)
+gmm_i8_tile_kernel(GmmI8Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int tprefix[kMaxGmmExperts + 1];   // m-tiles before expert e
+  __shared__ int scan_buf[GmmCfg::THREADS];
+  __shared__ int rowinfo[GmmCfg::BM];
+  gmm_tile_prefix(a, tprefix, scan_buf);
+  const int ntile = (int)((a.N + GmmCfg::BN - 1) / GmmCfg::BN);
+  const int live = tprefix[a.E] * ntile;
+  if ((int)blockIdx.x >= live) return;
+  const GmmTile t = gmm_tile_at(a, tprefix, ntile, xcd_remap((int)blockIdx.x, live));
+  const int kst = (int)((a.K + GmmCfg::ROWB - 1) / GmmCfg::ROWB);
+  GmmAcc acc;
+  gmm_acc_clear(acc);
+  float ar = 0.0f;
+  gmm_tile_mainloop(a, t, 0, kst, kst, smem, rowinfo, acc, &ar);
+  gmm_tile_epilogue(a, t, rowinfo, acc, smem, ar);
 }
 
 // Dynamic LDS beyond 64 KiB has to be requested per kernel.

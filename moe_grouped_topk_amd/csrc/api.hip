@@ -519,13 +519,14 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   st = check_gemm(g2);
   if (st != MOE_OK) return st;
 
+  // routing also quantises each token's x row as it loads it (one wave per
+  // token for both)
+  moe::RouteExtra rx{x, x_dtype == MOE_DTYPE_BF16 ? 1 : 0, H, xq, sx, nullptr, 0};
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
-                                     renormalize ? 1 : 0, routed_scaling_factor, w, ids, s);
+                                     renormalize ? 1 : 0, routed_scaling_factor, w, ids, s, &rx);
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
                              reinterpret_cast<int32_t*>(base + L.hist), s);
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_quantize_rows(x, x_dtype, T, H, H, nullptr, nullptr, 0, xq, sx, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
   st = enqueue_gemm(g1, s);
   if (st != MOE_OK) return st;

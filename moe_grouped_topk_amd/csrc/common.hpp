@@ -106,6 +106,49 @@ __device__ __forceinline__ void store4(void* dst, float a, float b, float c, flo
   }
 }
 
+// Per-row symmetric int8 quantisation (low-precision GMM article, section
+// 3.2): scale = max|row| / 127 (1 for an all-zero row), codes
+// round-half-to-even(x / scale) clamped to +-127, in float32 with IEEE
+// division, so the codes are a pure function of the row's float32 values
+// whichever kernel computes them.
+//   load8: eight consecutive row values (XDT 1: bf16, 16-byte load;
+//   0: f32, two 16-byte loads) as float32.
+template <int XDT>
+__device__ __forceinline__ void load8(const void* row, int64_t i, float (&v)[8]) {
+  if constexpr (XDT == 1) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(row) + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(u[k] << 16);
+      v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+  } else {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(row) + i);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(row) + i + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[4 + k] = b[k];
+    }
+  }
+}
+
+__device__ __forceinline__ float quant_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 127.0f;
+}
+
+// Four codes packed little-endian into 32 bits.
+__device__ __forceinline__ uint32_t code4(const float* v, float scale) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float q = rintf(v[k] / scale);               // IEEE division, round half to even
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    r |= ((uint32_t)(int32_t)q & 0xffu) << (8 * k);
+  }
+  return r;
+}
+
 template <int CDT> struct ElemBytes;
 template <> struct ElemBytes<0> { static constexpr int value = 4; };
 template <> struct ElemBytes<1> { static constexpr int value = 2; };

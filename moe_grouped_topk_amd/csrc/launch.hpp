@@ -7,9 +7,24 @@
 
 namespace moe {
 
+// Optional work of the routing launch for the int8 layer: each token's row
+// of x quantised per row as it is loaded (x_dtype 1 bf16, 0 f32; cols % 8
+// == 0, rows 16-byte aligned) into q / scales, and nzero ints at zero set to
+// 0 (counters of a later launch).
+struct RouteExtra {
+  const void* x;
+  int x_dtype;
+  int64_t cols;
+  int8_t* q;
+  float* scales;
+  int32_t* zero;
+  int64_t nzero;
+};
+
 hipError_t launch_route(const float* gating, int64_t T, int E, int topk, int G,
                         int topk_group, int scoring, int renormalize, float scale,
-                        float* out_w, int32_t* out_ids, hipStream_t stream);
+                        float* out_w, int32_t* out_ids, hipStream_t stream,
+                        const RouteExtra* extra = nullptr);
 
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total,

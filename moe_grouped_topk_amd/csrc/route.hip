@@ -22,13 +22,21 @@
 
 namespace moe {
 
-template <int V>
+// QX (int8 layer): 0 none; 1 / 2: the token's row of bf16 / f32 x is also
+// quantised per row (low-precision GMM article, section 3.2: the scale is
+// taken from the row as it is loaded), and ex.zero is cleared.
+template <int V, int QX>
 __global__ void __launch_bounds__(256)
 route_kernel(const float* __restrict__ gating, int64_t T, int E, int topk,
              int G, int topk_group, int scoring, int renormalize, float scale,
-             float* __restrict__ out_w, int32_t* __restrict__ out_ids) {
+             float* __restrict__ out_w, int32_t* __restrict__ out_ids, RouteExtra ex) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if constexpr (QX != 0) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ex.nzero;
+         i += (int64_t)gridDim.x * blockDim.x)
+      ex.zero[i] = 0;
+  }
   if (t >= T) return;
   const float* row = gating + t * (int64_t)E;
 
@@ -193,25 +201,57 @@ route_kernel(const float* __restrict__ gating, int64_t T, int E, int topk,
     out_w[t * topk + lane] = w;
     out_ids[t * topk + lane] = my_id;
   }
+  if constexpr (QX != 0) {
+    // max |x| of the row (wave max), then its codes, 8 values per lane per step
+    constexpr int XDT = QX == 1 ? 1 : 0;
+    const void* xr = reinterpret_cast<const uint8_t*>(ex.x) + t * ex.cols * (XDT == 1 ? 2 : 4);
+    float amax = 0.0f;
+    for (int64_t i = (int64_t)lane * 8; i < ex.cols; i += kWave * 8) {
+      float v[8];
+      load8<XDT>(xr, i, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    const float qs = quant_scale(amax);
+    int8_t* qr = ex.q + t * ex.cols;
+    for (int64_t i = (int64_t)lane * 8; i < ex.cols; i += kWave * 8) {
+      float v[8];
+      load8<XDT>(xr, i, v);
+      *reinterpret_cast<uint2*>(qr + i) = make_uint2(code4(v, qs), code4(v + 4, qs));
+    }
+    if (lane == 0) ex.scales[t] = qs;
+  }
 }
 
 hipError_t launch_route(const float* gating, int64_t T, int E, int topk, int G,
                         int topk_group, int scoring, int renormalize, float scale,
-                        float* out_w, int32_t* out_ids, hipStream_t stream) {
+                        float* out_w, int32_t* out_ids, hipStream_t stream,
+                        const RouteExtra* extra) {
   if (T == 0) return hipSuccess;
   const int waves_per_block = 4;
   const dim3 block(kWave * waves_per_block);
   const dim3 grid((unsigned)((T + waves_per_block - 1) / waves_per_block));
   const int per_lane = (E + kWave - 1) / kWave;
-#define MOE_ROUTE_CASE(VV)                                                          \
-  hipLaunchKernelGGL(route_kernel<VV>, grid, block, 0, stream, gating, T, E, topk, \
-                     G, topk_group, scoring, renormalize, scale, out_w, out_ids)
+  const RouteExtra ex = extra ? *extra : RouteExtra{};
+  const int qx = extra ? (extra->x_dtype == 1 ? 1 : 2) : 0;
+#define MOE_ROUTE_LAUNCH(VV, QQ)                                                        \
+  hipLaunchKernelGGL((route_kernel<VV, QQ>), grid, block, 0, stream, gating, T, E, topk, \
+                     G, topk_group, scoring, renormalize, scale, out_w, out_ids, ex)
+#define MOE_ROUTE_CASE(VV)                  \
+  do {                                      \
+    if (qx == 0) MOE_ROUTE_LAUNCH(VV, 0);   \
+    else if (qx == 1) MOE_ROUTE_LAUNCH(VV, 1); \
+    else MOE_ROUTE_LAUNCH(VV, 2);           \
+  } while (0)
   if (per_lane <= 1) MOE_ROUTE_CASE(1);
   else if (per_lane <= 2) MOE_ROUTE_CASE(2);
   else if (per_lane <= 4) MOE_ROUTE_CASE(4);
   else if (per_lane <= 8) MOE_ROUTE_CASE(8);
   else MOE_ROUTE_CASE(16);
 #undef MOE_ROUTE_CASE
+#undef MOE_ROUTE_LAUNCH
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill
 # layer).  Only valid for that kernel configuration; None for any other block size or once the
 # kernel has changed since the counters were taken.
-GATE_UP_TRAFFIC = {"block_m": 128, "bytes": None}
+GATE_UP_TRAFFIC = {"block_m": 32, "bytes": None}
 
 
 def log(msg):
@@ -225,9 +225,9 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
         del q1, q2, ws8
 
     # Per-kernel breakdown: the launches moe_forward makes (route, the
-    # two-kernel alignment, gate_up with SiLU*up, down with the routing
-    # weight), each timed with HIP events on the stream they run on; the
-    # top-k reduce is the rest of the step.
+    # two-kernel alignment, the tile table of the expert-wide tiles, gate_up
+    # with SiLU*up, down with the routing weight), each timed with HIP events
+    # on the stream they run on; the top-k reduce is the rest of the step.
     P = T * K
     bm = moe.moe_forward_block_m(T, E, K, "bf16", "packed")   # the block size used here
     w_t, ids_t = moe.moe_route(g, K)
@@ -242,13 +242,23 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
         "route": lambda: moe.moe_route(g, K, topk_weights=w_t, topk_ids=ids_t),
         "align": lambda: moe.moe_align_block_size(ids_t, E, bm, sorted_ids, eids, total,
                                                   workspace=aws),
-        "gemm1_gate_up_silu": lambda: moe.moe_grouped_gemm(
-            x, w1, sorted_ids, eids, total, bm, P, a_rows="pair", a_row_div=K,
-            epilogue="silu_mul", C=h, c_rows="sorted"),
-        "gemm2_down_weighted": lambda: moe.moe_grouped_gemm(
-            h, w2, sorted_ids, eids, total, bm, P, a_rows="sorted", topk_weights=w_t,
-            C=y, c_rows="pair"),
     }
+    if bm == 32:   # expert-wide tiles, as moe_forward runs them for bf16 x
+        table = moe.moe_wide_tile_table(eids, total, E, cap)
+        parts["tile_table"] = lambda: moe.moe_wide_tile_table(eids, total, E, cap, table)
+        parts["gemm1_gate_up_silu"] = lambda: moe.moe_grouped_gemm_wide(
+            x, w1, sorted_ids, eids, total, table, P, a_rows="pair", a_row_div=K,
+            epilogue="silu_mul", C=h, c_rows="sorted")
+        parts["gemm2_down_weighted"] = lambda: moe.moe_grouped_gemm_wide(
+            h, w2, sorted_ids, eids, total, table, P, a_rows="sorted", topk_weights=w_t,
+            C=y, c_rows="pair")
+    else:
+        parts["gemm1_gate_up_silu"] = lambda: moe.moe_grouped_gemm(
+            x, w1, sorted_ids, eids, total, bm, P, a_rows="pair", a_row_div=K,
+            epilogue="silu_mul", C=h, c_rows="sorted")
+        parts["gemm2_down_weighted"] = lambda: moe.moe_grouped_gemm(
+            h, w2, sorted_ids, eids, total, bm, P, a_rows="sorted", topk_weights=w_t,
+            C=y, c_rows="pair")
     br = {}
     for name, fn in parts.items():
         for _ in range(warmup):
@@ -264,10 +274,21 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
         gemm1_flops / br["gemm1_gate_up_silu"]["mean_ms"] * 1e-9
     br["gemm2_down_weighted"]["tflops"] = \
         gemm2_flops / br["gemm2_down_weighted"]["mean_ms"] * 1e-9
+    # algorithmic HBM bytes of each GEMM launch: its weights, its token rows
+    # read once, its output written once (bf16)
+    gemm1_bytes = E * 2 * I * H * 2 + T * H * 2 + P * I * 2
+    gemm2_bytes = E * H * I * 2 + P * I * 2 + P * H * 2
+    for name, nb in (("gemm1_gate_up_silu", gemm1_bytes), ("gemm2_down_weighted", gemm2_bytes)):
+        br[name]["algorithmic_bytes"] = nb
+        br[name]["gbs"] = nb / br[name]["mean_ms"] * 1e-6
+        br[name]["frac_hbm"] = br[name]["gbs"] / PEAK_HBM_GBS
+    br["gemm1_gate_up_silu"]["flushed"]["gbs"] = \
+        gemm1_bytes / br["gemm1_gate_up_silu"]["flushed"]["mean_ms"] * 1e-6
     br["remainder_reduce_and_gaps_ms"] = ms - sum(
-        br[k]["mean_ms"] for k in ("route", "align", "gemm1_gate_up_silu", "gemm2_down_weighted"))
+        br[k]["mean_ms"] for k in parts)
     res["breakdown"] = br
     res["gemm1_flops"] = gemm1_flops
+    res["gemm1_bytes"] = gemm1_bytes
     res["block_m"] = bm
     res["inputs"] = (x_host, g_host, w1_plain, w2_plain)
     return res
@@ -503,15 +524,27 @@ def main():
     log("prefill layer")
     pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
     g1 = pre["breakdown"]["gemm1_gate_up_silu"]
+    # MFMA is the graded bound; at this shape HBM co-binds (206 GFLOP over
+    # 872 MB of weights, tokens and h: 236 FLOP/B, under the 315 FLOP/B
+    # ridge), so the attainable fraction of the MFMA peak is 236 / 315
+    ai = pre["gemm1_flops"] / pre["gemm1_bytes"]
+    attainable = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS * 1e-3)
     roofline = dict(bound="mfma", achieved=g1["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=g1["tflops"] / PEAK_BF16_TFLOPS,
                     traffic=(GATE_UP_TRAFFIC["bytes"] if pre["block_m"] == GATE_UP_TRAFFIC["block_m"]
                              else None),
                     traffic_unit="bytes per launch",
-                    kernel="moe_gemm_dma_kernel, gate_up with the SiLU*up epilogue (the layer's "
-                           "dominant kernel), packed weights",
+                    kernel=("moe_gemm_wide_kernel<1>, gate_up with the SiLU*up epilogue on "
+                            "expert-wide tiles (the layer's dominant kernel), packed weights"
+                            if pre["block_m"] == 32 else
+                            "moe_gemm_dma_kernel, gate_up with the SiLU*up epilogue (the layer's "
+                            "dominant kernel), packed weights"),
                     block_m=pre["block_m"],
-                    flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"])
+                    flops_per_launch=pre["gemm1_flops"], mean_ms=g1["mean_ms"],
+                    hbm=dict(algorithmic_bytes=pre["gemm1_bytes"], achieved_gbs=g1["gbs"],
+                             peak_gbs=PEAK_HBM_GBS, frac=g1["frac_hbm"],
+                             flop_per_byte=ai, attainable_tflops=attainable,
+                             frac_of_attainable=g1["tflops"] / attainable))
     components = {"calibration": calib, "prefill_flushed": pre["flushed"],
                   "prefill_breakdown": pre["breakdown"], "prefill_plain_weights": pre.get("plain_weights"),
                   "prefill_w8a8": pre.get("w8a8"), "prefill_pack_weights_ms": pre["pack_weights_ms"]}

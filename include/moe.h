@@ -231,14 +231,60 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
                      const float* topk_weights, int32_t epilogue, void* C,
                      int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream);
 
+/* ---- grouped GEMM on expert-wide tiles ----------------------------------
+ * The same GEMM as moe_grouped_gemm at block_m 32, with its work cut into
+ * tiles of up to 10 consecutive blocks (320 sorted entries) of one expert
+ * times 256 rows of B, so each slice of an expert's weights is read by one
+ * tile (by two or more only for experts of more than 320 entries).  The
+ * MFMA sequence over K is the tile kernels' one: C is bit-identical to
+ * moe_grouped_gemm at block_m 64 or 128 for the same rows.  Scheduling
+ * follows [GMM] 3.3 and 4.1: work is assigned per expert, with large
+ * experts cut into tiles of near-equal size so that no tile holds much more
+ * than another; a workgroup takes one tile (160 KiB of LDS, one per CU).
+ *
+ * moe_wide_tile_table_size: ints of the tile table for a block-32
+ *   alignment of capacity max_padded (-1 if max_padded is negative or not a
+ *   multiple of 32).
+ * moe_wide_tile_table: writes the table from moe_align_block_size's output
+ *   at block_m 32: table[0] = number of tiles; tile j: table[1 + 3j] =
+ *   expert, table[2 + 3j] = first block, table[3 + 3j] = blocks (1..10); an
+ *   expert of n blocks gets ceil(n / 10) tiles of near-equal size.  One
+ *   launch; E <= 1024 (MOE_ERR_CONFIG otherwise); table_ints below the size
+ *   above is MOE_ERR_WORKSPACE.
+ * moe_grouped_gemm_wide: moe_grouped_gemm's arguments with tile_table (as
+ *   written by moe_wide_tile_table for the same alignment) in place of
+ *   block_m.  A and C bf16 only (MOE_ERR_DTYPE otherwise); SILU_MUL takes no
+ *   topk_weights (MOE_ERR_CONFIG); plain or packed B; E <= 1024.  Table
+ *   entries outside the alignment's blocks or experts are skipped.  Needs
+ *   160 KiB of LDS per workgroup (one per CU).
+ */
+MOE_API int64_t moe_wide_tile_table_size(int64_t max_padded);
+MOE_API int moe_wide_tile_table(const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                                int32_t E, int64_t max_padded, int32_t* table,
+                                int64_t table_ints, void* stream);
+MOE_API int moe_grouped_gemm_wide(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows,
+                                  int32_t a_row_div, const void* B, int32_t b_layout, int32_t E,
+                                  int64_t N, int64_t K, const int32_t* sorted_token_ids,
+                                  const int32_t* expert_ids,
+                                  const int32_t* num_tokens_post_padded, int64_t max_padded,
+                                  const int32_t* tile_table, int64_t num_valid_pairs,
+                                  const float* topk_weights, int32_t epilogue, void* C,
+                                  int32_t c_dtype, int64_t ldc, int32_t c_rows, void* stream);
+
 /* ---- whole layer -------------------------------------------------------
  * moe_forward: [MSG] fused MoE, FusedMoeBackend.forward, with routing per
  * moe_route: route -> align -> gate_up GEMM with silu(gate)*up in its
  * epilogue (intermediate h kept in sorted order, bf16) -> down GEMM times
  * the routing weight -> per-token sum over the topk slots, written in x's
  * dtype.  out[t] = sum_k w[t,k] * W2[e] (silu(W1g[e] x[t]) * (W1u[e] x[t])).
- * The GEMMs are two moe_grouped_gemm launches (gate_up into h in sorted
- * order, then down into per-pair rows y) and the sum is a third launch.
+ * The GEMMs are two launches (gate_up into h in sorted order, then down
+ * into per-pair rows y) and the sum is a third.  At block_m 32 with bf16 x
+ * (and E <= 1024) they run on expert-wide tiles: a small launch builds a
+ * table of tiles of up to 320 consecutive rows of one expert, and each tile
+ * multiplies them against 256 weight rows, so every weight slice is read
+ * once per expert; results are bit-identical to the moe_grouped_gemm tile
+ * kernels (same MFMA sequence over K).  Otherwise the GEMMs are two
+ * moe_grouped_gemm launches.
  *
  *   x        [T, H] bf16 or f32 (x_dtype); out [T, H] in the same dtype.
  *   gating   [T, E] f32 logits.
@@ -246,12 +292,14 @@ MOE_API int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_
  *   w2       [E, H, I] bf16.
  *   w_layout MOE_WEIGHTS_PLAIN, or MOE_WEIGHTS_PACKED: w1 packed with
  *            MOE_EPILOGUE_SILU_MUL and w2 with MOE_EPILOGUE_NONE by
- *            moe_pack_weights (needs bf16 x; block_m 64, 128 or 256).
+ *            moe_pack_weights (needs bf16 x; block_m 32, 64, 128 or 256).
  *   topk_weights_out [T, topk] f32, topk_ids_out [T, topk] int32: optional
  *            (NULL = kept in the workspace only).
- *   block_m  0 = chosen from the average pairs per expert (64 or 128 with
- *            bf16 x or packed weights; 16, 32, 64 or 128 for f32 x on plain
- *            weights); otherwise one of the moe_grouped_gemm block sizes.  With 0, plain weights and a
+ *   block_m  0 = chosen from the average pairs per expert (with bf16 x: 32,
+ *            the expert-wide tiles, at 96 or more pairs per expert and
+ *            E <= 1024, else 64 or 128;
+ *            16, 32, 64 or 128 for f32 x on plain weights); otherwise one of
+ *            the moe_grouped_gemm block sizes.  With 0, plain weights and a
  *            small layer (T * topk <= 2048 and 6 * T * topk * H * I <= 2^28)
  *            the alignment and the tiled GEMMs are skipped: after routing
  *            one launch computes each token's pairs in k order in fp32 (x

@@ -18,7 +18,8 @@ __all__ = [
     "moe_forward_block_m", "moe_forward_workspace_size", "moe_forward", "gmm_int8", "DTYPE", "SCORING",
     "EPILOGUE", "ROWS", "WEIGHTS", "moe_packed_weights_size", "moe_pack_weights",
     "PackedWeights", "moe_quantize_rows", "moe_forward_w8a8_workspace_size", "moe_forward_w8a8",
-    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_wide_tile_table_size",
+    "moe_wide_tile_table", "moe_grouped_gemm_wide",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -62,6 +63,13 @@ def _load():
     L.moe_grouped_gemm.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
                                    i32, i64, vp, i32, vp, i32, i64, i32, vp]
     L.moe_grouped_gemm.restype = ctypes.c_int
+    L.moe_wide_tile_table_size.argtypes = [i64]
+    L.moe_wide_tile_table_size.restype = i64
+    L.moe_wide_tile_table.argtypes = [vp, vp, i32, i64, vp, i64, vp]
+    L.moe_wide_tile_table.restype = ctypes.c_int
+    L.moe_grouped_gemm_wide.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i64, i64, vp, vp,
+                                        vp, i64, vp, i64, vp, i32, vp, i32, i64, i32, vp]
+    L.moe_grouped_gemm_wide.restype = ctypes.c_int
     L.moe_forward_block_m.argtypes = [i64, i32, i32, i32, i32]
     L.moe_forward_block_m.restype = i32
     L.moe_forward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
@@ -256,6 +264,53 @@ def moe_grouped_gemm(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded,
         _ptr(expert_ids, torch.int32, "expert_ids"),
         _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
         sorted_token_ids.numel(), block_m, num_valid_pairs,
+        _ptr(topk_weights, torch.float32, "topk_weights"), EPILOGUE[epilogue],
+        _ptr(C, None, "C"), _dtype_code(C), C.shape[-1], ROWS[c_rows], _stream(stream)))
+    return C
+
+
+def moe_wide_tile_table_size(max_padded):
+    return int(lib.moe_wide_tile_table_size(int(max_padded)))
+
+
+def moe_wide_tile_table(expert_ids, num_tokens_post_padded, num_experts, max_padded, table=None,
+                        stream=None):
+    """Tile table of the expert-wide GEMM tiles from a block-32 alignment
+    (int32 [moe_wide_tile_table_size(max_padded)])."""
+    torch = _torch()
+    n = moe_wide_tile_table_size(max_padded)
+    if n < 0:
+        raise ValueError("max_padded must be a non-negative multiple of 32")
+    if table is None:
+        table = torch.empty(n, dtype=torch.int32, device=expert_ids.device)
+    _check("moe_wide_tile_table", lib.moe_wide_tile_table(
+        _ptr(expert_ids, torch.int32, "expert_ids"),
+        _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"), num_experts,
+        max_padded, _ptr(table, torch.int32, "table"), table.numel(), _stream(stream)))
+    return table
+
+
+def moe_grouped_gemm_wide(A, B, sorted_token_ids, expert_ids, num_tokens_post_padded, tile_table,
+                          num_valid_pairs, a_rows="pair", a_row_div=1, topk_weights=None,
+                          epilogue="none", C=None, c_rows="pair", c_num_rows=None, stream=None):
+    """moe_grouped_gemm at block_m 32 on expert-wide tiles (bf16 A and C);
+    tile_table from moe_wide_tile_table on the same alignment."""
+    torch = _torch()
+    b_ptr, b_layout, (E, N, K) = _weights(B, epilogue, "B")
+    nout = N // 2 if epilogue == "silu_mul" else N
+    if C is None:
+        rows = c_num_rows if c_num_rows is not None else (
+            num_valid_pairs if c_rows == "pair" else sorted_token_ids.numel())
+        C = torch.empty((rows, nout), dtype=torch.bfloat16, device=A.device)
+    if expert_ids.numel() < sorted_token_ids.numel() // 32:
+        raise ValueError("expert_ids is smaller than sorted_token_ids / 32")
+    _check("moe_grouped_gemm_wide", lib.moe_grouped_gemm_wide(
+        _ptr(A, None, "A"), _dtype_code(A), A.shape[-1], ROWS[a_rows], a_row_div,
+        b_ptr, b_layout, E, N, K,
+        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _ptr(expert_ids, torch.int32, "expert_ids"),
+        _ptr(num_tokens_post_padded, torch.int32, "num_tokens_post_padded"),
+        sorted_token_ids.numel(), _ptr(tile_table, torch.int32, "tile_table"), num_valid_pairs,
         _ptr(topk_weights, torch.float32, "topk_weights"), EPILOGUE[epilogue],
         _ptr(C, None, "C"), _dtype_code(C), C.shape[-1], ROWS[c_rows], _stream(stream)))
     return C

@@ -64,7 +64,8 @@ int64_t align_max_padded(int64_t P, int32_t E, int32_t B) {
   return (bound + B - 1) / B * B;
 }
 
-int check_gemm(const moe::MoeGemmArgs& a) {
+// wide: the call runs on the expert-wide tile kernel (block 32, packed allowed)
+int check_gemm(const moe::MoeGemmArgs& a, bool wide = false) {
   if (!a.B || !a.total) return MOE_ERR_NULL;
   if (a.max_padded > 0 && (!a.A || !a.C || !a.sorted_ids || !a.expert_ids)) return MOE_ERR_NULL;
   if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16 && a.a_dtype != MOE_DTYPE_I8)
@@ -83,7 +84,8 @@ int check_gemm(const moe::MoeGemmArgs& a) {
   if (!valid_block_m(a.block_m)) return MOE_ERR_CONFIG;
   if (a.block_m == 256 && a.a_dtype == MOE_DTYPE_F32) return MOE_ERR_CONFIG;
   if (a.a_rows == MOE_ROWS_PAIR && a.a_row_div < 1) return MOE_ERR_CONFIG;
-  if (a.b_packed && (a.block_m < 64 || a.a_dtype == MOE_DTYPE_F32)) return MOE_ERR_CONFIG;
+  if (a.b_packed && ((a.block_m < 64 && !wide) || a.a_dtype == MOE_DTYPE_F32))
+    return MOE_ERR_CONFIG;
   if (a.E < 1 || a.N < 16 || a.K < 8 || a.K % 8 != 0) return MOE_ERR_SHAPE;
   const int64_t nout = a.epilogue == MOE_EPILOGUE_SILU_MUL ? a.N / 2 : a.N;
   if (a.epilogue == MOE_EPILOGUE_SILU_MUL ? (a.N % 32 != 0) : (a.N % 16 != 0)) return MOE_ERR_SHAPE;
@@ -106,10 +108,18 @@ int enqueue_gemm(const moe::MoeGemmArgs& a, hipStream_t s) {
   return hip_status(err);
 }
 
-// Packed weights run on the tile kernels only (block_m >= 64); with few rows
-// per expert those skip the MFMAs of empty token columns and stream weights.
-int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
+// Packed weights run on the tile kernels (block_m >= 64) or, with bf16 tokens,
+// on the expert-wide tiles (block 32); with few rows per expert the tile
+// kernels skip the MFMAs of empty token columns and stream weights.
+// (wide: the bf16 layer may take the expert-wide tiles; the int8 layer may not)
+int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout,
+                   bool wide = true) {
   const double avg = (double)T * topk / (double)E;   // pairs per expert
+  // bf16 tokens, many pairs per expert: one tile per expert and 256 weight
+  // rows streams every weight slice once (prefill T = 4096, E = 128: layer
+  // 465 us against 504 us on 256 x 128 tiles at block 128, same bits)
+  if (wide && avg >= 96.0 && x_dtype == MOE_DTYPE_BF16 && E <= moe::kWidePrepMaxExperts)
+    return 32;
   // bf16 tokens take the direct-to-LDS tile kernels at any size (decode
   // T = 16 on plain weights: 1.59 ms at block 64 against 2.40 ms with the
   // weight-streaming kernel at block 16); f32 tokens with plain weights keep
@@ -124,11 +134,16 @@ int choose_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t 
 bool valid_layout(int32_t l) { return l == MOE_WEIGHTS_PLAIN || l == MOE_WEIGHTS_PACKED; }
 
 struct ForwardLayout {
-  size_t w, ids, sorted, eids, total, hist, h, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, h, y, table, bytes;
   int64_t max_padded;
   int block_m;
   bool small;   // the layer after routing runs as one launch (small_layer.hip)
+  bool wide;    // bf16 tokens at block 32: expert-wide tiles from a tile table
 };
+
+bool use_wide(int32_t block_m, int32_t x_dtype, int32_t E) {
+  return block_m == 32 && x_dtype == MOE_DTYPE_BF16 && E <= moe::kWidePrepMaxExperts;
+}
 
 // Small layers with plain weights and the automatic block size skip the
 // alignment and run both GEMMs and the sum in one launch after routing.
@@ -154,6 +169,8 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   L.h = take(2 * (size_t)L.max_padded * (size_t)I);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
   L.small = use_small_layer(T, H, I, E, topk, block_m, w_layout);
+  L.wide = !L.small && use_wide(L.block_m, x_dtype, E);
+  if (L.wide) L.table = take(sizeof(int32_t) * (size_t)moe::wide_table_ints(L.max_padded));
   L.bytes = off;
   return L;
 }
@@ -168,7 +185,7 @@ struct W8a8Layout {
 W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t block_m,
                        int32_t x_dtype) {
   W8a8Layout L{};
-  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, MOE_WEIGHTS_PACKED);
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, MOE_WEIGHTS_PACKED, false);
   const int64_t P = T * topk;
   L.max_padded = align_max_padded(P, E, L.block_m);
   size_t off = 0;
@@ -309,6 +326,50 @@ int moe_grouped_gemm(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows
   return enqueue_gemm(a, as_stream(stream));
 }
 
+int64_t moe_wide_tile_table_size(int64_t max_padded) {
+  if (max_padded < 0 || max_padded % 32 != 0) return -1;
+  return moe::wide_table_ints(max_padded);
+}
+
+int moe_wide_tile_table(const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                        int32_t E, int64_t max_padded, int32_t* table, int64_t table_ints,
+                        void* stream) {
+  if (!num_tokens_post_padded || !table) return MOE_ERR_NULL;
+  if (max_padded > 0 && !expert_ids) return MOE_ERR_NULL;
+  if (E < 1 || E > moe::kWidePrepMaxExperts) return MOE_ERR_CONFIG;
+  if (max_padded < 0 || max_padded % 32 != 0 || max_padded >= INT32_MAX) return MOE_ERR_SHAPE;
+  if (table_ints < moe::wide_table_ints(max_padded)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_wide_prep(expert_ids, num_tokens_post_padded, E, max_padded,
+                                          table, as_stream(stream)));
+}
+
+int moe_grouped_gemm_wide(const void* A, int32_t a_dtype, int64_t lda, int32_t a_rows,
+                          int32_t a_row_div, const void* B, int32_t b_layout, int32_t E, int64_t N,
+                          int64_t K, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                          const int32_t* num_tokens_post_padded, int64_t max_padded,
+                          const int32_t* tile_table, int64_t num_valid_pairs,
+                          const float* topk_weights, int32_t epilogue, void* C, int32_t c_dtype,
+                          int64_t ldc, int32_t c_rows, void* stream) {
+  moe::MoeGemmArgs a{};
+  a.A = A; a.a_dtype = a_dtype; a.lda = lda; a.a_rows = a_rows;
+  a.a_row_div = a_row_div < 1 ? 1 : a_row_div;
+  if (a_rows == MOE_ROWS_PAIR && a_row_div < 1) return MOE_ERR_CONFIG;
+  if (!valid_layout(b_layout)) return MOE_ERR_CONFIG;
+  if (a_dtype != MOE_DTYPE_BF16 || c_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (epilogue == MOE_EPILOGUE_SILU_MUL && topk_weights) return MOE_ERR_CONFIG;
+  if (E > moe::kWidePrepMaxExperts) return MOE_ERR_CONFIG;
+  a.B = B; a.b_packed = b_layout == MOE_WEIGHTS_PACKED; a.E = E; a.N = N; a.K = K;
+  a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.total = num_tokens_post_padded;
+  a.max_padded = max_padded; a.block_m = 32; a.num_valid = num_valid_pairs;
+  a.topk_weights = topk_weights; a.epilogue = epilogue;
+  a.C = C; a.c_dtype = c_dtype; a.ldc = ldc; a.c_rows = c_rows;
+  const int st = check_gemm(a, true);
+  if (st != MOE_OK) return st;
+  if (max_padded == 0) return MOE_OK;
+  if (!tile_table) return MOE_ERR_NULL;
+  return hip_status(moe::launch_moe_gemm_wide(a, tile_table, as_stream(stream)));
+}
+
 int32_t moe_forward_block_m(int64_t T, int32_t E, int32_t topk, int32_t x_dtype, int32_t w_layout) {
   if (T < 0 || E < 1 || topk < 1) return -1;
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return -1;
@@ -346,7 +407,9 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
   if (block_m != 0 && !valid_block_m(block_m)) return MOE_ERR_CONFIG;
   if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
   const bool packed = w_layout == MOE_WEIGHTS_PACKED;
-  if (packed && (x_dtype != MOE_DTYPE_BF16 || (block_m != 0 && block_m < 64))) return MOE_ERR_CONFIG;
+  if (packed && (x_dtype != MOE_DTYPE_BF16 ||
+                 (block_m != 0 && block_m < 64 && !use_wide(block_m, x_dtype, E))))
+    return MOE_ERR_CONFIG;
   if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0) return MOE_ERR_SHAPE;
   int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
   if (st != MOE_OK) return st;
@@ -395,19 +458,27 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
   g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
   g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I;
   g1.c_rows = MOE_ROWS_SORTED;
-  st = check_gemm(g1);
+  st = check_gemm(g1, L.wide);
   if (st != MOE_OK) return st;
 
   moe::MoeGemmArgs g2 = g1;
   g2.A = h; g2.a_dtype = MOE_DTYPE_BF16; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1;
   g2.B = w2; g2.N = H; g2.K = I; g2.topk_weights = w; g2.epilogue = MOE_EPILOGUE_NONE;
   g2.C = y; g2.c_dtype = x_dtype; g2.ldc = H; g2.c_rows = MOE_ROWS_PAIR;
-  st = check_gemm(g2);
+  st = check_gemm(g2, L.wide);
   if (st != MOE_OK) return st;
 
-  st = enqueue_gemm(g1, s);
-  if (st == MOE_OK) st = enqueue_gemm(g2, s);
-  if (st != MOE_OK) return st;
+  if (L.wide) {
+    int32_t* table = reinterpret_cast<int32_t*>(base + L.table);
+    err = moe::launch_wide_prep(eids, total, E, L.max_padded, table, s);
+    if (err == hipSuccess) err = moe::launch_moe_gemm_wide(g1, table, s);
+    if (err == hipSuccess) err = moe::launch_moe_gemm_wide(g2, table, s);
+    if (err != hipSuccess) return hip_status(err);
+  } else {
+    st = enqueue_gemm(g1, s);
+    if (st == MOE_OK) st = enqueue_gemm(g2, s);
+    if (st != MOE_OK) return st;
+  }
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }
 

@@ -83,6 +83,16 @@ struct MoeGemmArgs {
 
 // MFMA tile kernel, block_m 64 or 128.
 hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream);
+
+// Expert-wide tiles (bf16 tokens and h, block_m 32): a tile table of
+// wide_table_ints(max_padded) ints built from the alignment by
+// launch_wide_prep, then one launch per GEMM (gate_up with SiLU*up into h
+// in sorted order; down with the routing weight into pair rows).
+constexpr int kWidePrepMaxExperts = 1024;
+int64_t wide_table_ints(int64_t max_padded);
+hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int E,
+                            int64_t max_padded, int32_t* table, hipStream_t stream);
+hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipStream_t stream);
 // Weight-streaming kernel, block_m 16 or 32.
 hipError_t launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t stream);
 

@@ -1231,6 +1231,453 @@ gmm_i8_tile_kernel(GmmI8Args a) {
   gmm_tile_epilogue(a, t, rowinfo, acc, smem, ar);
 }
 
+// ---------------------------------------------------------------------------
+// Expert-wide tiles (bf16).  The alignment pads each expert to 32-row blocks
+// and one tile covers up to kWideMaxBlk consecutive blocks of one expert
+// (every block of an expert with up to 320 pairs) against 256 weight rows,
+// so a weight slice is streamed once for all of the expert's rows, and the
+// tiles of one expert's n-tiles run side by side and share its token rows in
+// L2.  One workgroup per CU (8 waves of 64 weight rows x up to 160 tokens).
+// Weights and tokens have rings of their own: kWideNW weight stages (they
+// come from HBM, so they are issued kWideNW - 1 stages ahead) and kWideNT
+// token stages (token rows are mostly L2 hits).  Token pieces past the
+// tile's blocks are not loaded at all (each wave's count of loads per stage
+// is then smaller, and its waits count exactly what it issued).
+#ifndef MOE_WIDE_NW
+#define MOE_WIDE_NW 4
+#endif
+#ifndef MOE_WIDE_NT
+#define MOE_WIDE_NT 4
+#endif
+#ifndef MOE_WIDE_MAXBLK
+#define MOE_WIDE_MAXBLK 10
+#endif
+constexpr int kWideBN = 256;
+constexpr int kWideBlk = 32;
+constexpr int kWideMaxBlk = MOE_WIDE_MAXBLK;
+constexpr int kWideBM = kWideBlk * kWideMaxBlk;            // token rows of a full tile
+constexpr int kWideWN = 4, kWideWM = 2, kWideThreads = 64 * kWideWN * kWideWM;
+constexpr int kWideNW = MOE_WIDE_NW, kWideNT = MOE_WIDE_NT;
+static_assert(kWideNW >= kWideNT && kWideNT >= 2, "weight stages go out no later than token stages");
+constexpr int kWideRowB = 64;                               // K bytes per row per stage
+constexpr int kWideWStage = kWideBN * kWideRowB;            // 16 KiB
+constexpr int kWideTStage = kWideBM * kWideRowB;            // 20 KiB
+constexpr int kWideLds = kWideNW * kWideWStage + kWideNT * kWideTStage;
+constexpr int kWideRB = kWideBN / kWideWN / 32;             // 2
+constexpr int kWideCB = (kWideMaxBlk + kWideWM - 1) / kWideWM;   // token blocks per wave
+constexpr int kWideWP = kWideBN / 16 / (kWideWN * kWideWM); // 2 weight pieces per wave
+constexpr int kWideTP = (kWideBM / 16 + (kWideWN * kWideWM) - 1) / (kWideWN * kWideWM);   // <= 3
+static_assert(kWideBN == kPackRows, "a wide tile's weight rows are one packed tile");
+static_assert(kWideLds + kWideBM * 4 <= 160 * 1024, "rings of the wide tile");
+
+// Tile table of a layer: t[0] = number of tiles; tile j: t[1 + 3 j] = expert,
+// t[2 + 3 j] = first block, t[3 + 3 j] = blocks (1..kWideMaxBlk).  An expert
+// of nb blocks gets ceil(nb / kWideMaxBlk) tiles of nearly equal size.
+constexpr int kWidePrepThreads = kWidePrepMaxExperts;
+
+__global__ void __launch_bounds__(kWidePrepThreads)
+wide_prep_kernel(const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ total, int E,
+                 int nblk_max, int32_t* __restrict__ table) {
+  __shared__ int cnt[kWidePrepThreads], first[kWidePrepThreads], scan[kWidePrepThreads];
+  const int tid = threadIdx.x;
+  int nblk = *total / kWideBlk;
+  nblk = nblk < nblk_max ? nblk : nblk_max;
+  cnt[tid] = 0;
+  first[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < nblk; b += kWidePrepThreads) {
+    const int e = expert_ids[b];
+    if (e < 0 || e >= E) continue;
+    atomicAdd(&cnt[e], 1);
+    if (b == 0 || expert_ids[b - 1] != e) first[e] = b;   // an expert's blocks are contiguous
+  }
+  __syncthreads();
+  const int nt = tid < E ? (cnt[tid] + kWideMaxBlk - 1) / kWideMaxBlk : 0;
+  scan[tid] = nt;
+  __syncthreads();
+  for (int off = 1; off < kWidePrepThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int start = scan[tid] - nt;
+  for (int i = 0; i < nt; ++i) {
+    const int j = start + i;
+    const int b0 = first[tid] + (int)((int64_t)i * cnt[tid] / nt);
+    const int b1 = first[tid] + (int)((int64_t)(i + 1) * cnt[tid] / nt);
+    table[1 + 3 * j] = tid;
+    table[2 + 3 * j] = b0;
+    table[3 + 3 * j] = b1 - b0;
+  }
+  if (tid == kWidePrepThreads - 1) table[0] = scan[tid];
+}
+
+// Loads of one stage by this wave: nt token pieces (1 KiB each; positions
+// q = wave + 8 i) and kWideWP weight pieces (q = wave * kWideWP + i).
+// Order in the instruction stream: tokens, then weights.
+struct WideSrc {
+  const uint8_t* w[kWideWP];   // this lane's 16 bytes of stage 0 of each weight piece
+  const uint8_t* t[kWideTP];   // this lane's token row start of each token piece
+  uint32_t wlds[kWideWP], tlds[kWideTP];   // LDS byte offset of each piece in its ring stage 0
+  int nt;                      // token pieces of this wave (wave-uniform)
+  bool packed, stream;         // packed weights; non-temporal weight loads
+};
+
+// wait until at most N of this wave's loads are outstanding, then barrier
+// (n is wave-uniform; the most a wave can have issued after a stage's token
+// loads is (kWideNT - 2) * (kWideTP + kWideWP))
+static_assert((kWideNT - 2) * (kWideTP + kWideWP) <= 15, "wide_wait covers 0..15");
+__device__ __forceinline__ void wide_wait(int n) {
+  switch (n) {
+    case 0: wait_vm_barrier<0>(); break;
+    case 1: wait_vm_barrier<1>(); break;
+    case 2: wait_vm_barrier<2>(); break;
+    case 3: wait_vm_barrier<3>(); break;
+    case 4: wait_vm_barrier<4>(); break;
+    case 5: wait_vm_barrier<5>(); break;
+    case 6: wait_vm_barrier<6>(); break;
+    case 7: wait_vm_barrier<7>(); break;
+    case 8: wait_vm_barrier<8>(); break;
+    case 9: wait_vm_barrier<9>(); break;
+    case 10: wait_vm_barrier<10>(); break;
+    case 11: wait_vm_barrier<11>(); break;
+    case 12: wait_vm_barrier<12>(); break;
+    case 13: wait_vm_barrier<13>(); break;
+    case 14: wait_vm_barrier<14>(); break;
+    default: wait_vm_barrier<15>(); break;
+  }
+}
+
+// K loop of a wide tile: stages [0, nk) of kbytes bytes of K.  ncb: this
+// wave's token blocks (its accumulators beyond them stay untouched).
+template <int NCB>
+__device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src, int64_t kbytes,
+                                              const int (&wrow)[kWideRB], int tcol0,
+                                              f32x16_t (&acc)[kWideRB][kWideCB]) {
+  const int tid = tile_tid(), lane = tid & 63;
+  const uint32_t wbase = lds_addr(smem), tbase = wbase + kWideNW * kWideWStage;
+  const int nk = (int)((kbytes + kWideRowB - 1) / kWideRowB);
+  const int chunk_pos = lane & 3;
+  const int nw = kWideWP, ntw = __builtin_amdgcn_readfirstlane(src.nt);
+
+  auto issue_t = [&](int kt) {
+    const uint32_t st = tbase + (uint32_t)((kt % kWideNT) * kWideTStage);
+    const int64_t koff = (int64_t)kt * kWideRowB;
+#pragma unroll
+    for (int i = 0; i < kWideTP; ++i) {
+      if (i < ntw) {
+        const int row = (int)(src.tlds[i] / kWideRowB) + (lane >> 2);
+        const int c = chunk_pos ^ ((row >> 2) & 3);
+        const int64_t off = koff + c * 16 < kbytes ? koff + c * 16 : 0;   // past K: row start
+        dma16(__builtin_amdgcn_readfirstlane(st + src.tlds[i]), src.t[i] + off);
+      }
+    }
+  };
+  auto issue_w = [&](int kt) {
+    const uint32_t st = wbase + (uint32_t)((kt % kWideNW) * kWideWStage);
+    const int64_t koff = (int64_t)kt * kWideRowB;
+#pragma unroll
+    for (int i = 0; i < kWideWP; ++i) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + src.wlds[i]);
+      if (src.packed) {
+        const uint8_t* g = src.w[i] + (int64_t)kt * kPackBlockBytes;
+        if (src.stream) dma16_nt(m0, g); else dma16(m0, g);
+      } else {
+        const int row = (int)(src.wlds[i] / kWideRowB) + (lane >> 2);
+        const int c = chunk_pos ^ ((row >> 2) & 3);
+        dma16(m0, src.w[i] + (koff + c * 16 < kbytes ? koff + c * 16 : 0));
+      }
+    }
+  };
+  // zero the chunks of a partial stage that lie past K (after its loads landed)
+  auto zero_tail = [&](int kt) {
+    const int64_t koff = (int64_t)kt * kWideRowB;
+    uint8_t* ws = smem + (kt % kWideNW) * kWideWStage;
+    uint8_t* ts = smem + kWideNW * kWideWStage + (kt % kWideNT) * kWideTStage;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    if (!src.packed) {
+#pragma unroll
+      for (int i = 0; i < kWideWP; ++i) {
+        const int row = (int)(src.wlds[i] / kWideRowB) + (lane >> 2);
+        if (koff + (chunk_pos ^ ((row >> 2) & 3)) * 16 >= kbytes)
+          *reinterpret_cast<u32x4_t*>(ws + src.wlds[i] + lane * 16) = z;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWideTP; ++i) {
+      if (i < ntw) {
+        const int row = (int)(src.tlds[i] / kWideRowB) + (lane >> 2);
+        if (koff + (chunk_pos ^ ((row >> 2) & 3)) * 16 >= kbytes)
+          *reinterpret_cast<u32x4_t*>(ts + src.tlds[i] + lane * 16) = z;
+      }
+    }
+  };
+  // Issue schedule: at the start of iteration i (its stage published, every
+  // wave done with stage i - 1) W(i + NW - 1), then T(i + NT - 1), into the
+  // buffers of stage i - 1; the prologue issues the same sequence for i < 0.
+  // Loads complete in issue order, so stage s is in when the loads issued
+  // after T(s) are all that may be outstanding: the W and T of the NT - 2
+  // iterations after the one that issued T(s) (W(s) went out before T(s),
+  // in the same iteration or an earlier one, as NW >= NT).
+  auto n_after = [&](int s) {
+    int n = 0;
+#pragma unroll
+    for (int i = s - kWideNT + 2; i < s; ++i)
+      n += (i + kWideNT - 1 < nk ? ntw : 0) + (i + kWideNW - 1 < nk ? nw : 0);
+    return n;
+  };
+  const bool partial = (kbytes % kWideRowB) != 0;
+  auto publish = [&](int s) {
+    if (partial && s == nk - 1) {
+      wide_wait(0);
+      zero_tail(s);
+      __syncthreads();
+    } else {
+      wide_wait(n_after(s));
+    }
+  };
+  for (int i = 1 - kWideNW; i < 0; ++i) {
+    if (i + kWideNW - 1 < nk) issue_w(i + kWideNW - 1);
+    if (i + kWideNT - 1 >= 0 && i + kWideNT - 1 < nk) issue_t(i + kWideNT - 1);
+  }
+
+  const int swz = ((lane & 31) >> 2) & 3;
+  auto load_frags = [&](int kt, int ks, u32x4_t (&af)[kWideRB], u32x4_t (&bf)[kWideCB]) {
+    const uint8_t* ws = smem + (kt % kWideNW) * kWideWStage + (lane & 31) * kWideRowB;
+    const uint8_t* ts = smem + kWideNW * kWideWStage + (kt % kWideNT) * kWideTStage +
+                        (lane & 31) * kWideRowB;
+    const int pos = ((ks * 2 + (lane >> 5)) ^ swz) * 16;
+    if constexpr (NCB > 0) {
+#pragma unroll
+      for (int rb = 0; rb < kWideRB; ++rb)
+        af[rb] = *reinterpret_cast<const u32x4_t*>(ws + wrow[rb] * kWideRowB + pos);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      bf[cb] = *reinterpret_cast<const u32x4_t*>(ts + (tcol0 + cb * 32) * kWideRowB + pos);
+  };
+  auto mfmas = [&](const u32x4_t (&af)[kWideRB], const u32x4_t (&bf)[kWideCB]) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kWideRB; ++rb) acc[rb][cb] = Mma<0>::run(af[rb], bf[cb], acc[rb][cb]);
+  };
+  // one set of fragments (the accumulators take most of the registers; the
+  // other wave on the SIMD covers the LDS latency)
+  u32x4_t af[kWideRB], bf[kWideCB];
+  publish(0);
+  // the first fragments go out before the refills, whose address arithmetic
+  // then runs under their LDS latency
+  load_frags(0, 0, af, bf);
+  if (kWideNW - 1 < nk) issue_w(kWideNW - 1);
+  if (kWideNT - 1 < nk) issue_t(kWideNT - 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    mfmas(af, bf);
+    load_frags(kt, 1, af, bf);
+    mfmas(af, bf);
+    if (kt + 1 < nk) {
+      publish(kt + 1);
+      load_frags(kt + 1, 0, af, bf);
+      // every wave has finished reading stage kt: refill its buffers
+      if (kt + kWideNW < nk) issue_w(kt + kWideNW);
+      if (kt + kWideNT < nk) issue_t(kt + kWideNT);
+    }
+  }
+}
+
+// Runs the K loop specialised for this wave's number of token blocks.
+__device__ __forceinline__ void wide_mainloop_live(uint8_t* smem, const WideSrc& src,
+                                                   int64_t kbytes, const int (&wrow)[kWideRB],
+                                                   int tcol0, int ncb,
+                                                   f32x16_t (&acc)[kWideRB][kWideCB]) {
+  switch (__builtin_amdgcn_readfirstlane(ncb)) {
+    case 5: return wide_mainloop<5>(smem, src, kbytes, wrow, tcol0, acc);
+    case 4: return wide_mainloop<4>(smem, src, kbytes, wrow, tcol0, acc);
+    case 3: return wide_mainloop<3>(smem, src, kbytes, wrow, tcol0, acc);
+    case 2: return wide_mainloop<2>(smem, src, kbytes, wrow, tcol0, acc);
+    case 1: return wide_mainloop<1>(smem, src, kbytes, wrow, tcol0, acc);
+    default: return wide_mainloop<0>(smem, src, kbytes, wrow, tcol0, acc);
+  }
+}
+
+// EPI 1: gate_up with the SiLU*up epilogue, bf16 h in sorted order;
+// EPI 0: down times the routing weight, bf16 rows in pair order.
+template <int EPI>
+__global__ void __launch_bounds__(kWideThreads, 2)
+moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[kWideBM];
+  const int ntile = moe_ntiles<kWideBN, EPI>(a);
+  const int live = table[0] * ntile;
+  if ((int)blockIdx.x >= live) return;
+  // the n-tiles of one expert tile are neighbours: they run side by side and
+  // share the expert's token rows in L2
+  const int L = xcd_remap((int)blockIdx.x, live);
+  const int j = L / ntile, nt = L % ntile;
+  const int e = table[1 + 3 * j], b0 = table[2 + 3 * j], nb = table[3 + 3 * j];
+  // a tile outside the alignment's blocks or experts is skipped, not read
+  if (e < 0 || e >= a.E || b0 < 0 || nb < 1 || nb > kWideMaxBlk ||
+      (int64_t)(b0 + nb) * kWideBlk > a.max_padded)
+    return;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % kWideWN, wm = wave / kWideWN;
+  const int nrows = nb * kWideBlk;
+  const int64_t s0 = (int64_t)b0 * kWideBlk;          // first sorted position
+  for (int r = tid; r < kWideBM; r += kWideThreads) {
+    int p = -1;
+    if (r < nrows) {
+      p = a.sorted_ids[s0 + r];
+      if (p < 0 || p >= a.num_valid) p = -1;
+    }
+    rowinfo[r] = p;
+  }
+  __syncthreads();
+
+  MoeTile t;
+  t.e = e; t.blk = b0; t.nt = nt; t.s0 = s0;
+  t.c0 = (int64_t)nt * (EPI ? kWideBN / 2 : kWideBN);
+  t.solo = 0;
+  WideSrc src;
+  src.packed = a.b_packed != 0;
+  const int64_t wrow_bytes = a.K * 2;
+  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)e * a.N * wrow_bytes;
+  const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
+                      ((int64_t)e * packed_tiles(a.N, EPI) + nt) * packed_kstages(a.K, 2) *
+                          kPackBlockBytes;
+  // the only tile that streams this weight slice: non-temporal loads
+  src.stream = src.packed && (j == 0 || table[1 + 3 * (j - 1)] != e) &&
+               (j + 1 >= table[0] || table[1 + 3 * (j + 1)] != e);
+#pragma unroll
+  for (int i = 0; i < kWideWP; ++i) {
+    const int q = wave * kWideWP + i;
+    src.wlds[i] = (uint32_t)(q * 1024);
+    if (src.packed) {
+      src.w[i] = Bp + q * 1024 + lane * 16;
+    } else {
+      const int64_t g = moe_weight_row<kWideBN, EPI>(a, t.c0, q * 16 + (lane >> 2));
+      src.w[i] = Bw + (g < 0 ? 0 : g) * wrow_bytes;      // past the matrix: row 0
+    }
+  }
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
+  const int64_t arow_bytes = a.lda * 2;
+  src.nt = 0;
+#pragma unroll
+  for (int i = 0; i < kWideTP; ++i) {
+    const int q = wave + i * (kWideWN * kWideWM);
+    src.tlds[i] = (uint32_t)(q * 1024);
+    const int r = q * 16 + (lane >> 2);
+    if (q * 16 < nrows) {
+      src.nt = i + 1;
+      const int p = rowinfo[r];
+      const int p0 = rowinfo[0] < 0 ? 0 : rowinfo[0];  // row 0 of a tile is a pair
+      const int64_t row = a.a_rows == 0 ? (int64_t)((p < 0 ? p0 : p) / a.a_row_div)
+                                        : (p < 0 ? s0 : s0 + r);
+      src.t[i] = Ab + row * arow_bytes;
+    } else {
+      src.t[i] = Ab;
+    }
+  }
+  int wrow[kWideRB];
+  wave_rows<kWideBN, kWideWN, kWideRB, EPI>(wn, wrow);
+  const int h = (nb + 1) / 2;                          // token blocks of wave row 0
+  const int tcol0 = wm ? h * kWideBlk : 0;
+  const int ncb = wm ? nb - h : h;
+  // this thread's row weight (down), read while the K loop runs
+  float wr = 1.0f;
+  if (!EPI && a.topk_weights && tid < nrows && rowinfo[tid] >= 0)
+    wr = a.topk_weights[rowinfo[tid]];
+  f32x16_t acc[kWideRB][kWideCB];
+#pragma unroll
+  for (int rb = 0; rb < kWideRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kWideCB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+  wide_mainloop_live(smem, src, wrow_bytes, wrow, tcol0, ncb, acc);
+
+  // Epilogue through LDS (the drained rings), whole 16-byte pieces of rows.
+  const int rsub = 4 * (lane >> 5);
+  uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
+  if constexpr (EPI) {
+    constexpr int HC = kWideBN / 2, PITCH = HC * 2 + 16, LPR = HC * 2 / 16;
+    constexpr int RPP = kWideThreads / LPR;
+    static_assert(kWideBM * PITCH <= kWideLds, "staged wide SiLU tile");
+    const int64_t Nout = a.N / 2;
+    __syncthreads();                                   // every wave has left the rings
+#pragma unroll
+    for (int cb = 0; cb < kWideCB; ++cb) {
+      if (cb < ncb) {
+        uint8_t* dst = smem + (tcol0 + cb * 32 + (lane & 31)) * PITCH;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wrow[0] + 8 * g + rsub;
+          const f32x16_t& gt = acc[0][cb];
+          const f32x16_t& up = acc[1][cb];
+          *reinterpret_cast<uint2*>(dst + col * 2) = make_uint2(
+              pack_bf16x2(silu_f32(gt[4 * g]) * up[4 * g], silu_f32(gt[4 * g + 1]) * up[4 * g + 1]),
+              pack_bf16x2(silu_f32(gt[4 * g + 2]) * up[4 * g + 2],
+                          silu_f32(gt[4 * g + 3]) * up[4 * g + 3]));
+        }
+      }
+    }
+    __syncthreads();
+    const int ch = tid % LPR;
+    const int64_t col = t.c0 + ch * 8;
+    for (int r0 = 0; r0 < nrows; r0 += RPP) {
+      const int r = r0 + tid / LPR;
+      if (r >= nrows || rowinfo[r] < 0 || col >= Nout) continue;
+      const int64_t crow = a.c_rows == 0 ? (int64_t)rowinfo[r] : s0 + r;
+      *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) =
+          *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+    }
+  } else {
+    // two passes, one per wave row (at most kWideCB * 32 rows each)
+    constexpr int PITCH = kWideBN * 2 + 16, LPR = kWideBN * 2 / 16;
+    constexpr int RPP = kWideThreads / LPR, PR = kWideCB * 32;
+    static_assert(PR * PITCH + kWideBM * 4 <= kWideLds, "staged wide down tile");
+    float* s_w = reinterpret_cast<float*>(smem + PR * PITCH);
+    __syncthreads();                                   // every wave has left the rings
+    if (tid < kWideBM) s_w[tid] = wr;
+    const int ch = tid % LPR;
+    const int64_t col = t.c0 + ch * 8;
+#pragma unroll
+    for (int pass = 0; pass < kWideWM; ++pass) {
+      const int rbase = pass ? h * kWideBlk : 0;
+      const int rend = pass ? nrows : h * kWideBlk;
+      __syncthreads();
+      if (wm == pass) {
+#pragma unroll
+        for (int cb = 0; cb < kWideCB; ++cb) {
+          if (cb < ncb) {
+            const int trow = tcol0 + cb * 32 + (lane & 31);
+            const float w = s_w[trow];
+            uint8_t* dst = smem + (trow - rbase) * PITCH;
+#pragma unroll
+            for (int rb = 0; rb < kWideRB; ++rb) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x16_t& v = acc[rb][cb];
+                *reinterpret_cast<uint2*>(dst + (wrow[rb] + 8 * g + rsub) * 2) =
+                    make_uint2(pack_bf16x2(v[4 * g] * w, v[4 * g + 1] * w),
+                               pack_bf16x2(v[4 * g + 2] * w, v[4 * g + 3] * w));
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int r0 = rbase; r0 < rend; r0 += RPP) {
+        const int r = r0 + tid / LPR;
+        if (r >= rend || rowinfo[r] < 0 || col >= a.N) continue;
+        const int64_t crow = a.c_rows == 0 ? (int64_t)rowinfo[r] : s0 + r;
+        *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) =
+            *reinterpret_cast<const u32x4_t*>(smem + (r - rbase) * PITCH + ch * 16);
+      }
+    }
+  }
+}
+
 // Dynamic LDS beyond 64 KiB has to be requested per kernel.
 template <typename K>
 hipError_t ensure_lds(K kernel, size_t bytes) {
@@ -1334,6 +1781,34 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream) {
     case 128: return launch_tile_bm<128>(a, stream);
     default: return launch_tile_bm<256>(a, stream);
   }
+}
+
+int64_t wide_table_ints(int64_t max_padded) { return 1 + 3 * (max_padded / kWideBlk); }
+
+hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int E,
+                            int64_t max_padded, int32_t* table, hipStream_t stream) {
+  if (E < 1 || E > kWidePrepThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wide_prep_kernel, dim3(1), dim3(kWidePrepThreads), 0, stream, expert_ids,
+                     total, E, (int)(max_padded / kWideBlk), table);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipStream_t stream) {
+  if (a.block_m != kWideBlk || a.a_dtype != 1 || a.c_dtype != 1 || (a.epilogue && a.topk_weights))
+    return hipErrorInvalidValue;   // the ABI layer checks these first
+  // tiles: at most one per expert plus one per kWideMaxBlk blocks
+  const int64_t nblk = a.max_padded / kWideBlk;
+  const int64_t tiles = nblk / kWideMaxBlk + (a.E < nblk ? a.E : nblk);
+  const int64_t ntile = a.epilogue ? (a.N / 2 + kWideBN / 2 - 1) / (kWideBN / 2)
+                                   : (a.N + kWideBN - 1) / kWideBN;
+  const int64_t grid = tiles * ntile;
+  if (grid == 0) return hipSuccess;
+  void (*k)(MoeGemmArgs, const int32_t*) =
+      a.epilogue ? moe_gemm_wide_kernel<1> : moe_gemm_wide_kernel<0>;
+  const hipError_t st = ensure_lds(k, kWideLds);
+  if (st != hipSuccess) return st;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kWideThreads), kWideLds, stream, a, table);
+  return hipGetLastError();
 }
 
 hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream) {

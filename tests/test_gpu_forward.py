@@ -83,9 +83,9 @@ def test_tiny_layer(moe, dev, block_m):
     assert err <= BAR_BF16
 
 
-@pytest.mark.parametrize("block_m,layout", [(16, "plain"), (128, "plain"), (256, "plain"),
-                                            (0, "packed"), (64, "packed"), (128, "packed"),
-                                            (256, "packed")])
+@pytest.mark.parametrize("block_m,layout", [(16, "plain"), (32, "plain"), (128, "plain"),
+                                            (256, "plain"), (0, "packed"), (32, "packed"),
+                                            (64, "packed"), (128, "packed"), (256, "packed")])
 def test_tiny_layer_bf16_x(moe, dev, block_m, layout):
     cfg = synth.CONFIGS["tiny"]
     d = layer_inputs(cfg, dev, x_dtype="bf16")
@@ -173,7 +173,7 @@ def test_decode_layer_full(moe, dev, name):
         assert err <= BAR_BF16, k
 
 
-@pytest.mark.parametrize("block_m", [64, 128, 256])
+@pytest.mark.parametrize("block_m", [32, 64, 128, 256])
 def test_layer_reuses_workspace(moe, dev, block_m):
     """Consecutive layers on one workspace that starts full of garbage, with
     different tokens and sizes: no call reads another call's alignment, h or
@@ -269,7 +269,7 @@ def test_small_layer_repeatable_on_garbage_workspace(moe, dev):
 
 @pytest.mark.parametrize("scoring,renorm,scale", [("sigmoid", True, 1.0), ("sigmoid", False, 2.5),
                                                   ("softmax", False, 1.5)])
-@pytest.mark.parametrize("block_m", [0, 128])
+@pytest.mark.parametrize("block_m", [0, 32, 128])
 def test_layer_routing_variants(moe, dev, scoring, renorm, scale, block_m):
     """The whole layer with the other routing variants (sigmoid scores, no
     renormalisation, a scale): moe_forward's own routing is checked against

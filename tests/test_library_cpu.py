@@ -189,7 +189,9 @@ def test_forward_validation(mod):
     assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
     a = list(args); a[5] = 1; a[1] = 0      # packed weights with f32 x
     assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
-    a = list(args); a[5] = 1; a[16] = 32    # packed weights with the streaming block size
+    a = list(args); a[5] = 1; a[16] = 16    # packed weights with the streaming block size
+    assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[5] = 1; a[1] = 0; a[16] = 32   # block 32 packed: bf16 x only (wide tiles)
     assert L.moe_forward(*a) == d["MOE_ERR_CONFIG"]
 
 
@@ -295,13 +297,16 @@ def test_gmm_validation(mod):
 
 
 def test_forward_block_m_choice(mod):
-    assert mod.moe_forward_block_m(4096, 128, 8) == 128          # prefill shape: 256 x 128 tiles
-    assert mod.moe_forward_block_m(4096, 128, 8, "f32") == 128
+    assert mod.moe_forward_block_m(4096, 128, 8) == 32           # prefill shape: expert-wide tiles
+    assert mod.moe_forward_block_m(4096, 128, 8, "f32") == 128   # f32 x: 256 x 128 tiles
+    assert mod.moe_forward_block_m(1536, 128, 8) == 32           # 96 pairs per expert
+    assert mod.moe_forward_block_m(1535, 128, 8) == 64
+    assert mod.moe_forward_block_m(32768, 2048, 8) == 128        # more experts than the table takes
     assert mod.moe_forward_block_m(16, 256, 8) == 64             # decode shape, bf16 x
     assert mod.moe_forward_block_m(16, 256, 8, "f32") == 16      # f32 x, plain weights
     assert mod.moe_forward_block_m(64, 8, 2, "f32") == 32        # tiny layer
     assert mod.moe_forward_block_m(16, 256, 8, weights="packed") == 64    # tile kernels only
-    assert mod.moe_forward_block_m(4096, 128, 8, weights="packed") == 128
+    assert mod.moe_forward_block_m(4096, 128, 8, weights="packed") == 32
     assert mod.lib.moe_forward_block_m(16, 0, 8, 1, 0) == -1
     assert mod.lib.moe_forward_block_m(16, 256, 8, 1, 5) == -1
 
@@ -317,3 +322,37 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_wide_gemm_validation(mod):
+    """Argument checks of the expert-wide tile entry points (no GPU work)."""
+    L, d = mod.lib, _defines()
+    assert L.moe_wide_tile_table_size(320) == 31
+    assert L.moe_wide_tile_table_size(0) == 1
+    assert L.moe_wide_tile_table_size(33) == -1
+    assert L.moe_wide_tile_table_size(-32) == -1
+    f = ctypes.c_void_p(256)
+    assert L.moe_wide_tile_table(f, f, 0, 320, f, 31, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_wide_tile_table(f, f, 1025, 320, f, 31, None) == d["MOE_ERR_CONFIG"]
+    assert L.moe_wide_tile_table(f, f, 8, 320, f, 30, None) == d["MOE_ERR_WORKSPACE"]
+    assert L.moe_wide_tile_table(f, f, 8, 330, f, 31, None) == d["MOE_ERR_SHAPE"]
+    assert L.moe_wide_tile_table(f, None, 8, 320, f, 31, None) == d["MOE_ERR_NULL"]
+    assert L.moe_wide_tile_table(f, f, 8, 320, None, 31, None) == d["MOE_ERR_NULL"]
+    # A, a_dtype, lda, a_rows, a_row_div, B, b_layout, E, N, K, sorted, eids, total,
+    # max_padded, table, num_valid, topk_weights, epilogue, C, c_dtype, ldc, c_rows, stream
+    base = [f, 1, 128, 0, 2, f, 0, 8, 256, 128, f, f, f, 320, f, 100, None, 1, f, 1, 128, 1,
+            None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[{"a_dtype": 1, "E": 7, "table": 14, "w": 16, "epi": 17, "c_dtype": 19,
+               "bl": 6, "K": 9}[k]] = v
+        return L.moe_grouped_gemm_wide(*a)
+    assert call(a_dtype=0) == d["MOE_ERR_DTYPE"]                # f32 A
+    assert call(c_dtype=0) == d["MOE_ERR_DTYPE"]                # f32 C
+    assert call(w=f) == d["MOE_ERR_CONFIG"]                     # SiLU takes no weights
+    assert call(E=1025) == d["MOE_ERR_CONFIG"]
+    assert call(bl=2) == d["MOE_ERR_CONFIG"]
+    assert call(K=100) == d["MOE_ERR_SHAPE"]
+    assert call(table=None) == d["MOE_ERR_NULL"]

@@ -1,9 +1,10 @@
 """GPU check of moe_forward_noalloc, the layer call that allocates nothing
 (its workspace is the library's static per-device scratch): through the C
 ABI, two calls in a row (the second with fewer tokens) give bit-identical
-results to moe_forward on a workspace of its own, on the persistent-launch
-path (bf16 tokens, packed weights) and on the two-launch path (f32 tokens,
-plain weights); the first is also checked against the oracle."""
+results to moe_forward on a workspace of its own: bf16 tokens on packed
+weights (the expert-wide tiles for the first call, 300 pairs per expert,
+then the 256 x 64 tiles) and f32 tokens on plain weights; the first call is
+also checked against the oracle."""
 
 import numpy as np
 import pytest
@@ -38,9 +39,13 @@ def _host(out):
         else bf16_host_f64(out)
 
 
-@pytest.mark.parametrize("x_dtype,layout", [("bf16", "packed"), ("f32", "plain")])
-def test_noalloc_matches_moe_forward(moe, dev, x_dtype, layout):
-    for i, T in enumerate([600, 100]):          # the second call is smaller
+@pytest.mark.parametrize("x_dtype,layout,sizes", [("bf16", "packed", (2400, 100)),
+                                                  ("bf16", "packed", (600, 100)),
+                                                  ("f32", "plain", (600, 100))])
+def test_noalloc_matches_moe_forward(moe, dev, x_dtype, layout, sizes):
+    if x_dtype == "bf16" and sizes[0] == 2400:
+        assert moe.moe_forward_block_m(2400, 32, 4, "bf16", "packed") == 32   # expert-wide
+    for i, T in enumerate(sizes):               # the second call is smaller
         cfg = _cfg(T, i, x_dtype, groups=4, topk_group=2, scale=1.5)
         d = layer_inputs(cfg, dev)
         w1, w2 = d["w1"], d["w2"]

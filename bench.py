@@ -35,11 +35,12 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
-# HBM bytes per launch of the gate_up GEMM (the layer's dominant kernel), from rocprofv3
-# FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy (see the profile summary of the prefill
-# layer).  Only valid for that kernel configuration; None for any other block size or once the
-# kernel has changed since the counters were taken.
-GATE_UP_TRAFFIC = {"block_m": 32, "bytes": None}
+# HBM bytes per launch of the gate_up GEMM (the layer's dominant kernel, expert-wide tiles at
+# block 32), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy: 915,874 KiB
+# read + 49,152 KiB written (profiles/prefill_layer_wide_tiles.md).  Only valid for that kernel
+# configuration; None for any other block size or once the kernel has changed since the
+# counters were taken.
+GATE_UP_TRAFFIC = {"block_m": 32, "bytes": 988186624}
 
 
 def log(msg):
@@ -91,8 +92,8 @@ def flushed_events(torch, fn, reps, flush):
 def calibrate(torch, dev, timer):
     """Ceilings measured on this GPU, for context: hipBLASLt bf16 GEMMs (a
     dense 8192^3 and the prefill gate_up as one batched GEMM of 128 experts x
-    256 tokens x 1536 x 2048) and a 1 GiB device copy.  Run before the timed
-    layer, they also bring the GPU clock up."""
+    256 tokens x 1536 x 2048) and a 1 GiB device copy.  Run right before the
+    timed layer's warm-up, they also bring the GPU clock up."""
     res = {}
     a = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
     b = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
@@ -188,7 +189,10 @@ def w8a8_weights(torch, moe, w1, w2):
     return p1, s1, p2, s2
 
 
-def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
+def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True, before=None):
+    """The prefill layer.  before() runs right before the warm-up steps (the
+    calibration GEMMs: GPU work that brings the clock up after the host-side
+    set-up, so that a short timed region starts at the steady clock)."""
     import synth
     cfg = synth.CONFIGS["prefill"]
     T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
@@ -200,9 +204,11 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True):
     def step():
         moe.moe_forward(x, g, w1, w2, K, out=out, workspace=ws)
 
+    before_res = before() if before is not None else None
     ms = wall_steps(torch, step, steps, warmup)
     flops = 6.0 * T * K * H * I
-    res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops, pack_weights_ms=pack_ms)
+    res = dict(ms=ms, tflops=flops / ms * 1e-9, flops=flops, pack_weights_ms=pack_ms,
+               before=before_res)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     fl = flushed_events(torch, step, max(steps, 10), flush)
     fl["tflops"] = flops / fl["mean_ms"] * 1e-9
@@ -519,10 +525,10 @@ def main():
                           "warmup": args.warmup, "result": res}), flush=True)
         return
 
-    log("calibration (hipBLASLt GEMMs, device copy)")
-    calib = calibrate(torch, dev, timer)
-    log("prefill layer")
-    pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain)
+    log("prefill layer (calibration GEMMs and copy right before its warm-up)")
+    pre = bench_prefill(torch, moe, dev, args.steps, args.warmup, timer, plain=not args.no_plain,
+                        before=lambda: calibrate(torch, dev, timer))
+    calib = pre["before"]
     g1 = pre["breakdown"]["gemm1_gate_up_silu"]
     # MFMA is the graded bound; at this shape HBM co-binds (206 GFLOP over
     # 872 MB of weights, tokens and h: 236 FLOP/B, under the 315 FLOP/B

@@ -38,6 +38,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -1361,34 +1363,38 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
   const int chunk_pos = lane & 3;
   const int nw = kWideWP, ntw = __builtin_amdgcn_readfirstlane(src.nt);
 
-  auto issue_t = [&](int kt) {
-    const uint32_t st = tbase + (uint32_t)((kt % kWideNT) * kWideTStage);
-    const int64_t koff = (int64_t)kt * kWideRowB;
-#pragma unroll
-    for (int i = 0; i < kWideTP; ++i) {
-      if (i < ntw) {
-        const int row = (int)(src.tlds[i] / kWideRowB) + (lane >> 2);
-        const int c = chunk_pos ^ ((row >> 2) & 3);
-        const int64_t off = koff + c * 16 < kbytes ? koff + c * 16 : 0;   // past K: row start
-        dma16(__builtin_amdgcn_readfirstlane(st + src.tlds[i]), src.t[i] + off);
-      }
+  // token piece i of stage kt (if this wave has it)
+  auto issue_t1 = [&](int kt, int i) {
+    if (i < ntw) {
+      const uint32_t st = tbase + (uint32_t)((kt % kWideNT) * kWideTStage);
+      const int64_t koff = (int64_t)kt * kWideRowB;
+      const int row = (int)(src.tlds[i] / kWideRowB) + (lane >> 2);
+      const int c = chunk_pos ^ ((row >> 2) & 3);
+      const int64_t off = koff + c * 16 < kbytes ? koff + c * 16 : 0;   // past K: row start
+      dma16(__builtin_amdgcn_readfirstlane(st + src.tlds[i]), src.t[i] + off);
     }
   };
-  auto issue_w = [&](int kt) {
+  // weight piece i of stage kt
+  auto issue_w1 = [&](int kt, int i) {
     const uint32_t st = wbase + (uint32_t)((kt % kWideNW) * kWideWStage);
     const int64_t koff = (int64_t)kt * kWideRowB;
-#pragma unroll
-    for (int i = 0; i < kWideWP; ++i) {
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + src.wlds[i]);
-      if (src.packed) {
-        const uint8_t* g = src.w[i] + (int64_t)kt * kPackBlockBytes;
-        if (src.stream) dma16_nt(m0, g); else dma16(m0, g);
-      } else {
-        const int row = (int)(src.wlds[i] / kWideRowB) + (lane >> 2);
-        const int c = chunk_pos ^ ((row >> 2) & 3);
-        dma16(m0, src.w[i] + (koff + c * 16 < kbytes ? koff + c * 16 : 0));
-      }
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(st + src.wlds[i]);
+    if (src.packed) {
+      const uint8_t* g = src.w[i] + (int64_t)kt * kPackBlockBytes;
+      if (src.stream) dma16_nt(m0, g); else dma16(m0, g);
+    } else {
+      const int row = (int)(src.wlds[i] / kWideRowB) + (lane >> 2);
+      const int c = chunk_pos ^ ((row >> 2) & 3);
+      dma16(m0, src.w[i] + (koff + c * 16 < kbytes ? koff + c * 16 : 0));
     }
+  };
+  auto issue_t = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < kWideTP; ++i) issue_t1(kt, i);
+  };
+  auto issue_w = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < kWideWP; ++i) issue_w1(kt, i);
   };
   // zero the chunks of a partial stage that lie past K (after its loads landed)
   auto zero_tail = [&](int kt) {
@@ -1457,31 +1463,54 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
     for (int cb = 0; cb < NCB; ++cb)
       bf[cb] = *reinterpret_cast<const u32x4_t*>(ts + (tcol0 + cb * 32) * kWideRowB + pos);
   };
-  auto mfmas = [&](const u32x4_t (&af)[kWideRB], const u32x4_t (&bf)[kWideCB]) {
+  // The MFMAs of one K step, token block by token block; after block cb the
+  // load pieces that the schedule puts there (pw: weight piece, pt: token
+  // piece, -1 none).  The scheduling barriers keep the order.
+  auto step = [&](const u32x4_t (&af)[kWideRB], const u32x4_t (&bf)[kWideCB], int kw, int ktk,
+                  auto sched) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int cb = 0; cb < (NCB > 0 ? NCB : 1); ++cb) {
+      if (cb < NCB) {
 #pragma unroll
-      for (int rb = 0; rb < kWideRB; ++rb) acc[rb][cb] = Mma<0>::run(af[rb], bf[cb], acc[rb][cb]);
+        for (int rb = 0; rb < kWideRB; ++rb) acc[rb][cb] = Mma<0>::run(af[rb], bf[cb], acc[rb][cb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      sched(cb, kw, ktk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // K step 0 of a stage carries the weight pieces, step 1 the token pieces,
+  // one after each of the first token blocks (all after the last block when
+  // the wave has fewer blocks than pieces)
+  constexpr int kLast = (NCB > 0 ? NCB : 1) - 1;
+  auto sched_w = [&](int cb, int kw, int) {
+#pragma unroll
+    for (int i = 0; i < kWideWP; ++i)
+      if (kw >= 0 && (i < kLast ? cb == i : cb == kLast)) issue_w1(kw, i);
+  };
+  auto sched_t = [&](int cb, int, int ktk) {
+#pragma unroll
+    for (int i = 0; i < kWideTP; ++i)
+      if (ktk >= 0 && (i < kLast ? cb == i : cb == kLast)) issue_t1(ktk, i);
   };
   // one set of fragments (the accumulators take most of the registers; the
   // other wave on the SIMD covers the LDS latency)
   u32x4_t af[kWideRB], bf[kWideCB];
   publish(0);
-  // the first fragments go out before the refills, whose address arithmetic
-  // then runs under their LDS latency
   load_frags(0, 0, af, bf);
-  if (kWideNW - 1 < nk) issue_w(kWideNW - 1);
-  if (kWideNT - 1 < nk) issue_t(kWideNT - 1);
+  // Iteration kt refills the buffers of stage kt - 1 (every wave left them
+  // at the barrier before it) with W(kt + NW - 1), then T(kt + NT - 1).  The
+  // loads go out one by one between the MFMAs: when the memory queues are
+  // full a load waits at issue, and the MFMAs already issued keep the matrix
+  // core busy meanwhile (issued in one burst after the barrier, the loads
+  // held every wave of the CU at once).
   for (int kt = 0; kt < nk; ++kt) {
-    mfmas(af, bf);
+    step(af, bf, kt + kWideNW - 1 < nk ? kt + kWideNW - 1 : -1, -1, sched_w);
     load_frags(kt, 1, af, bf);
-    mfmas(af, bf);
+    step(af, bf, -1, kt + kWideNT - 1 < nk ? kt + kWideNT - 1 : -1, sched_t);
     if (kt + 1 < nk) {
       publish(kt + 1);
       load_frags(kt + 1, 0, af, bf);
-      // every wave has finished reading stage kt: refill its buffers
-      if (kt + kWideNW < nk) issue_w(kt + kWideNW);
-      if (kt + kWideNT < nk) issue_t(kt + kWideNT);
     }
   }
 }

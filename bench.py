@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 # read + 49,152 KiB written (profiles/prefill_layer_wide_tiles.md).  Only valid for that kernel
 # configuration; None for any other block size or once the kernel has changed since the
 # counters were taken.
-GATE_UP_TRAFFIC = {"block_m": 32, "bytes": 988186624}
+GATE_UP_TRAFFIC = {"block_m": 32, "bytes": None}
 
 
 def log(msg):

@@ -1,9 +1,16 @@
 """Build libmoe.so (the HIP library behind include/moe.h) for gfx950, in-tree.
 
 Every call recompiles: one hipcc per source in parallel, then a shared link.
+The compiler's per-kernel resource report is checked: a kernel that uses
+scratch memory (VGPR spills, private arrays) fails the build.  The
+direct-to-LDS GEMM loops count their own outstanding loads in their waits,
+and a scratch load or store would fall between those loads unseen by the
+counts.  SGPR spills are allowed: they go to VGPR lanes, not to memory
+(the report shows ScratchSize 0 for them).
 """
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -40,10 +47,15 @@ def build(verbose=False):
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
 
     def compile_one(i):
-        return _run([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
+        return _run([HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                                       os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         logs = list(ex.map(compile_one, range(len(SOURCES))))
+    spills = check_scratch(logs)
+    if spills:
+        raise RuntimeError("kernels use scratch memory:\n" + "\n".join(spills))
+    logs = [strip_remarks(l) for l in logs]
     tmp = LIB + ".tmp"
     logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
     os.replace(tmp, LIB)
@@ -52,6 +64,39 @@ def build(verbose=False):
             if l.strip():
                 print(l)
     return LIB
+
+
+_FN = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark: +(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)")
+
+
+def check_scratch(logs):
+    """Kernels whose resource report shows VGPR spills or scratch memory."""
+    bad = []
+    for log in logs:
+        fn = None
+        for line in log.splitlines():
+            m = _FN.search(line)
+            if m:
+                fn = m.group(1)
+                continue
+            m = _SCRATCH.search(line)
+            if m and int(m.group(2)) > 0:
+                bad.append("%s: %s %s" % (fn, m.group(1), m.group(2)))
+    return bad
+
+
+def strip_remarks(log):
+    keep, skip = [], False
+    for line in log.splitlines():
+        if "remark:" in line:
+            skip = True
+            continue
+        if skip and (line.startswith(" ") or not line.strip()):
+            continue   # source excerpt under a remark
+        skip = False
+        keep.append(line)
+    return "\n".join(keep)
 
 
 if __name__ == "__main__":

@@ -356,3 +356,22 @@ def test_wide_gemm_validation(mod):
     assert call(bl=2) == d["MOE_ERR_CONFIG"]
     assert call(K=100) == d["MOE_ERR_SHAPE"]
     assert call(table=None) == d["MOE_ERR_NULL"]
+
+
+def test_build_rejects_scratch_use():
+    """build.py fails on any kernel whose resource report shows VGPR spills or
+    scratch memory (the GEMM loops' load counts assume no scratch traffic);
+    SGPR spills, which stay in VGPR lanes, pass."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "moe_build", os.path.join(ROOT, "moe_grouped_topk_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    tag = " [-Rpass-analysis=kernel-resource-usage]"
+    log = "\n".join("k.hip:1:2: remark: " + l + tag for l in [
+        "Function Name: kA", "    ScratchSize [bytes/lane]: 0", "    SGPRs Spill: 30",
+        "    VGPRs Spill: 0",
+        "Function Name: kB", "    ScratchSize [bytes/lane]: 32", "    VGPRs Spill: 7"])
+    bad = b.check_scratch([log])
+    assert bad == ["kB: ScratchSize [bytes/lane] 32", "kB: VGPRs Spill 7"]
+    assert b.check_scratch([log.split("Function Name: kB")[0]]) == []

@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(kPlaceThreads)
 align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, int chunk, int nchunk,
                    const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
                    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out,
-                   int max_padded) {
+                   int max_padded, int32_t* __restrict__ wide_table) {
   extern __shared__ int smem[];
   int* seg = smem;                               // [E + 1] segment starts
   int* cur = seg + (E + 1);                      // [kPlaceWaves][E] per-wave cursors
@@ -390,6 +390,34 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
   if (tid == 0) seg[E] = total;
   for (int i = tid; i < kPlaceWaves * E; i += kPlaceThreads) cur[i] = 0;
   __syncthreads();
+
+  // The first chunk also writes the expert-wide tile table: each expert's
+  // blocks in ceil(n / kWideMaxBlocks) runs of near-equal length.
+  if (wide_table && c == 0) {
+    int nb[2], nt[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      nb[q] = padded[q] / B;
+      nt[q] = (nb[q] + kWideMaxBlocks - 1) / kWideMaxBlocks;
+    }
+    int ntiles;
+    int j = place_exclusive_scan(nt[0] + nt[1], tmp, ntiles);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      if (e < E) {
+        const int first = seg[e] / B;
+        for (int i = 0; i < nt[q]; ++i, ++j) {
+          const int b0 = first + (int)((int64_t)i * nb[q] / nt[q]);
+          const int b1 = first + (int)((int64_t)(i + 1) * nb[q] / nt[q]);
+          wide_table[1 + 3 * j] = e;
+          wide_table[2 + 3 * j] = b0;
+          wide_table[3 + 3 * j] = b1 - b0;
+        }
+      }
+    }
+    if (tid == 0) wide_table[0] = ntiles;
+  }
 
   // per-wave counts of this chunk, then each wave's first slot per expert
   const int c0 = c * chunk, c1 = min(P, c0 + chunk);
@@ -497,7 +525,9 @@ size_t align_ws_bytes(int64_t P, int E) {
 
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
-                           hipStream_t stream) {
+                           hipStream_t stream, int32_t* wide_table) {
+  if (wide_table && (B != kWideBlockRows || E > kWidePrepMaxExperts || E > 2 * kPlaceThreads))
+    return hipErrorInvalidValue;
   const int64_t chunk = align_ws_chunk(P);
   const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
   hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
@@ -512,7 +542,7 @@ hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int
   }
   hipLaunchKernelGGL(align_place_kernel, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
                      (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
-                     (int)max_padded);
+                     (int)max_padded, wide_table);
   return hipGetLastError();
 }
 

@@ -447,8 +447,9 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
     a.w1 = w1; a.w2 = w2; a.out = out; a.T = T; a.H = H; a.I = I; a.topk = topk;
     return hip_status(moe::launch_small_layer(a, s));
   }
+  int32_t* table = L.wide ? reinterpret_cast<int32_t*>(base + L.table) : nullptr;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
-                             reinterpret_cast<int32_t*>(base + L.hist), s);
+                             reinterpret_cast<int32_t*>(base + L.hist), s, table);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
   moe::MoeGemmArgs g1{};
@@ -468,10 +469,8 @@ int forward_impl(const void* x, int32_t x_dtype, const float* gating, const void
   st = check_gemm(g2, L.wide);
   if (st != MOE_OK) return st;
 
-  if (L.wide) {
-    int32_t* table = reinterpret_cast<int32_t*>(base + L.table);
-    err = moe::launch_wide_prep(eids, total, E, L.max_padded, table, s);
-    if (err == hipSuccess) err = moe::launch_moe_gemm_wide(g1, table, s);
+  if (L.wide) {   // the alignment wrote the tile table
+    err = moe::launch_moe_gemm_wide(g1, table, s);
     if (err == hipSuccess) err = moe::launch_moe_gemm_wide(g2, table, s);
     if (err != hipSuccess) return hip_status(err);
   } else {

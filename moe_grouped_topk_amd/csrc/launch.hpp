@@ -33,9 +33,12 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
 // The same alignment in two kernels (per-chunk counts, then placement),
 // with a workspace of align_ws_bytes(P, E) bytes for the counts.
 size_t align_ws_bytes(int64_t P, int E);
+// With wide_table (B = kWideBlockRows, E <= kWidePrepMaxExperts), the placement
+// kernel also writes the expert-wide tile table (the layout launch_wide_prep
+// writes), from the per-expert segment sizes it computes anyway.
 hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int32_t* sorted_ids,
                            int32_t* expert_ids, int32_t* total, int64_t max_padded, int32_t* hist,
-                           hipStream_t stream);
+                           hipStream_t stream, int32_t* wide_table = nullptr);
 
 // Packed expert weights (see moe_pack_weights in moe.h): tiles of 256 rows,
 // K stages of 64 bytes, one 16 KiB block per (expert, tile, stage).
@@ -86,8 +89,17 @@ hipError_t launch_moe_gemm_tile(const MoeGemmArgs& a, hipStream_t stream);
 
 // Expert-wide tiles (bf16 tokens and h, block_m 32): a tile table of
 // wide_table_ints(max_padded) ints built from the alignment by
-// launch_wide_prep, then one launch per GEMM (gate_up with SiLU*up into h
-// in sorted order; down with the routing weight into pair rows).
+// launch_wide_prep (or by launch_align_ws itself), then one launch per GEMM
+// (gate_up with SiLU*up into h in sorted order; down with the routing weight
+// into pair rows).  Table: t[0] = number of tiles; tile j: t[1 + 3j] =
+// expert, t[2 + 3j] = first block, t[3 + 3j] = blocks; an expert of n blocks
+// gets ceil(n / kWideMaxBlocks) tiles, tile i of its t tiles starting at
+// block first + floor(i * n / t).
+#ifndef MOE_WIDE_MAXBLK
+#define MOE_WIDE_MAXBLK 10
+#endif
+constexpr int kWideBlockRows = 32;
+constexpr int kWideMaxBlocks = MOE_WIDE_MAXBLK;
 constexpr int kWidePrepMaxExperts = 1024;
 int64_t wide_table_ints(int64_t max_padded);
 hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int E,

@@ -1251,12 +1251,9 @@ gmm_i8_tile_kernel(GmmI8Args a) {
 #ifndef MOE_WIDE_NT
 #define MOE_WIDE_NT 4
 #endif
-#ifndef MOE_WIDE_MAXBLK
-#define MOE_WIDE_MAXBLK 10
-#endif
 constexpr int kWideBN = 256;
-constexpr int kWideBlk = 32;
-constexpr int kWideMaxBlk = MOE_WIDE_MAXBLK;
+constexpr int kWideBlk = kWideBlockRows;
+constexpr int kWideMaxBlk = kWideMaxBlocks;
 constexpr int kWideBM = kWideBlk * kWideMaxBlk;            // token rows of a full tile
 constexpr int kWideWN = 4, kWideWM = 2, kWideThreads = 64 * kWideWN * kWideWM;
 constexpr int kWideNW = MOE_WIDE_NW, kWideNT = MOE_WIDE_NT;

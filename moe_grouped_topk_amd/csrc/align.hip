@@ -301,6 +301,7 @@ align_expert_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B,
 constexpr int kCountThreads = 256;
 constexpr int kPlaceThreads = 512;
 constexpr int kPlaceWaves = kPlaceThreads / kWave;
+constexpr int64_t kAlignSelfPairs = 2048;   // one chunk of the two-kernel path
 
 __global__ void __launch_bounds__(kCountThreads)
 align_count_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int chunk,
@@ -352,6 +353,10 @@ __device__ __forceinline__ int place_exclusive_scan(int v, int* tmp, int& total)
   return before + x - v;
 }
 
+// SELF: one workgroup takes every pair (c = 0, chunk = P) and counts the
+// experts itself from its per-wave counts, without a count kernel's
+// histogram (hist is not read).
+template <bool SELF>
 __global__ void __launch_bounds__(kPlaceThreads)
 align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, int chunk, int nchunk,
                    const int32_t* __restrict__ hist, int32_t* __restrict__ sorted_ids,
@@ -365,22 +370,66 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int c = blockIdx.x;
 
+  // this wave's run of the chunk, read once into registers kR ids per lane
+  // at a time when it is short
+  const int c0 = c * chunk, c1 = min(P, c0 + chunk);
+  const int run = (chunk + kPlaceWaves * kWave - 1) / (kPlaceWaves * kWave) * kWave;
+  const int r0 = min(c1, c0 + wave * run), r1 = min(c1, r0 + run);
+  constexpr int kR = 4;
+  const bool one_batch = r1 - r0 <= kR * kWave;
+  int v[kR];
+  // per-wave counts of this chunk
+  auto count_runs = [&]() {
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      const int i = r0 + j * kWave + lane;
+      v[j] = i < r1 ? topk_ids[i] : -1;
+    }
+    if (one_batch) {
+#pragma unroll
+      for (int j = 0; j < kR; ++j)
+        if (v[j] >= 0 && v[j] < E) atomicAdd(&cur[wave * E + v[j]], 1);
+    } else {
+      for (int i = r0 + lane; i < r1; i += kWave) {
+        const int e = topk_ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cur[wave * E + e], 1);
+      }
+    }
+  };
+
   // totals, and pairs of each expert in the chunks before this one
   int padded[2] = {0, 0}, before_c[2] = {0, 0};
+  if constexpr (SELF) {
+    for (int i = tid; i < kPlaceWaves * E; i += kPlaceThreads) cur[i] = 0;
+    __syncthreads();
+    count_runs();
+    __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * tid + q;
-    if (e < E) {
-      int t = 0, b = 0;
-#pragma unroll 16
-      for (int cc = 0; cc < nchunk; ++cc) {   // independent loads, issued together
-        const int h = hist[(int64_t)cc * E + e];
-        t += h;
-        b += cc < c ? h : 0;
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      if (e < E) {
+        int t = 0;
+        for (int w = 0; w < kPlaceWaves; ++w) t += cur[w * E + e];
+        tot[e] = t;
+        padded[q] = (t + B - 1) / B * B;
       }
-      tot[e] = t;
-      padded[q] = (t + B - 1) / B * B;
-      before_c[q] = b;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      if (e < E) {
+        int t = 0, b = 0;
+#pragma unroll 16
+        for (int cc = 0; cc < nchunk; ++cc) {   // independent loads, issued together
+          const int h = hist[(int64_t)cc * E + e];
+          t += h;
+          b += cc < c ? h : 0;
+        }
+        tot[e] = t;
+        padded[q] = (t + B - 1) / B * B;
+        before_c[q] = b;
+      }
     }
   }
   int total;
@@ -388,7 +437,8 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
   if (2 * tid < E) seg[2 * tid] = start;
   if (2 * tid + 1 < E) seg[2 * tid + 1] = start + padded[0];
   if (tid == 0) seg[E] = total;
-  for (int i = tid; i < kPlaceWaves * E; i += kPlaceThreads) cur[i] = 0;
+  if constexpr (!SELF)
+    for (int i = tid; i < kPlaceWaves * E; i += kPlaceThreads) cur[i] = 0;
   __syncthreads();
 
   // The first chunk also writes the expert-wide tile table: each expert's
@@ -419,30 +469,12 @@ align_place_kernel(const int32_t* __restrict__ topk_ids, int P, int E, int B, in
     if (tid == 0) wide_table[0] = ntiles;
   }
 
-  // per-wave counts of this chunk, then each wave's first slot per expert
-  const int c0 = c * chunk, c1 = min(P, c0 + chunk);
-  const int run = (chunk + kPlaceWaves * kWave - 1) / (kPlaceWaves * kWave) * kWave;
-  const int r0 = min(c1, c0 + wave * run), r1 = min(c1, r0 + run);
-  // the wave's run is read once into registers, kR ids per lane at a time
-  constexpr int kR = 4;
-  const bool one_batch = r1 - r0 <= kR * kWave;
-  int v[kR];
-#pragma unroll
-  for (int j = 0; j < kR; ++j) {
-    const int i = r0 + j * kWave + lane;
-    v[j] = i < r1 ? topk_ids[i] : -1;
+  // per-wave counts of this chunk (already taken in SELF mode), then each
+  // wave's first slot per expert
+  if constexpr (!SELF) {
+    count_runs();
+    __syncthreads();
   }
-  if (one_batch) {
-#pragma unroll
-    for (int j = 0; j < kR; ++j)
-      if (v[j] >= 0 && v[j] < E) atomicAdd(&cur[wave * E + v[j]], 1);
-  } else {
-    for (int i = r0 + lane; i < r1; i += kWave) {
-      const int e = topk_ids[i];
-      if (e >= 0 && e < E) atomicAdd(&cur[wave * E + e], 1);
-    }
-  }
-  __syncthreads();
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * tid + q;
@@ -528,19 +560,28 @@ hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int
                            hipStream_t stream, int32_t* wide_table) {
   if (wide_table && (B != kWideBlockRows || E > kWidePrepMaxExperts || E > 2 * kPlaceThreads))
     return hipErrorInvalidValue;
-  const int64_t chunk = align_ws_chunk(P);
+  // Up to kAlignSelfPairs pairs one workgroup counts and places them all;
+  // beyond, per-chunk counts first, then placement by every chunk.
+  const bool self = P <= kAlignSelfPairs;
+  const int64_t chunk = self ? (P > 0 ? P : 1) : align_ws_chunk(P);
   const int nchunk = P > 0 ? (int)((P + chunk - 1) / chunk) : 1;
-  hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
-                     stream, topk_ids, (int)P, E, (int)chunk, hist);
-  hipError_t st = hipGetLastError();
-  if (st != hipSuccess) return st;
-  const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
-  if (lds > 65536) {
-    st = hipFuncSetAttribute((const void*)align_place_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t st;
+  if (!self) {
+    hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kCountThreads), sizeof(int) * E,
+                       stream, topk_ids, (int)P, E, (int)chunk, hist);
+    st = hipGetLastError();
     if (st != hipSuccess) return st;
   }
-  hipLaunchKernelGGL(align_place_kernel, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
+  void (*place)(const int32_t*, int, int, int, int, int, const int32_t*, int32_t*, int32_t*,
+                int32_t*, int, int32_t*) =
+      self ? align_place_kernel<true> : align_place_kernel<false>;
+  const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
+  if (lds > 65536) {
+    st = hipFuncSetAttribute((const void*)place, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+    if (st != hipSuccess) return st;
+  }
+  hipLaunchKernelGGL(place, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
                      (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
                      (int)max_padded, wide_table);
   return hipGetLastError();

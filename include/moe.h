@@ -378,7 +378,10 @@ MOE_API int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int6
  *   moe_pack_weights(MOE_DTYPE_I8, MOE_EPILOGUE_SILU_MUL) and w2q with
  *   MOE_EPILOGUE_NONE.
  *   x [T, H] bf16 or f32; out [T, H] in x's dtype.
- *   block_m  0 (chosen, at least 64) or 64, 128, 256.
+ *   block_m  0 (chosen: 32, the expert-wide int8 tiles, for bf16 x at 96 or
+ *            more pairs per expert and E <= 1024, else at least 64), 32
+ *            (bf16 x only), 64, 128 or 256.  The expert-wide tiles give the
+ *            same bits as the 256 x 128 / 256 x 64 tiles (exact int32 sums).
  *   ws       at least moe_forward_w8a8_workspace_size(...) bytes, 256-byte
  *            aligned.
  * Requirements: H % 16 == 0, I % 16 == 0, H and I <= 131072, plus

@@ -71,7 +71,7 @@ int check_gemm(const moe::MoeGemmArgs& a, bool wide = false) {
   if (a.a_dtype != MOE_DTYPE_F32 && a.a_dtype != MOE_DTYPE_BF16 && a.a_dtype != MOE_DTYPE_I8)
     return MOE_ERR_DTYPE;
   if (a.a_dtype == MOE_DTYPE_I8) {   // int8 tokens and weights (moe_forward_w8a8)
-    if (a.block_m < 64 || !a.a_scales || !a.b_scales) return MOE_ERR_CONFIG;
+    if ((a.block_m < 64 && !wide) || !a.a_scales || !a.b_scales) return MOE_ERR_CONFIG;
     if (a.c_dtype != MOE_DTYPE_F32 && a.c_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
     if (a.K % 16 != 0 || a.lda % 16 != 0) return MOE_ERR_SHAPE;
     if (!aligned16(a.b_scales)) return MOE_ERR_SHAPE;
@@ -177,15 +177,16 @@ ForwardLayout forward_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
 
 // Workspace of moe_forward_w8a8 (256-byte aligned pieces).
 struct W8a8Layout {
-  size_t w, ids, sorted, eids, total, hist, xq, sx, h, hq, sh, y, bytes;
+  size_t w, ids, sorted, eids, total, hist, xq, sx, h, hq, sh, y, table, bytes;
   int64_t max_padded;
   int block_m;
+  bool wide;    // bf16 x at block 32: expert-wide int8 tiles from a tile table
 };
 
 W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t block_m,
                        int32_t x_dtype) {
   W8a8Layout L{};
-  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, MOE_WEIGHTS_PACKED, false);
+  L.block_m = block_m ? block_m : choose_block_m(T, E, topk, x_dtype, MOE_WEIGHTS_PACKED);
   const int64_t P = T * topk;
   L.max_padded = align_max_padded(P, E, L.block_m);
   size_t off = 0;
@@ -202,6 +203,8 @@ W8a8Layout w8a8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
   L.hq = take((size_t)L.max_padded * (size_t)I);
   L.sh = take(sizeof(float) * (size_t)L.max_padded);
   L.y = take((x_dtype == MOE_DTYPE_F32 ? 4 : 2) * (size_t)P * (size_t)H);
+  L.wide = use_wide(L.block_m, x_dtype, E);
+  if (L.wide) L.table = take(sizeof(int32_t) * (size_t)moe::wide_table_ints(L.max_padded));
   L.bytes = off;
   return L;
 }
@@ -522,7 +525,7 @@ int moe_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols
 size_t moe_forward_w8a8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                        int32_t block_m) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
-  if (block_m != 0 && (!valid_block_m(block_m) || block_m < 64)) return 0;
+  if (block_m != 0 && (!valid_block_m(block_m) || (block_m < 64 && block_m != 32))) return 0;
   size_t most = 0;
   for (int32_t dt : {MOE_DTYPE_BF16, MOE_DTYPE_F32}) {
     const size_t b = w8a8_layout(T, H, I, E, topk, block_m, dt).bytes;
@@ -540,7 +543,9 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
                      void* stream) {
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (!valid_layout(w_layout)) return MOE_ERR_CONFIG;
-  if (block_m != 0 && (!valid_block_m(block_m) || block_m < 64)) return MOE_ERR_CONFIG;
+  if (block_m != 0 &&
+      (!valid_block_m(block_m) || (block_m < 64 && !use_wide(block_m, x_dtype, E))))
+    return MOE_ERR_CONFIG;
   if (H < 16 || H % 16 != 0 || I < 16 || I % 16 != 0 || H > 131072 || I > 131072)
     return MOE_ERR_SHAPE;
   int st = check_route_shape(T, E, topk, num_expert_group, topk_group, scoring);
@@ -579,14 +584,14 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   g1.block_m = L.block_m; g1.num_valid = P; g1.topk_weights = nullptr;
   g1.epilogue = MOE_EPILOGUE_SILU_MUL; g1.C = h; g1.c_dtype = MOE_DTYPE_BF16; g1.ldc = I;
   g1.c_rows = MOE_ROWS_SORTED;
-  st = check_gemm(g1);
+  st = check_gemm(g1, L.wide);
   if (st != MOE_OK) return st;
   moe::MoeGemmArgs g2 = g1;
   g2.A = hq; g2.lda = I; g2.a_rows = MOE_ROWS_SORTED; g2.a_row_div = 1; g2.a_scales = sh;
   g2.B = w2q; g2.b_scales = w2_scales; g2.N = H; g2.K = I; g2.topk_weights = w;
   g2.epilogue = MOE_EPILOGUE_NONE; g2.C = y; g2.c_dtype = x_dtype; g2.ldc = H;
   g2.c_rows = MOE_ROWS_PAIR;
-  st = check_gemm(g2);
+  st = check_gemm(g2, L.wide);
   if (st != MOE_OK) return st;
 
   // routing also quantises each token's x row as it loads it (one wave per
@@ -595,14 +600,15 @@ int moe_forward_w8a8(const void* x, int32_t x_dtype, const float* gating, const 
   hipError_t err = moe::launch_route(gating, T, E, topk, num_expert_group, topk_group, scoring,
                                      renormalize ? 1 : 0, routed_scaling_factor, w, ids, s, &rx);
   if (err != hipSuccess) return MOE_ERR_HIP;
+  int32_t* table = L.wide ? reinterpret_cast<int32_t*>(base + L.table) : nullptr;
   err = moe::launch_align_ws(ids, P, E, L.block_m, sorted, eids, total, L.max_padded,
-                             reinterpret_cast<int32_t*>(base + L.hist), s);
+                             reinterpret_cast<int32_t*>(base + L.hist), s, table);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  st = enqueue_gemm(g1, s);
+  st = L.wide ? hip_status(moe::launch_moe_gemm_wide(g1, table, s)) : enqueue_gemm(g1, s);
   if (st != MOE_OK) return st;
   err = moe::launch_quantize_rows(h, MOE_DTYPE_BF16, L.max_padded, I, I, sorted, total, P, hq, sh, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  st = enqueue_gemm(g2, s);
+  st = L.wide ? hip_status(moe::launch_moe_gemm_wide(g2, table, s)) : enqueue_gemm(g2, s);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_topk_reduce(y, x_dtype, T, topk, H, out, x_dtype, s));
 }

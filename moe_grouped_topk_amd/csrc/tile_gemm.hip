@@ -1350,10 +1350,10 @@ __device__ __forceinline__ void wide_wait(int n) {
 
 // K loop of a wide tile: stages [0, nk) of kbytes bytes of K.  ncb: this
 // wave's token blocks (its accumulators beyond them stay untouched).
-template <int NCB>
+template <int KIND, int NCB>
 __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src, int64_t kbytes,
                                               const int (&wrow)[kWideRB], int tcol0,
-                                              f32x16_t (&acc)[kWideRB][kWideCB]) {
+                                              typename Mma<KIND>::acc_t (&acc)[kWideRB][kWideCB]) {
   const int tid = tile_tid(), lane = tid & 63;
   const uint32_t wbase = lds_addr(smem), tbase = wbase + kWideNW * kWideWStage;
   const int nk = (int)((kbytes + kWideRowB - 1) / kWideRowB);
@@ -1469,7 +1469,7 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
     for (int cb = 0; cb < (NCB > 0 ? NCB : 1); ++cb) {
       if (cb < NCB) {
 #pragma unroll
-        for (int rb = 0; rb < kWideRB; ++rb) acc[rb][cb] = Mma<0>::run(af[rb], bf[cb], acc[rb][cb]);
+        for (int rb = 0; rb < kWideRB; ++rb) acc[rb][cb] = Mma<KIND>::run(af[rb], bf[cb], acc[rb][cb]);
       }
       __builtin_amdgcn_sched_barrier(0);
       sched(cb, kw, ktk);
@@ -1513,25 +1513,31 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
 }
 
 // Runs the K loop specialised for this wave's number of token blocks.
+template <int KIND>
 __device__ __forceinline__ void wide_mainloop_live(uint8_t* smem, const WideSrc& src,
                                                    int64_t kbytes, const int (&wrow)[kWideRB],
                                                    int tcol0, int ncb,
-                                                   f32x16_t (&acc)[kWideRB][kWideCB]) {
+                                                   typename Mma<KIND>::acc_t (&acc)[kWideRB][kWideCB]) {
+  static_assert(kWideCB <= 5, "wide_mainloop_live dispatches up to 5 token blocks");
   switch (__builtin_amdgcn_readfirstlane(ncb)) {
-    case 5: return wide_mainloop<5>(smem, src, kbytes, wrow, tcol0, acc);
-    case 4: return wide_mainloop<4>(smem, src, kbytes, wrow, tcol0, acc);
-    case 3: return wide_mainloop<3>(smem, src, kbytes, wrow, tcol0, acc);
-    case 2: return wide_mainloop<2>(smem, src, kbytes, wrow, tcol0, acc);
-    case 1: return wide_mainloop<1>(smem, src, kbytes, wrow, tcol0, acc);
-    default: return wide_mainloop<0>(smem, src, kbytes, wrow, tcol0, acc);
+    case 5: return wide_mainloop<KIND, 5>(smem, src, kbytes, wrow, tcol0, acc);
+    case 4: return wide_mainloop<KIND, 4>(smem, src, kbytes, wrow, tcol0, acc);
+    case 3: return wide_mainloop<KIND, 3>(smem, src, kbytes, wrow, tcol0, acc);
+    case 2: return wide_mainloop<KIND, 2>(smem, src, kbytes, wrow, tcol0, acc);
+    case 1: return wide_mainloop<KIND, 1>(smem, src, kbytes, wrow, tcol0, acc);
+    default: return wide_mainloop<KIND, 0>(smem, src, kbytes, wrow, tcol0, acc);
   }
 }
 
 // EPI 1: gate_up with the SiLU*up epilogue, bf16 h in sorted order;
 // EPI 0: down times the routing weight, bf16 rows in pair order.
-template <int EPI>
+// KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights, exact
+// int32 sums times the row scale (a_scales) and the channel scale (b_scales).
+template <int EPI, int KIND>
 __global__ void __launch_bounds__(kWideThreads, 2)
 moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
+  typedef typename Mma<KIND>::acc_t Acc;
+  constexpr int kElem = KIND ? 1 : 2;                  // bytes per operand element
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int rowinfo[kWideBM];
   const int ntile = moe_ntiles<kWideBN, EPI>(a);
@@ -1566,10 +1572,10 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
   t.solo = 0;
   WideSrc src;
   src.packed = a.b_packed != 0;
-  const int64_t wrow_bytes = a.K * 2;
+  const int64_t wrow_bytes = a.K * kElem;
   const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)e * a.N * wrow_bytes;
   const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
-                      ((int64_t)e * packed_tiles(a.N, EPI) + nt) * packed_kstages(a.K, 2) *
+                      ((int64_t)e * packed_tiles(a.N, EPI) + nt) * packed_kstages(a.K, kElem) *
                           kPackBlockBytes;
   // the only tile that streams this weight slice: non-temporal loads
   src.stream = src.packed && (j == 0 || table[1 + 3 * (j - 1)] != e) &&
@@ -1586,7 +1592,7 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
     }
   }
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
-  const int64_t arow_bytes = a.lda * 2;
+  const int64_t arow_bytes = a.lda * kElem;
   src.nt = 0;
 #pragma unroll
   for (int i = 0; i < kWideTP; ++i) {
@@ -1613,18 +1619,32 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
   float wr = 1.0f;
   if (!EPI && a.topk_weights && tid < nrows && rowinfo[tid] >= 0)
     wr = a.topk_weights[rowinfo[tid]];
-  f32x16_t acc[kWideRB][kWideCB];
+  Acc acc[kWideRB][kWideCB];
 #pragma unroll
   for (int rb = 0; rb < kWideRB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < kWideCB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
-  wide_mainloop_live(smem, src, wrow_bytes, wrow, tcol0, ncb, acc);
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+  wide_mainloop_live<KIND>(smem, src, wrow_bytes, wrow, tcol0, ncb, acc);
 
   // Epilogue through LDS (the drained rings), whole 16-byte pieces of rows.
+  // Scales (int8): the row's a_scales entry and the channel's b_scales entry
+  // (1 for bf16, which leaves the sums' bits as they are).
   const int rsub = 4 * (lane >> 5);
   uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
+  const float* bsc = KIND ? a.b_scales + (int64_t)e * a.N : nullptr;
+  const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
+  auto row_scale = [&](int trow) -> float {   // trow a valid row of the tile
+    if constexpr (KIND == 0) return 1.0f;
+    const int p = rowinfo[trow];
+    if (p < 0) return 0.0f;
+    return a.a_scales[a.a_rows == 0 ? (int64_t)(p / a.a_row_div) : s0 + trow];
+  };
+  auto col_scale = [&](int64_t n) -> f32x4_t {   // channels n .. n + 3
+    if constexpr (KIND == 0) return one4;
+    return *reinterpret_cast<const f32x4_t*>(bsc + (n < a.N ? n : 0));   // past N: never stored
+  };
   if constexpr (EPI) {
     constexpr int HC = kWideBN / 2, PITCH = HC * 2 + 16, LPR = HC * 2 / 16;
     constexpr int RPP = kWideThreads / LPR;
@@ -1634,16 +1654,18 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
 #pragma unroll
     for (int cb = 0; cb < kWideCB; ++cb) {
       if (cb < ncb) {
-        uint8_t* dst = smem + (tcol0 + cb * 32 + (lane & 31)) * PITCH;
+        const int trow = tcol0 + cb * 32 + (lane & 31);
+        const float as = row_scale(trow);
+        uint8_t* dst = smem + trow * PITCH;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = wrow[0] + 8 * g + rsub;
-          const f32x16_t& gt = acc[0][cb];
-          const f32x16_t& up = acc[1][cb];
+          const int64_t n = t.c0 + col;                // output column (gate row n, up row Nout + n)
+          const f32x4_t gt = acc4(acc[0][cb], g, as, col_scale(n));
+          const f32x4_t up = acc4(acc[1][cb], g, as, col_scale(n < Nout ? Nout + n : a.N));
           *reinterpret_cast<uint2*>(dst + col * 2) = make_uint2(
-              pack_bf16x2(silu_f32(gt[4 * g]) * up[4 * g], silu_f32(gt[4 * g + 1]) * up[4 * g + 1]),
-              pack_bf16x2(silu_f32(gt[4 * g + 2]) * up[4 * g + 2],
-                          silu_f32(gt[4 * g + 3]) * up[4 * g + 3]));
+              pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]),
+              pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]));
         }
       }
     }
@@ -1678,15 +1700,16 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
           if (cb < ncb) {
             const int trow = tcol0 + cb * 32 + (lane & 31);
             const float w = s_w[trow];
+            const float as = row_scale(trow);
             uint8_t* dst = smem + (trow - rbase) * PITCH;
 #pragma unroll
             for (int rb = 0; rb < kWideRB; ++rb) {
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
-                const f32x16_t& v = acc[rb][cb];
-                *reinterpret_cast<uint2*>(dst + (wrow[rb] + 8 * g + rsub) * 2) =
-                    make_uint2(pack_bf16x2(v[4 * g] * w, v[4 * g + 1] * w),
-                               pack_bf16x2(v[4 * g + 2] * w, v[4 * g + 3] * w));
+                const int col = wrow[rb] + 8 * g + rsub;
+                const f32x4_t v = acc4(acc[rb][cb], g, as, col_scale(t.c0 + col));
+                *reinterpret_cast<uint2*>(dst + col * 2) =
+                    make_uint2(pack_bf16x2(v[0] * w, v[1] * w), pack_bf16x2(v[2] * w, v[3] * w));
               }
             }
           }
@@ -1820,7 +1843,9 @@ hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int
 }
 
 hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipStream_t stream) {
-  if (a.block_m != kWideBlk || a.a_dtype != 1 || a.c_dtype != 1 || (a.epilogue && a.topk_weights))
+  const bool i8 = a.a_dtype == 3;
+  if (a.block_m != kWideBlk || (a.a_dtype != 1 && !i8) || a.c_dtype != 1 ||
+      (a.epilogue && a.topk_weights) || (i8 && (!a.a_scales || !a.b_scales)))
     return hipErrorInvalidValue;   // the ABI layer checks these first
   // tiles: at most one per expert plus one per kWideMaxBlk blocks
   const int64_t nblk = a.max_padded / kWideBlk;
@@ -1830,7 +1855,8 @@ hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipS
   const int64_t grid = tiles * ntile;
   if (grid == 0) return hipSuccess;
   void (*k)(MoeGemmArgs, const int32_t*) =
-      a.epilogue ? moe_gemm_wide_kernel<1> : moe_gemm_wide_kernel<0>;
+      i8 ? (a.epilogue ? moe_gemm_wide_kernel<1, 1> : moe_gemm_wide_kernel<0, 1>)
+         : (a.epilogue ? moe_gemm_wide_kernel<1, 0> : moe_gemm_wide_kernel<0, 0>);
   const hipError_t st = ensure_lds(k, kWideLds);
   if (st != hipSuccess) return st;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kWideThreads), kWideLds, stream, a, table);

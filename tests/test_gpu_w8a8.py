@@ -148,3 +148,44 @@ def test_w8a8_layer_full(moe, dev, name):
     err = max_abs_rel(o, ref)
     print("w8a8 %s, all rows: err=%.3e" % (name, err))
     assert err <= BAR_INT8
+
+
+@pytest.mark.parametrize("case", ["prefill", "ragged", "big_expert"])
+def test_w8a8_wide_tiles_match_tile_kernels(moe, dev, case):
+    """moe_forward_w8a8 on the expert-wide int8 tiles (block_m 32) gives the
+    same bits as on the 256 x 128 tiles (block_m 128): the int32 sums are
+    exact and the epilogues apply the same scales in the same order.  At the
+    prefill size (the automatic choice), with H and I not multiples of the
+    tiles, and with one expert of 700 pairs split over three tiles; both
+    weight layouts."""
+    from synth.configs import Config
+    if case == "prefill":
+        cfg = synth.CONFIGS["prefill"]
+        assert moe.moe_forward_block_m(cfg.T, cfg.E, cfg.topk, "bf16", "packed") == 32
+    elif case == "ragged":
+        cfg = Config(31, "w8a8 ragged", T=333, H=272, I=160, E=40, topk=6, groups=8,
+                     topk_group=3, x_dtype="bf16", w_std=0.05)
+    else:
+        cfg = Config(32, "w8a8 big expert", T=700, H=256, I=384, E=8, topk=1, x_dtype="bf16",
+                     w_std=0.05)
+    d = layer_inputs(cfg, dev)
+    g = d["gating"]
+    if case == "big_expert":
+        g = g.clone()
+        g[:, 5] += 8.0
+    w1q, s1 = _device_quantize(d["w1"])
+    w2q, s2 = _device_quantize(d["w2"])
+    layouts = ["packed"] if case == "prefill" else ["plain", "packed"]
+    for layout in layouts:
+        q1, q2 = w1q, w2q
+        if layout == "packed":
+            q1, q2 = moe.moe_pack_weights(w1q, "silu_mul"), moe.moe_pack_weights(w2q, "none")
+        outs = []
+        for bm in (32, 128):
+            outs.append(moe.moe_forward_w8a8(d["x"], g, q1, s1, q2, s2, cfg.topk, cfg.groups,
+                                             cfg.topk_group, "softmax", cfg.renormalize,
+                                             cfg.scale, block_m=bm))
+        torch.cuda.synchronize()
+        nd = int((outs[0].view(torch.int16) != outs[1].view(torch.int16)).sum())
+        print("w8a8 %s %s: %d of %d outputs differ" % (case, layout, nd, outs[0].numel()))
+        assert nd == 0

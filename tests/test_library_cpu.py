@@ -265,14 +265,17 @@ def test_forward_w8a8_validation(mod):
     f = ctypes.c_void_p(256)
     ws = mod.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2)
     assert ws > 0 and ws % 256 == 0
-    assert mod.lib.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2, 32) == 0   # block_m < 64
+    assert mod.lib.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2, 16) == 0   # block_m < 32
+    assert mod.lib.moe_forward_w8a8_workspace_size(64, 128, 256, 8, 2, 32) > 0    # wide int8 tiles
     args = [f, 1, f, f, f, f, f, 0, 64, 128, 256, 8, 2, 1, 1, 0, 1, 1.0, 0, f, None, None, f,
             1 << 30, None]
     a = list(args); a[1] = 2
     assert L.moe_forward_w8a8(*a) == d["MOE_ERR_DTYPE"]
     a = list(args); a[7] = 5
     assert L.moe_forward_w8a8(*a) == d["MOE_ERR_CONFIG"]
-    a = list(args); a[18] = 32
+    a = list(args); a[18] = 16
+    assert L.moe_forward_w8a8(*a) == d["MOE_ERR_CONFIG"]
+    a = list(args); a[18] = 32; a[1] = 0   # block 32 (the wide int8 tiles) needs bf16 x
     assert L.moe_forward_w8a8(*a) == d["MOE_ERR_CONFIG"]
     a = list(args); a[9] = 120      # H % 16
     assert L.moe_forward_w8a8(*a) == d["MOE_ERR_SHAPE"]

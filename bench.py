@@ -70,17 +70,23 @@ class Timer:
         return float(np.mean(ms)), float(np.median(ms))
 
 
-FLUSH_BYTES = 512 << 20        # larger than the 256 MB Infinity Cache and every L2
+FLUSH_BYTES = 1 << 30          # two halves, each larger than the 256 MB Infinity Cache
 
 
 def flushed_events(torch, fn, reps, flush):
     """Mean and median of fn, each call event-timed after a write of the
-    whole flush buffer (outside the timed region), so no call finds the
-    previous call's data in the Infinity Cache or an L2."""
+    first half of the flush buffer and a read of its second half (outside the
+    timed region), so no call finds the previous call's data in the Infinity
+    Cache or an L2.  The read evicts the write's dirty lines as well: left in
+    the Infinity Cache they would be written back during the timed call,
+    about 20 us of HBM time that belongs to the flush."""
     start = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     end = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    half = flush.numel() // 2
+    wr, rd = flush[:half], flush[half:].view(torch.int64)
     for i in range(reps):
-        flush.fill_(i & 0x7f)
+        wr.fill_(i & 0x7f)
+        rd.sum()
         start[i].record()
         fn()
         end[i].record()

@@ -1016,30 +1016,77 @@ static_assert(GmmCfg::BN == kPackRows, "packed int8 weights are cut into tiles o
 
 typedef i32x16_t GmmAcc[GmmCfg::RB][GmmCfg::CB];
 
-// m-tiles before each expert, tprefix[e] (e <= E), from the clamped offsets.
-// Every thread takes part (barriers); scan_buf: THREADS ints of LDS.
 __device__ __forceinline__ int gmm_row_of(const GmmI8Args& a, int e) {
   const int v = a.offsets[e], M = (int)a.M;
   return v < 0 ? 0 : (v > M ? M : v);
 }
 
-__device__ __forceinline__ void gmm_tile_prefix(const GmmI8Args& a, int* tprefix, int* scan_buf) {
+// Order of the GMM's tiles.  A weight slice (expert e, n-tile nt) has one
+// tile per m-tile of e; those run back to back on one XCD, so the slice is
+// fetched once into that XCD's L2.  Slices are dealt to the 8 XCDs
+// round-robin in the order: experts by rows, most first (ties by id), then
+// n-tiles, so every XCD streams an even share of every expert's weights and
+// runs its slices in that order.  Workgroup id i is placed on XCD i % 8
+// (slot i / 8 of that XCD's sequence): each XCD starts with its share of the
+// largest experts, and the tiles left for the slots that free up first are
+// those of the smallest.
+struct GmmOrder {
+  int prefix[kMaxGmmExperts + 1];   // this XCD's tiles before sorted position p
+  uint16_t order[kMaxGmmExperts];   // expert at sorted position p
+};
+
+// n-tiles nt in [0, ntile) with (p * ntile + nt) % 8 == xcd: the first one and
+// how many.
+__device__ __forceinline__ int gmm_first_nt(int p, int ntile, int xcd) {
+  const int base = ((p % kNumXcd) * (ntile % kNumXcd)) % kNumXcd;
+  return (xcd - base + kNumXcd) % kNumXcd;
+}
+__device__ __forceinline__ int gmm_units_on(int p, int ntile, int xcd) {
+  const int nt0 = gmm_first_nt(p, ntile, xcd);
+  return nt0 < ntile ? (ntile - 1 - nt0) / kNumXcd + 1 : 0;
+}
+
+// Builds o for this workgroup's XCD.  work: at least THREADS + E + 4 ints of
+// LDS that are free until the K loop (rows per expert, then the scan).
+// Every thread takes part (barriers).
+__device__ __forceinline__ void gmm_build_order(const GmmI8Args& a, int ntile, int xcd,
+                                                GmmOrder& o, int* work) {
   constexpr int BM = GmmCfg::BM, NT = GmmCfg::THREADS;
-  const int tid = tile_tid(), E = a.E;
-  const int per = (E + NT - 1) / NT;   // <= 4
-  int cnt[4] = {0, 0, 0, 0};
-  int local = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid * per + j;
-    if (j < per && e < E) {
-      const int lo = gmm_row_of(a, e);
-      int hi = gmm_row_of(a, e + 1);
-      hi = hi < lo ? lo : hi;
-      cnt[j] = (hi - lo + BM - 1) / BM;
-      local += cnt[j];
+  static_assert(kMaxGmmExperts <= 2 * NT, "two sorted positions per thread");
+  const int tid = tile_tid(), E = a.E, E4 = (E + 3) & ~3;
+  int* rows = work;                 // [E4]; -1 past E sorts after every expert
+  int* scan_buf = work + E4;        // [NT]
+  for (int e = tid; e < E4; e += NT) {
+    int r = -1;
+    if (e < E) {
+      const int lo = gmm_row_of(a, e), hi = gmm_row_of(a, e + 1);
+      r = hi > lo ? hi - lo : 0;
     }
+    rows[e] = r;
   }
+  __syncthreads();
+  // sorted position of e: experts with more rows, or as many rows and a
+  // smaller id, come first
+  for (int e = tid; e < E; e += NT) {
+    const int re = rows[e];
+    int pos = 0;
+    for (int f = 0; f < E4; f += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(rows + f);
+      pos += (v.x > re || (v.x == re && f < e)) + (v.y > re || (v.y == re && f + 1 < e)) +
+             (v.z > re || (v.z == re && f + 2 < e)) + (v.w > re || (v.w == re && f + 3 < e));
+    }
+    o.order[pos] = (uint16_t)e;
+  }
+  __syncthreads();
+  // this XCD's tiles per sorted position, then their exclusive prefix
+  const int p0 = tid * 2;
+  int cnt[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = p0 + j;
+    if (p < E) cnt[j] = (rows[o.order[p]] + BM - 1) / BM * gmm_units_on(p, ntile, xcd);
+  }
+  const int local = cnt[0] + cnt[1];
   scan_buf[tid] = local;
   __syncthreads();
   for (int off = 1; off < NT; off <<= 1) {
@@ -1048,42 +1095,38 @@ __device__ __forceinline__ void gmm_tile_prefix(const GmmI8Args& a, int* tprefix
     scan_buf[tid] += add;
     __syncthreads();
   }
-  int run = scan_buf[tid] - local;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid * per + j;
-    if (j < per && e < E) {
-      tprefix[e] = run;
-      run += cnt[j];
-    }
-  }
-  if (tid == NT - 1) tprefix[E] = scan_buf[tid];
+  const int run = scan_buf[tid] - local;
+  if (p0 < E) o.prefix[p0] = run;
+  if (p0 + 1 < E) o.prefix[p0 + 1] = run + cnt[0];
+  if (tid == NT - 1) o.prefix[E] = scan_buf[tid];
   __syncthreads();
 }
 
-// Tile L of the GMM (0 <= L < tprefix[E] * ntile): its expert, and inside
-// the expert the m-tiles of one n-tile adjacent (they share the weight slice).
+static_assert((kMaxGmmExperts + 4 + GmmCfg::THREADS) * 4 <= GmmCfg::kBytes,
+              "the order's work space fits the K ring");
+
 struct GmmTile {
   int e, mcount, nt, mt, row_lo, row_hi, row0;
   int64_t n0;
 };
 
-__device__ __forceinline__ GmmTile gmm_tile_at(const GmmI8Args& a, const int* tprefix, int ntile,
-                                               int L) {
+// Tile s (0 <= s < o.prefix[E]) of this XCD's sequence.
+__device__ __forceinline__ GmmTile gmm_tile_at(const GmmI8Args& a, const GmmOrder& o, int ntile,
+                                               int xcd, int s) {
   GmmTile t;
-  int lo = 0, hi = a.E;   // the largest e with tprefix[e] * ntile <= L
+  int lo = 0, hi = a.E;   // the largest p with prefix[p] <= s; it has tiles here
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tprefix[mid] * ntile <= L) lo = mid; else hi = mid;
+    if (o.prefix[mid] <= s) lo = mid; else hi = mid;
   }
-  t.e = lo;
-  t.mcount = tprefix[lo + 1] - tprefix[lo];
-  const int lin = L - tprefix[lo] * ntile;
-  t.nt = lin / t.mcount;
-  t.mt = lin % t.mcount;
-  t.row_lo = gmm_row_of(a, lo);
-  const int rh = gmm_row_of(a, lo + 1);
+  t.e = o.order[lo];
+  t.row_lo = gmm_row_of(a, t.e);
+  const int rh = gmm_row_of(a, t.e + 1);
   t.row_hi = rh < t.row_lo ? t.row_lo : rh;
+  t.mcount = (t.row_hi - t.row_lo + GmmCfg::BM - 1) / GmmCfg::BM;
+  const int r = s - o.prefix[lo];
+  t.nt = gmm_first_nt(lo, ntile, xcd) + kNumXcd * (r / t.mcount);
+  t.mt = r % t.mcount;
   t.row0 = t.row_lo + t.mt * GmmCfg::BM;
   t.n0 = (int64_t)t.nt * GmmCfg::BN;
   return t;
@@ -1217,14 +1260,13 @@ __device__ __forceinline__ void gmm_acc_clear(GmmAcc& acc) {
 __global__ void __launch_bounds__(GmmCfg::THREADS, GmmCfg::OCC * GmmCfg::THREADS / 256)
 gmm_i8_tile_kernel(GmmI8Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int tprefix[kMaxGmmExperts + 1];   // m-tiles before expert e
-  __shared__ int scan_buf[GmmCfg::THREADS];
+  __shared__ GmmOrder order;
   __shared__ int rowinfo[GmmCfg::BM];
-  gmm_tile_prefix(a, tprefix, scan_buf);
   const int ntile = (int)((a.N + GmmCfg::BN - 1) / GmmCfg::BN);
-  const int live = tprefix[a.E] * ntile;
-  if ((int)blockIdx.x >= live) return;
-  const GmmTile t = gmm_tile_at(a, tprefix, ntile, xcd_remap((int)blockIdx.x, live));
+  const int xcd = (int)blockIdx.x % kNumXcd, slot = (int)blockIdx.x / kNumXcd;
+  gmm_build_order(a, ntile, xcd, order, reinterpret_cast<int*>(smem));
+  if (slot >= order.prefix[a.E]) return;
+  const GmmTile t = gmm_tile_at(a, order, ntile, xcd, slot);
   const int kst = (int)((a.K + GmmCfg::ROWB - 1) / GmmCfg::ROWB);
   GmmAcc acc;
   gmm_acc_clear(acc);
@@ -1866,10 +1908,12 @@ hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipS
 hipError_t launch_gmm_int8(const GmmI8Args& a, hipStream_t stream) {
   typedef GmmCfg C;
   const int ntile = (int)((a.N + C::BN - 1) / C::BN);
-  // Upper bound of m-tiles: every non-empty expert adds at most one partial tile.
+  // Upper bound of m-tiles: every non-empty expert adds at most one partial
+  // tile; an XCD gets at most ceil(ntile / 8) n-tiles of each expert.
   const int64_t mt_max = (a.M + C::BM - 1) / C::BM + a.E;
-  const int64_t grid = mt_max * ntile;
+  const int64_t grid = mt_max * ((ntile + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0 || a.M == 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   constexpr size_t lds = C::kBytes;
   const hipError_t st = ensure_lds(gmm_i8_tile_kernel, lds);
   if (st != hipSuccess) return st;

@@ -98,3 +98,27 @@ def test_int8_quantisation_error_informational(moe, dev):
     cos = float((got * fp).sum() / np.sqrt((got * got).sum() * (fp * fp).sum()))
     print("int8 vs fp32 GEMM: max-abs-rel %.3e cosine %.6f" % (rel, cos))
     assert cos > 0.99
+
+
+@pytest.mark.parametrize("mtiles,N", [
+    (65, 2048),    # one n-tile of each expert per XCD: 65 tiles each, one past a round
+    (97, 2048),
+    (40, 4096)])   # two n-tiles of each expert per XCD
+def test_int8_tile_order_shapes(moe, dev, mtiles, N):
+    """Tiles dealt to the XCDs by expert size (ties by id): experts of 1 to
+    128 rows, many of equal size, every output written once."""
+    rng = np.random.default_rng(mtiles * 1000 + N)
+    sizes = rng.integers(1, 129, size=mtiles)
+    sizes[::7] = 128
+    sizes[::11] = 5
+    _run_and_check(moe, dev, int(sizes.sum()), 128, N, mtiles, sizes, 90 + mtiles,
+                   layout="packed")
+
+
+def test_int8_tile_order_narrow_n(moe, dev):
+    """N = 256 (one n-tile per expert): the experts themselves are dealt to
+    the XCDs in turn, so the XCDs hold different numbers of tiles."""
+    sizes = np.full(600, 3)
+    sizes[::5] = 250
+    sizes[::9] = 0
+    _run_and_check(moe, dev, int(sizes.sum()), 64, 256, 600, sizes, 95, layout="packed")

@@ -31,9 +31,11 @@
 //    padded to 144 bytes so every group of 8 lanes reading 16 bytes hits 8
 //    distinct bank quads.
 //  * Tiles are numbered block-major (the n-tiles of a block adjacent, the
-//    blocks of one expert adjacent), and xcd_remap gives each XCD one
-//    contiguous run of tiles, so an expert's weight slab and its gathered
-//    rows are shared in one XCD's L2.
+//    blocks of one expert adjacent).  The tile kernels hand consecutive
+//    tiles to consecutive XCDs (each XCD streams a share of every expert's
+//    weights); the expert-wide kernel gives each XCD one contiguous run of
+//    tiles (xcd_remap), so an expert's gathered rows are shared in one XCD's
+//    L2; the GMM deals each expert's weight slices to the XCDs in turn.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -567,12 +569,17 @@ __device__ __forceinline__ bool moe_tile_at(const MoeGemmArgs& a, int L, int nbl
 }
 
 // Tile of this workgroup in a grid of one workgroup per tile; false if none.
+// Logical tile L is workgroup L, so consecutive tiles (an expert's n-tiles)
+// go to consecutive XCDs and every XCD streams a share of every expert's
+// weights.  (Measured on the decode layers against giving each XCD one
+// contiguous run of tiles: T = 16 1404 against 1422 us, T = 64 2818 against
+// 2891 us.)
 template <int BN, int BM, int EPI>
 __device__ __forceinline__ bool moe_tile(const MoeGemmArgs& a, MoeTile& t, int* s_win) {
   const int nblk = *a.total / BM;
   const int live = nblk * moe_ntiles<BN, EPI>(a);
   if ((int)blockIdx.x >= live) return false;
-  return moe_tile_at<BN, BM, EPI>(a, xcd_remap((int)blockIdx.x, live), nblk, t, s_win);
+  return moe_tile_at<BN, BM, EPI>(a, (int)blockIdx.x, nblk, t, s_win);
 }
 
 // Local weight row of tile row r (0 <= r < BN) -> global row of expert e,

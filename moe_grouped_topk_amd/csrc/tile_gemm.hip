@@ -40,6 +40,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace moe {
@@ -1316,7 +1317,7 @@ constexpr int kWideCB = (kWideMaxBlk + kWideWM - 1) / kWideWM;   // token blocks
 constexpr int kWideWP = kWideBN / 16 / (kWideWN * kWideWM); // 2 weight pieces per wave
 constexpr int kWideTP = (kWideBM / 16 + (kWideWN * kWideWM) - 1) / (kWideWN * kWideWM);   // <= 3
 static_assert(kWideBN == kPackRows, "a wide tile's weight rows are one packed tile");
-static_assert(kWideLds + kWideBM * 4 <= 160 * 1024, "rings of the wide tile");
+static_assert(kWideLds + 2 * kWideBM * 4 <= 160 * 1024, "rings, row info and row weights of the wide tile");
 
 // Tile table of a layer: t[0] = number of tiles; tile j: t[1 + 3 j] = expert,
 // t[2 + 3 j] = first block, t[3 + 3 j] = blocks (1..kWideMaxBlk).  An expert
@@ -1401,7 +1402,7 @@ __device__ __forceinline__ void wide_wait(int n) {
 // wave's token blocks (its accumulators beyond them stay untouched).
 template <int KIND, int NCB>
 __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src, int64_t kbytes,
-                                              const int (&wrow)[kWideRB], int tcol0,
+                                              const int (&wrow)[kWideRB], int tcol0, bool w_issued,
                                               typename Mma<KIND>::acc_t (&acc)[kWideRB][kWideCB]) {
   const int tid = tile_tid(), lane = tid & 63;
   const uint32_t wbase = lds_addr(smem), tbase = wbase + kWideNW * kWideWStage;
@@ -1465,18 +1466,24 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
       }
     }
   };
-  // Issue schedule: at the start of iteration i (its stage published, every
-  // wave done with stage i - 1) W(i + NW - 1), then T(i + NT - 1), into the
-  // buffers of stage i - 1; the prologue issues the same sequence for i < 0.
-  // Loads complete in issue order, so stage s is in when the loads issued
-  // after T(s) are all that may be outstanding: the W and T of the NT - 2
-  // iterations after the one that issued T(s) (W(s) went out before T(s),
-  // in the same iteration or an earlier one, as NW >= NT).
+  // Issue schedule: the prologue issues W(0 .. NW - 2) (unless the previous
+  // tile of this workgroup already did, before its epilogue), then
+  // T(0 .. NT - 2); iteration i (its stage published, every wave done with
+  // stage i - 1) issues W(i + NW - 1), then T(i + NT - 1), into the buffers
+  // of stage i - 1.  Loads complete in issue order, so stage s is in when
+  // the loads issued after T(s) are all that may be outstanding: the later
+  // prologue T's and the W and T of the iterations from max(0, s - NT + 2)
+  // to s - 1 (W(s) went out before T(s), as NW >= NT).  Stores issued in
+  // between (the previous tile's epilogue) also count in vmcnt; they only
+  // make a wait longer.
   auto n_after = [&](int s) {
     int n = 0;
 #pragma unroll
     for (int i = s - kWideNT + 2; i < s; ++i)
-      n += (i + kWideNT - 1 < nk ? ntw : 0) + (i + kWideNW - 1 < nk ? nw : 0);
+      if (i >= 0) n += (i + kWideNT - 1 < nk ? ntw : 0) + (i + kWideNW - 1 < nk ? nw : 0);
+#pragma unroll
+    for (int j = 1; j <= kWideNT - 2; ++j)
+      if (j > s && j < nk) n += ntw;
     return n;
   };
   const bool partial = (kbytes % kWideRowB) != 0;
@@ -1489,10 +1496,10 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
       wide_wait(n_after(s));
     }
   };
-  for (int i = 1 - kWideNW; i < 0; ++i) {
-    if (i + kWideNW - 1 < nk) issue_w(i + kWideNW - 1);
-    if (i + kWideNT - 1 >= 0 && i + kWideNT - 1 < nk) issue_t(i + kWideNT - 1);
+  if (!w_issued) {
+    for (int i = 0; i < kWideNW - 1 && i < nk; ++i) issue_w(i);
   }
+  for (int i = 0; i < kWideNT - 1 && i < nk; ++i) issue_t(i);
 
   const int swz = ((lane & 31) >> 2) & 3;
   auto load_frags = [&](int kt, int ks, u32x4_t (&af)[kWideRB], u32x4_t (&bf)[kWideCB]) {
@@ -1565,70 +1572,56 @@ __device__ __forceinline__ void wide_mainloop(uint8_t* smem, const WideSrc& src,
 template <int KIND>
 __device__ __forceinline__ void wide_mainloop_live(uint8_t* smem, const WideSrc& src,
                                                    int64_t kbytes, const int (&wrow)[kWideRB],
-                                                   int tcol0, int ncb,
+                                                   int tcol0, int ncb, bool w_issued,
                                                    typename Mma<KIND>::acc_t (&acc)[kWideRB][kWideCB]) {
   static_assert(kWideCB <= 5, "wide_mainloop_live dispatches up to 5 token blocks");
   switch (__builtin_amdgcn_readfirstlane(ncb)) {
-    case 5: return wide_mainloop<KIND, 5>(smem, src, kbytes, wrow, tcol0, acc);
-    case 4: return wide_mainloop<KIND, 4>(smem, src, kbytes, wrow, tcol0, acc);
-    case 3: return wide_mainloop<KIND, 3>(smem, src, kbytes, wrow, tcol0, acc);
-    case 2: return wide_mainloop<KIND, 2>(smem, src, kbytes, wrow, tcol0, acc);
-    case 1: return wide_mainloop<KIND, 1>(smem, src, kbytes, wrow, tcol0, acc);
-    default: return wide_mainloop<KIND, 0>(smem, src, kbytes, wrow, tcol0, acc);
+    case 5: return wide_mainloop<KIND, 5>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
+    case 4: return wide_mainloop<KIND, 4>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
+    case 3: return wide_mainloop<KIND, 3>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
+    case 2: return wide_mainloop<KIND, 2>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
+    case 1: return wide_mainloop<KIND, 1>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
+    default: return wide_mainloop<KIND, 0>(smem, src, kbytes, wrow, tcol0, w_issued, acc);
   }
 }
 
-// EPI 1: gate_up with the SiLU*up epilogue, bf16 h in sorted order;
-// EPI 0: down times the routing weight, bf16 rows in pair order.
-// KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights, exact
-// int32 sums times the row scale (a_scales) and the channel scale (b_scales).
-template <int EPI, int KIND>
-__global__ void __launch_bounds__(kWideThreads, 2)
-moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
-  typedef typename Mma<KIND>::acc_t Acc;
-  constexpr int kElem = KIND ? 1 : 2;                  // bytes per operand element
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int rowinfo[kWideBM];
-  const int ntile = moe_ntiles<kWideBN, EPI>(a);
-  const int live = table[0] * ntile;
-  if ((int)blockIdx.x >= live) return;
-  // the n-tiles of one expert tile are neighbours: they run side by side and
-  // share the expert's token rows in L2
-  const int L = xcd_remap((int)blockIdx.x, live);
-  const int j = L / ntile, nt = L % ntile;
-  const int e = table[1 + 3 * j], b0 = table[2 + 3 * j], nb = table[3 + 3 * j];
-  // a tile outside the alignment's blocks or experts is skipped, not read
-  if (e < 0 || e >= a.E || b0 < 0 || nb < 1 || nb > kWideMaxBlk ||
-      (int64_t)(b0 + nb) * kWideBlk > a.max_padded)
-    return;
-  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % kWideWN, wm = wave / kWideWN;
-  const int nrows = nb * kWideBlk;
-  const int64_t s0 = (int64_t)b0 * kWideBlk;          // first sorted position
-  for (int r = tid; r < kWideBM; r += kWideThreads) {
-    int p = -1;
-    if (r < nrows) {
-      p = a.sorted_ids[s0 + r];
-      if (p < 0 || p >= a.num_valid) p = -1;
-    }
-    rowinfo[r] = p;
-  }
-  __syncthreads();
+// A wide tile: expert e, its blocks [b0, b0 + nb), n-tile nt, and whether it
+// is the only tile of its weight slice; valid = inside the alignment's
+// blocks and experts (a bad table entry is skipped, not read).
+struct WideTile {
+  int e, b0, nb, nt;
+  bool stream, valid;
+};
 
-  MoeTile t;
-  t.e = e; t.blk = b0; t.nt = nt; t.s0 = s0;
-  t.c0 = (int64_t)nt * (EPI ? kWideBN / 2 : kWideBN);
-  t.solo = 0;
-  WideSrc src;
+__device__ __forceinline__ WideTile wide_tile_at(const MoeGemmArgs& a, const int32_t* table,
+                                                 int ntile, int L) {
+  WideTile w;
+  const int j = L / ntile;
+  w.nt = L % ntile;
+  w.e = table[1 + 3 * j];
+  w.b0 = table[2 + 3 * j];
+  w.nb = table[3 + 3 * j];
+  w.valid = !(w.e < 0 || w.e >= a.E || w.b0 < 0 || w.nb < 1 || w.nb > kWideMaxBlk ||
+              (int64_t)(w.b0 + w.nb) * kWideBlk > a.max_padded);
+  w.stream = a.b_packed != 0 && (j == 0 || table[1 + 3 * (j - 1)] != w.e) &&
+             (j + 1 >= table[0] || table[1 + 3 * (j + 1)] != w.e);
+  return w;
+}
+
+// This wave's weight pieces of tile w (stage-0 addresses); rows past the
+// matrix read row 0.
+template <int EPI, int KIND>
+__device__ __forceinline__ void wide_weight_src(const MoeGemmArgs& a, const WideTile& w, int wave,
+                                                int lane, WideSrc& src) {
+  constexpr int kElem = KIND ? 1 : 2;
   src.packed = a.b_packed != 0;
+  src.stream = w.stream;
   const int64_t wrow_bytes = a.K * kElem;
-  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)e * a.N * wrow_bytes;
+  const int64_t c0 = (int64_t)w.nt * (EPI ? kWideBN / 2 : kWideBN);
+  const uint8_t* Bw = reinterpret_cast<const uint8_t*>(a.B) + (int64_t)w.e * a.N * wrow_bytes;
   const uint8_t* Bp = reinterpret_cast<const uint8_t*>(a.B) +
-                      ((int64_t)e * packed_tiles(a.N, EPI) + nt) * packed_kstages(a.K, kElem) *
+                      ((int64_t)w.e * packed_tiles(a.N, EPI) + w.nt) * packed_kstages(a.K, kElem) *
                           kPackBlockBytes;
-  // the only tile that streams this weight slice: non-temporal loads
-  src.stream = src.packed && (j == 0 || table[1 + 3 * (j - 1)] != e) &&
-               (j + 1 >= table[0] || table[1 + 3 * (j + 1)] != e);
 #pragma unroll
   for (int i = 0; i < kWideWP; ++i) {
     const int q = wave * kWideWP + i;
@@ -1636,129 +1629,235 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
     if (src.packed) {
       src.w[i] = Bp + q * 1024 + lane * 16;
     } else {
-      const int64_t g = moe_weight_row<kWideBN, EPI>(a, t.c0, q * 16 + (lane >> 2));
-      src.w[i] = Bw + (g < 0 ? 0 : g) * wrow_bytes;      // past the matrix: row 0
+      const int64_t g = moe_weight_row<kWideBN, EPI>(a, c0, q * 16 + (lane >> 2));
+      src.w[i] = Bw + (g < 0 ? 0 : g) * wrow_bytes;
     }
   }
-  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
-  const int64_t arow_bytes = a.lda * kElem;
-  src.nt = 0;
-#pragma unroll
-  for (int i = 0; i < kWideTP; ++i) {
-    const int q = wave + i * (kWideWN * kWideWM);
-    src.tlds[i] = (uint32_t)(q * 1024);
-    const int r = q * 16 + (lane >> 2);
-    if (q * 16 < nrows) {
-      src.nt = i + 1;
-      const int p = rowinfo[r];
-      const int p0 = rowinfo[0] < 0 ? 0 : rowinfo[0];  // row 0 of a tile is a pair
-      const int64_t row = a.a_rows == 0 ? (int64_t)((p < 0 ? p0 : p) / a.a_row_div)
-                                        : (p < 0 ? s0 : s0 + r);
-      src.t[i] = Ab + row * arow_bytes;
-    } else {
-      src.t[i] = Ab;
-    }
-  }
-  int wrow[kWideRB];
-  wave_rows<kWideBN, kWideWN, kWideRB, EPI>(wn, wrow);
-  const int h = (nb + 1) / 2;                          // token blocks of wave row 0
-  const int tcol0 = wm ? h * kWideBlk : 0;
-  const int ncb = wm ? nb - h : h;
-  // this thread's row weight (down), read while the K loop runs
-  float wr = 1.0f;
-  if (!EPI && a.topk_weights && tid < nrows && rowinfo[tid] >= 0)
-    wr = a.topk_weights[rowinfo[tid]];
-  Acc acc[kWideRB][kWideCB];
-#pragma unroll
-  for (int rb = 0; rb < kWideRB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < kWideCB; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
-  wide_mainloop_live<KIND>(smem, src, wrow_bytes, wrow, tcol0, ncb, acc);
+}
 
-  // Epilogue through LDS (the drained rings), whole 16-byte pieces of rows.
-  // Scales (int8): the row's a_scales entry and the channel's b_scales entry
-  // (1 for bf16, which leaves the sums' bits as they are).
-  const int rsub = 4 * (lane >> 5);
-  uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
-  const float* bsc = KIND ? a.b_scales + (int64_t)e * a.N : nullptr;
-  const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
-  auto row_scale = [&](int trow) -> float {   // trow a valid row of the tile
-    if constexpr (KIND == 0) return 1.0f;
-    const int p = rowinfo[trow];
-    if (p < 0) return 0.0f;
-    return a.a_scales[a.a_rows == 0 ? (int64_t)(p / a.a_row_div) : s0 + trow];
-  };
-  auto col_scale = [&](int64_t n) -> f32x4_t {   // channels n .. n + 3
-    if constexpr (KIND == 0) return one4;
-    return *reinterpret_cast<const f32x4_t*>(bsc + (n < a.N ? n : 0));   // past N: never stored
-  };
-  if constexpr (EPI) {
-    constexpr int HC = kWideBN / 2, PITCH = HC * 2 + 16, LPR = HC * 2 / 16;
-    constexpr int RPP = kWideThreads / LPR;
-    static_assert(kWideBM * PITCH <= kWideLds, "staged wide SiLU tile");
-    const int64_t Nout = a.N / 2;
-    __syncthreads();                                   // every wave has left the rings
+// The weight loads of stages 0 .. NW - 2 of a tile (the K loop's prologue
+// otherwise issues them), this wave's pieces, in the loop's order.
+__device__ __forceinline__ void wide_prefetch_w(uint8_t* smem, const WideSrc& src, int64_t kbytes) {
+  const int lane = tile_tid() & 63, chunk_pos = lane & 3;
+  const uint32_t wbase = lds_addr(smem);
+  const int nk = (int)((kbytes + kWideRowB - 1) / kWideRowB);
+  for (int kt = 0; kt < kWideNW - 1 && kt < nk; ++kt) {
 #pragma unroll
-    for (int cb = 0; cb < kWideCB; ++cb) {
-      if (cb < ncb) {
-        const int trow = tcol0 + cb * 32 + (lane & 31);
-        const float as = row_scale(trow);
-        uint8_t* dst = smem + trow * PITCH;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = wrow[0] + 8 * g + rsub;
-          const int64_t n = t.c0 + col;                // output column (gate row n, up row Nout + n)
-          const f32x4_t gt = acc4(acc[0][cb], g, as, col_scale(n));
-          const f32x4_t up = acc4(acc[1][cb], g, as, col_scale(n < Nout ? Nout + n : a.N));
-          *reinterpret_cast<uint2*>(dst + col * 2) = make_uint2(
-              pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]),
-              pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]));
-        }
+    for (int i = 0; i < kWideWP; ++i) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+          wbase + (uint32_t)(kt * kWideWStage) + src.wlds[i]);
+      if (src.packed) {
+        const uint8_t* g = src.w[i] + (int64_t)kt * kPackBlockBytes;
+        if (src.stream) dma16_nt(m0, g); else dma16(m0, g);
+      } else {
+        const int64_t koff = (int64_t)kt * kWideRowB;
+        const int row = (int)(src.wlds[i] / kWideRowB) + (lane >> 2);
+        const int c = chunk_pos ^ ((row >> 2) & 3);
+        dma16(m0, src.w[i] + (koff + c * 16 < kbytes ? koff + c * 16 : 0));
       }
     }
-    __syncthreads();
-    const int ch = tid % LPR;
-    const int64_t col = t.c0 + ch * 8;
-    for (int r0 = 0; r0 < nrows; r0 += RPP) {
-      const int r = r0 + tid / LPR;
-      if (r >= nrows || rowinfo[r] < 0 || col >= Nout) continue;
-      const int64_t crow = a.c_rows == 0 ? (int64_t)rowinfo[r] : s0 + r;
-      *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) =
-          *reinterpret_cast<const u32x4_t*>(smem + r * PITCH + ch * 16);
+  }
+}
+
+// EPI 1: gate_up with the SiLU*up epilogue, bf16 h in sorted order;
+// EPI 0: down times the routing weight, bf16 rows in pair order.
+// KIND 0: bf16 tokens and weights; KIND 1: int8 tokens and weights, exact
+// int32 sums times the row scale (a_scales) and the channel scale (b_scales).
+// One workgroup per CU, persistent: the grid is 8 x S workgroups, and
+// workgroup (XCD x = id % 8, slot id / 8) takes positions slot, slot + S, ...
+// of XCD x's contiguous run of tiles, so the n-tiles of one expert tile run
+// side by side on one XCD and share the expert's token rows in L2.  Once a
+// tile's K loop is done its workgroup issues the next tile's first weight
+// stages, then runs the epilogue (staged in the LDS the next tile does not
+// use yet), so the weight stream goes on through epilogues and tile changes.
+template <int EPI, int KIND>
+__global__ void __launch_bounds__(kWideThreads, 2)
+moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
+  typedef typename Mma<KIND>::acc_t Acc;
+  constexpr int kElem = KIND ? 1 : 2;                  // bytes per operand element
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int rowinfo[kWideBM];
+  __shared__ float s_w[kWideBM];
+  __shared__ float s_as[KIND ? kWideBM : 1];           // int8: row scales of the tile
+  __shared__ __attribute__((aligned(16))) float s_bs[KIND ? kWideBN : 4];   // and channel scales
+  // epilogue staging: the last weight stage and the token ring (the next
+  // tile's weight stages 0 .. NW - 2 are in flight meanwhile)
+  uint8_t* stage_lds = smem + (kWideNW - 1) * kWideWStage;
+  constexpr int kStageBytes = kWideWStage + kWideNT * kWideTStage;
+  const int ntile = moe_ntiles<kWideBN, EPI>(a);
+  const int live = table[0] * ntile;
+  const int xcd = (int)blockIdx.x % kNumXcd;
+  const int q = live / kNumXcd, r = live % kNumXcd;
+  const int run0 = xcd * q + (xcd < r ? xcd : r), runlen = q + (xcd < r ? 1 : 0);
+  const int tid = tile_tid(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % kWideWN, wm = wave / kWideWN;
+  const int64_t wrow_bytes = a.K * kElem;
+  int wrow[kWideRB];
+  wave_rows<kWideBN, kWideWN, kWideRB, EPI>(wn, wrow);
+  static_assert(kWideBM <= kWideThreads, "one row of row info per thread");
+  // pair index of tile row tid of tile w (-1: padding or out of range)
+  auto row_pair = [&](const WideTile& w) {
+    int p = -1;
+    if (tid < w.nb * kWideBlk) {
+      p = a.sorted_ids[(int64_t)w.b0 * kWideBlk + tid];
+      if (p < 0 || p >= a.num_valid) p = -1;
     }
-  } else {
-    // two passes, one per wave row (at most kWideCB * 32 rows each)
-    constexpr int PITCH = kWideBN * 2 + 16, LPR = kWideBN * 2 / 16;
-    constexpr int RPP = kWideThreads / LPR, PR = kWideCB * 32;
-    static_assert(PR * PITCH + kWideBM * 4 <= kWideLds, "staged wide down tile");
-    float* s_w = reinterpret_cast<float*>(smem + PR * PITCH);
-    __syncthreads();                                   // every wave has left the rings
-    if (tid < kWideBM) s_w[tid] = wr;
-    const int ch = tid % LPR;
+    return p;
+  };
+  const int S = (int)gridDim.x / kNumXcd, slot = (int)blockIdx.x / kNumXcd;
+  int pos = slot;
+  while (pos < runlen && !wide_tile_at(a, table, ntile, run0 + pos).valid) pos += S;
+  if (pos >= runlen) return;
+  WideTile w = wide_tile_at(a, table, ntile, run0 + pos);
+  int pair = row_pair(w);                              // this thread's row of the tile
+  bool w_issued = false;
+  for (;;) {
+    const int e = w.e, nb = w.nb, nt = w.nt;
+    const int nrows = nb * kWideBlk;
+    const int64_t s0 = (int64_t)w.b0 * kWideBlk;      // first sorted position
+    if (tid < kWideBM) rowinfo[tid] = pair;
+    __syncthreads();
+    MoeTile t;
+    t.e = e; t.blk = w.b0; t.nt = nt; t.s0 = s0;
+    t.c0 = (int64_t)nt * (EPI ? kWideBN / 2 : kWideBN);
+    t.solo = 0;
+    // int8: the tile's row and channel scales into LDS now, so that the
+    // epilogue does not wait on global loads queued behind the next tile's
+    // weight loads (loads complete in issue order)
+    if constexpr (KIND != 0) {
+      if (tid < kWideBM) {
+        const int p = rowinfo[tid];
+        s_as[tid] = p < 0 ? 0.0f
+                          : a.a_scales[a.a_rows == 0 ? (int64_t)(p / a.a_row_div) : s0 + tid];
+      }
+      if (tid < kWideBN) {
+        // weight row tid of the tile: gate / up channel (SiLU) or channel c0 + tid
+        const int64_t n = EPI ? (tid < kWideBN / 2 ? t.c0 + tid : a.N / 2 + t.c0 + tid - kWideBN / 2)
+                              : t.c0 + tid;
+        s_bs[tid] = n < a.N ? a.b_scales[(int64_t)e * a.N + n] : 0.0f;
+      }
+      asm volatile("" ::: "memory");                  // the stores go out here, not later
+    }
+    WideSrc src;
+    wide_weight_src<EPI, KIND>(a, w, wave, lane, src);
+    const uint8_t* Ab = reinterpret_cast<const uint8_t*>(a.A);
+    const int64_t arow_bytes = a.lda * kElem;
+    src.nt = 0;
+#pragma unroll
+    for (int i = 0; i < kWideTP; ++i) {
+      const int qq = wave + i * (kWideWN * kWideWM);
+      src.tlds[i] = (uint32_t)(qq * 1024);
+      const int rrow = qq * 16 + (lane >> 2);
+      if (qq * 16 < nrows) {
+        src.nt = i + 1;
+        const int p = rowinfo[rrow];
+        const int p0 = rowinfo[0] < 0 ? 0 : rowinfo[0];  // row 0 of a tile is a pair
+        const int64_t row = a.a_rows == 0 ? (int64_t)((p < 0 ? p0 : p) / a.a_row_div)
+                                          : (p < 0 ? s0 : s0 + rrow);
+        src.t[i] = Ab + row * arow_bytes;
+      } else {
+        src.t[i] = Ab;
+      }
+    }
+    const int h = (nb + 1) / 2;                        // token blocks of wave row 0
+    const int tcol0 = wm ? h * kWideBlk : 0;
+    const int ncb = wm ? nb - h : h;
+    // this thread's row weight (down), read while the K loop runs
+    float wr = 1.0f;
+    if (!EPI && a.topk_weights && tid < nrows && rowinfo[tid] >= 0)
+      wr = a.topk_weights[rowinfo[tid]];
+    Acc acc[kWideRB][kWideCB];
+#pragma unroll
+    for (int rb = 0; rb < kWideRB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < kWideCB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+    wide_mainloop_live<KIND>(smem, src, wrow_bytes, wrow, tcol0, ncb, w_issued, acc);
+
+    // every wave has left the rings: the next tile's first weight stages go
+    // out now and stream in while this tile's epilogue runs (its row info is
+    // read now too)
+    __syncthreads();
+    int next = pos + S;
+    while (next < runlen && !wide_tile_at(a, table, ntile, run0 + next).valid) next += S;
+    w_issued = next < runlen;
+    WideTile wn_tile = w;
+    if (w_issued) {
+      wn_tile = wide_tile_at(a, table, ntile, run0 + next);
+      WideSrc nsrc;
+      wide_weight_src<EPI, KIND>(a, wn_tile, wave, lane, nsrc);
+      wide_prefetch_w(smem, nsrc, wrow_bytes);
+      pair = row_pair(wn_tile);
+    }
+
+    // Epilogue through the token ring's LDS, whole 16-byte pieces of rows,
+    // in passes of whole token blocks.  Scales (int8): the row's a_scales
+    // entry and the channel's b_scales entry (1 for bf16, which leaves the
+    // sums' bits as they are).  The thread index goes through an empty asm
+    // statement so that nothing computed from it here is hoisted out of the
+    // tile loop, where it would hold registers through the K loop.
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
+    const int elane = etid & 63;
+    const int rsub = 4 * (elane >> 5);
+    uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
+    const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
+    auto row_scale = [&](int trow) -> float {   // trow a row of the tile
+      if constexpr (KIND == 0) return 1.0f;
+      return *reinterpret_cast<const volatile float*>(s_as + trow);
+    };
+    auto col_scale = [&](int c) -> f32x4_t {    // weight rows c .. c + 3 of the tile
+      if constexpr (KIND == 0) return one4;
+      // read where used (volatile: not hoisted out of the token-block loop,
+      // where the 8 values would hold 32 registers beside the accumulators)
+      return *reinterpret_cast<const volatile f32x4_t*>(s_bs + c);
+    };
+    if (!EPI && etid < kWideBM) s_w[etid] = wr;
+    // pass p stages the token blocks [p * BPP, (p + 1) * BPP) of the tile
+    constexpr int OUTC = EPI ? kWideBN / 2 : kWideBN;  // output columns of the tile
+    constexpr int PITCH = OUTC * 2 + 16, LPR = OUTC * 2 / 16;
+    constexpr int RPP = kWideThreads / LPR;
+    constexpr int BPP = kStageBytes / (32 * PITCH) < kWideMaxBlk ? kStageBytes / (32 * PITCH)
+                                                                 : kWideMaxBlk;
+    static_assert(BPP >= 1, "one token block of the staged tile fits the staging space");
+    const int npass = (nb + BPP - 1) / BPP;
+    const int64_t Nout = EPI ? a.N / 2 : a.N;
+    const int ch = etid % LPR;
     const int64_t col = t.c0 + ch * 8;
-#pragma unroll
-    for (int pass = 0; pass < kWideWM; ++pass) {
-      const int rbase = pass ? h * kWideBlk : 0;
-      const int rend = pass ? nrows : h * kWideBlk;
+    const int blk0 = tcol0 / kWideBlk;                 // this wave's first token block
+    for (int pass = 0; pass < npass; ++pass) {
+      const int rbase = pass * BPP * kWideBlk;
+      const int rend = nrows < rbase + BPP * kWideBlk ? nrows : rbase + BPP * kWideBlk;
       __syncthreads();
-      if (wm == pass) {
 #pragma unroll
-        for (int cb = 0; cb < kWideCB; ++cb) {
-          if (cb < ncb) {
-            const int trow = tcol0 + cb * 32 + (lane & 31);
-            const float w = s_w[trow];
-            const float as = row_scale(trow);
-            uint8_t* dst = smem + (trow - rbase) * PITCH;
+      for (int cb = 0; cb < kWideCB; ++cb) {
+        const int bi = blk0 + cb - pass * BPP;
+        if (cb < ncb && bi >= 0 && bi < BPP) {
+          const int trow = tcol0 + cb * 32 + (elane & 31);
+          const float as = row_scale(trow);
+          uint8_t* dst = stage_lds + (trow - rbase) * PITCH;
+          if constexpr (EPI) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = wrow[0] + 8 * g + rsub;   // output column t.c0 + c
+              const f32x4_t gt = acc4(acc[0][cb], g, as, col_scale(wrow[0] + 8 * g + rsub));
+              const f32x4_t up = acc4(acc[1][cb], g, as, col_scale(wrow[1] + 8 * g + rsub));
+              *reinterpret_cast<uint2*>(dst + c * 2) = make_uint2(
+                  pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]),
+                  pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]));
+            }
+          } else {
+            const float wt = s_w[trow];
 #pragma unroll
             for (int rb = 0; rb < kWideRB; ++rb) {
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
-                const int col = wrow[rb] + 8 * g + rsub;
-                const f32x4_t v = acc4(acc[rb][cb], g, as, col_scale(t.c0 + col));
-                *reinterpret_cast<uint2*>(dst + col * 2) =
-                    make_uint2(pack_bf16x2(v[0] * w, v[1] * w), pack_bf16x2(v[2] * w, v[3] * w));
+                const int c = wrow[rb] + 8 * g + rsub;
+                const f32x4_t v = acc4(acc[rb][cb], g, as, col_scale(c));
+                *reinterpret_cast<uint2*>(dst + c * 2) = make_uint2(
+                    pack_bf16x2(v[0] * wt, v[1] * wt), pack_bf16x2(v[2] * wt, v[3] * wt));
               }
             }
           }
@@ -1766,13 +1865,17 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
       }
       __syncthreads();
       for (int r0 = rbase; r0 < rend; r0 += RPP) {
-        const int r = r0 + tid / LPR;
-        if (r >= rend || rowinfo[r] < 0 || col >= a.N) continue;
-        const int64_t crow = a.c_rows == 0 ? (int64_t)rowinfo[r] : s0 + r;
+        const int rr = r0 + etid / LPR;
+        if (rr >= rend || rowinfo[rr] < 0 || col >= Nout) continue;
+        const int64_t crow = a.c_rows == 0 ? (int64_t)rowinfo[rr] : s0 + rr;
         *reinterpret_cast<u32x4_t*>(Cb + (crow * a.ldc + col) * 2) =
-            *reinterpret_cast<const u32x4_t*>(smem + (r - rbase) * PITCH + ch * 16);
+            *reinterpret_cast<const u32x4_t*>(stage_lds + (rr - rbase) * PITCH + ch * 16);
       }
     }
+    __syncthreads();                                   // staging and rowinfo free again
+    if (!w_issued) break;
+    pos = next;
+    w = wn_tile;
   }
 }
 
@@ -1891,6 +1994,30 @@ hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int
   return hipGetLastError();
 }
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, read once per device.
+hipError_t current_device_cus(int* cus) {
+  static std::atomic<int> cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t st = hipGetDevice(&dev);
+  if (st != hipSuccess) return st;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    st = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (st != hipSuccess) return st;
+    if (v <= 0) return hipErrorInvalidDevice;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  *cus = v;
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipStream_t stream) {
   const bool i8 = a.a_dtype == 3;
   if (a.block_m != kWideBlk || (a.a_dtype != 1 && !i8) || a.c_dtype != 1 ||
@@ -1901,12 +2028,20 @@ hipError_t launch_moe_gemm_wide(const MoeGemmArgs& a, const int32_t* table, hipS
   const int64_t tiles = nblk / kWideMaxBlk + (a.E < nblk ? a.E : nblk);
   const int64_t ntile = a.epilogue ? (a.N / 2 + kWideBN / 2 - 1) / (kWideBN / 2)
                                    : (a.N + kWideBN - 1) / kWideBN;
-  const int64_t grid = tiles * ntile;
-  if (grid == 0) return hipSuccess;
+  const int64_t max_tiles = tiles * ntile;
+  if (max_tiles == 0) return hipSuccess;
+  // one persistent workgroup per CU, the same number on each XCD
+  int cus = 0;
+  hipError_t st = current_device_cus(&cus);
+  if (st != hipSuccess) return st;
+  int64_t per_xcd = (cus + kNumXcd - 1) / kNumXcd;
+  const int64_t need = (max_tiles + kNumXcd - 1) / kNumXcd;
+  per_xcd = per_xcd < need ? per_xcd : need;
+  const int64_t grid = per_xcd * kNumXcd;
   void (*k)(MoeGemmArgs, const int32_t*) =
       i8 ? (a.epilogue ? moe_gemm_wide_kernel<1, 1> : moe_gemm_wide_kernel<0, 1>)
          : (a.epilogue ? moe_gemm_wide_kernel<1, 0> : moe_gemm_wide_kernel<0, 0>);
-  const hipError_t st = ensure_lds(k, kWideLds);
+  st = ensure_lds(k, kWideLds);
   if (st != hipSuccess) return st;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kWideThreads), kWideLds, stream, a, table);
   return hipGetLastError();

@@ -36,11 +36,11 @@ PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 
 # HBM bytes per launch of the gate_up GEMM (the layer's dominant kernel, expert-wide tiles at
-# block 32), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy: 915,840 KiB
-# read + 49,152 KiB written (profiles/prefill_layer_wide_tiles.md).  Only valid for that kernel
-# configuration; None for any other block size or once the kernel has changed since the
-# counters were taken.
-GATE_UP_TRAFFIC = {"block_m": 32, "bytes": 988151808}
+# block 32), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy: 457,972 KiB
+# of FETCH_SIZE (x 2: 915,944 KiB read) + 49,152 KiB written
+# (profiles/prefill_layer_wide_tiles.md).  Only valid for that kernel configuration; None for
+# any other block size or once the kernel has changed since the counters were taken.
+GATE_UP_TRAFFIC = {"block_m": 32, "bytes": 988258763}
 
 
 def log(msg):

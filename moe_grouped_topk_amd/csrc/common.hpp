@@ -58,16 +58,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// Workgroups of a 1-D grid are handed to the XCDs round-robin (id i goes to
-// XCD i % 8).  This maps the hardware id onto a logical tile id so that each
-// XCD receives one contiguous run of logical tiles; tiles that share
-// operands then share that XCD's L2.  Bijective on [0, n).
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
-  const int q = n / kNumXcd, r = n % kNumXcd;
-  return xcd * q + (xcd < r ? xcd : r) + slot;
-}
-
 // z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each);
 // for z -> -inf the reciprocal of +inf gives 0, for z -> +inf it gives z.
 __device__ __forceinline__ float silu_f32(float z) {

@@ -30,12 +30,13 @@
 //    -> registers (rounded to bf16) -> LDS with 128-byte K stages, LDS rows
 //    padded to 144 bytes so every group of 8 lanes reading 16 bytes hits 8
 //    distinct bank quads.
-//  * Tiles are numbered block-major (the n-tiles of a block adjacent, the
-//    blocks of one expert adjacent).  The tile kernels hand consecutive
-//    tiles to consecutive XCDs (each XCD streams a share of every expert's
-//    weights); the expert-wide kernel gives each XCD one contiguous run of
-//    tiles (xcd_remap), so an expert's gathered rows are shared in one XCD's
-//    L2; the GMM deals each expert's weight slices to the XCDs in turn.
+//  * Workgroups of a 1-D grid go to the 8 XCDs round-robin (id i to XCD
+//    i % 8).  Tiles are numbered block-major (the n-tiles of a block
+//    adjacent, the blocks of one expert adjacent).  The tile kernels hand
+//    consecutive tiles to consecutive XCDs (each XCD streams a share of
+//    every expert's weights); the expert-wide kernel gives each XCD one
+//    contiguous run of tiles, so an expert's gathered rows are shared in one
+//    XCD's L2; the GMM deals each expert's weight slices to the XCDs in turn.
 
 #include "common.hpp"
 #include "launch.hpp"

@@ -1061,7 +1061,7 @@ __device__ __forceinline__ int gmm_units_on(int p, int ntile, int xcd) {
 __device__ __forceinline__ void gmm_build_order(const GmmI8Args& a, int ntile, int xcd,
                                                 GmmOrder& o, int* work) {
   constexpr int BM = GmmCfg::BM, NT = GmmCfg::THREADS;
-  static_assert(kMaxGmmExperts <= 2 * NT, "two sorted positions per thread");
+  constexpr int PER = (kMaxGmmExperts + NT - 1) / NT;   // sorted positions per thread
   const int tid = tile_tid(), E = a.E, E4 = (E + 3) & ~3;
   int* rows = work;                 // [E4]; -1 past E sorts after every expert
   int* scan_buf = work + E4;        // [NT]
@@ -1088,14 +1088,15 @@ __device__ __forceinline__ void gmm_build_order(const GmmI8Args& a, int ntile, i
   }
   __syncthreads();
   // this XCD's tiles per sorted position, then their exclusive prefix
-  const int p0 = tid * 2;
-  int cnt[2] = {0, 0};
+  const int p0 = tid * PER;
+  int cnt[PER];
+  int local = 0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < PER; ++j) {
     const int p = p0 + j;
-    if (p < E) cnt[j] = (rows[o.order[p]] + BM - 1) / BM * gmm_units_on(p, ntile, xcd);
+    cnt[j] = p < E ? (rows[o.order[p]] + BM - 1) / BM * gmm_units_on(p, ntile, xcd) : 0;
+    local += cnt[j];
   }
-  const int local = cnt[0] + cnt[1];
   scan_buf[tid] = local;
   __syncthreads();
   for (int off = 1; off < NT; off <<= 1) {
@@ -1104,9 +1105,12 @@ __device__ __forceinline__ void gmm_build_order(const GmmI8Args& a, int ntile, i
     scan_buf[tid] += add;
     __syncthreads();
   }
-  const int run = scan_buf[tid] - local;
-  if (p0 < E) o.prefix[p0] = run;
-  if (p0 + 1 < E) o.prefix[p0 + 1] = run + cnt[0];
+  int run = scan_buf[tid] - local;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (p0 + j < E) o.prefix[p0 + j] = run;
+    run += cnt[j];
+  }
   if (tid == NT - 1) o.prefix[E] = scan_buf[tid];
   __syncthreads();
 }

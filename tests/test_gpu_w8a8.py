@@ -27,7 +27,10 @@ def moe(dev):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("rows,cols,ld", [(37, 64, 64), (5, 2048, 2048), (9, 200, 264)])
+@pytest.mark.parametrize("rows,cols,ld", [
+    (37, 64, 64), (5, 2048, 2048), (9, 200, 264),   # 32 lanes per row / 64 lanes
+    (11, 768, 768), (6, 1024, 1040), (7, 1536, 1536),   # 3 chunks per lane; 64 lanes x 2, x 3
+    (3, 2056, 2056)])                                  # past 2048 columns: read twice
 def test_quantize_rows_bit_exact(moe, dev, dtype, rows, cols, ld):
     rng = np.random.default_rng(rows * cols + ld)
     x = (rng.standard_normal((rows, ld)) * rng.uniform(1e-3, 1e3, (rows, 1))).astype(np.float32)

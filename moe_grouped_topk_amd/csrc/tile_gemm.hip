@@ -1599,7 +1599,7 @@ struct WideTile {
 };
 
 __device__ __forceinline__ WideTile wide_tile_at(const MoeGemmArgs& a, const int32_t* table,
-                                                 int ntile, int L) {
+                                                 int ntiles, int ntile, int L) {
   WideTile w;
   const int j = L / ntile;
   w.nt = L % ntile;
@@ -1609,7 +1609,7 @@ __device__ __forceinline__ WideTile wide_tile_at(const MoeGemmArgs& a, const int
   w.valid = !(w.e < 0 || w.e >= a.E || w.b0 < 0 || w.nb < 1 || w.nb > kWideMaxBlk ||
               (int64_t)(w.b0 + w.nb) * kWideBlk > a.max_padded);
   w.stream = a.b_packed != 0 && (j == 0 || table[1 + 3 * (j - 1)] != w.e) &&
-             (j + 1 >= table[0] || table[1 + 3 * (j + 1)] != w.e);
+             (j + 1 >= ntiles || table[1 + 3 * (j + 1)] != w.e);
   return w;
 }
 
@@ -1690,7 +1690,10 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
   uint8_t* stage_lds = smem + (kWideNW - 1) * kWideWStage;
   constexpr int kStageBytes = kWideWStage + kWideNT * kWideTStage;
   const int ntile = moe_ntiles<kWideBN, EPI>(a);
-  const int live = table[0] * ntile;
+  // tiles in the table, never more than its room: one per block at most
+  const int64_t nblk = a.max_padded / kWideBlk;
+  const int ntiles = (int)(table[0] < 0 ? 0 : (table[0] < nblk ? table[0] : nblk));
+  const int live = ntiles * ntile;
   const int xcd = (int)blockIdx.x % kNumXcd;
   const int q = live / kNumXcd, r = live % kNumXcd;
   const int run0 = xcd * q + (xcd < r ? xcd : r), runlen = q + (xcd < r ? 1 : 0);
@@ -1712,9 +1715,9 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
   };
   const int S = (int)gridDim.x / kNumXcd, slot = (int)blockIdx.x / kNumXcd;
   int pos = slot;
-  while (pos < runlen && !wide_tile_at(a, table, ntile, run0 + pos).valid) pos += S;
+  while (pos < runlen && !wide_tile_at(a, table, ntiles, ntile, run0 + pos).valid) pos += S;
   if (pos >= runlen) return;
-  WideTile w = wide_tile_at(a, table, ntile, run0 + pos);
+  WideTile w = wide_tile_at(a, table, ntiles, ntile, run0 + pos);
   int pair = row_pair(w);                              // this thread's row of the tile
   bool w_issued = false;
   for (;;) {
@@ -1786,11 +1789,11 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
     // read now too)
     __syncthreads();
     int next = pos + S;
-    while (next < runlen && !wide_tile_at(a, table, ntile, run0 + next).valid) next += S;
+    while (next < runlen && !wide_tile_at(a, table, ntiles, ntile, run0 + next).valid) next += S;
     w_issued = next < runlen;
     WideTile wn_tile = w;
     if (w_issued) {
-      wn_tile = wide_tile_at(a, table, ntile, run0 + next);
+      wn_tile = wide_tile_at(a, table, ntiles, ntile, run0 + next);
       WideSrc nsrc;
       wide_weight_src<EPI, KIND>(a, wn_tile, wave, lane, nsrc);
       wide_prefetch_w(smem, nsrc, wrow_bytes);

@@ -1812,15 +1812,20 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
     const int rsub = 4 * (elane >> 5);
     uint8_t* Cb = reinterpret_cast<uint8_t*>(a.C);
     const f32x4_t one4 = {1.0f, 1.0f, 1.0f, 1.0f};
+    // The scale reads are volatile, so that they are not hoisted out of the
+    // token-block loop (where the 8 column scale vectors would hold 32
+    // registers beside the accumulators), through pointers typed as LDS: a
+    // volatile read through a generic pointer compiles to a flat load, which
+    // counts in vmcnt and so waits for the next tile's weight stages.
+    typedef __attribute__((address_space(3))) const volatile float lds_cvf;
+    typedef __attribute__((address_space(3))) const volatile f32x4_t lds_cvf4;
     auto row_scale = [&](int trow) -> float {   // trow a row of the tile
       if constexpr (KIND == 0) return 1.0f;
-      return *reinterpret_cast<const volatile float*>(s_as + trow);
+      return *(lds_cvf*)(s_as + trow);
     };
     auto col_scale = [&](int c) -> f32x4_t {    // weight rows c .. c + 3 of the tile
       if constexpr (KIND == 0) return one4;
-      // read where used (volatile: not hoisted out of the token-block loop,
-      // where the 8 values would hold 32 registers beside the accumulators)
-      return *reinterpret_cast<const volatile f32x4_t*>(s_bs + c);
+      return *(lds_cvf4*)(s_bs + c);
     };
     if (!EPI && etid < kWideBM) s_w[etid] = wr;
     // pass p stages the token blocks [p * BPP, (p + 1) * BPP) of the tile

@@ -14,7 +14,7 @@ and times the oracle on a bounded sample of the prefill workload on the
 host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-       python bench.py --component decode16|decode64|int8gmm|routing|tiny
+       python bench.py --component decode16|decode64|int8gmm|routing|tiny|w8a8
 The second form runs one of the secondary measurements alone and prints its
 result as one JSON object (for profiling a single workload).
 """
@@ -195,6 +195,26 @@ def w8a8_weights(torch, moe, w1, w2):
     return p1, s1, p2, s2
 
 
+def bench_w8a8(torch, moe, dev, steps, warmup, inputs=None):
+    """The prefill layer with int8 weights and int8 activations
+    (moe_forward_w8a8), on the prefill layer's inputs (made here if not
+    given: x, gating, w1, w2 on the device)."""
+    import synth
+    cfg = synth.CONFIGS["prefill"]
+    T, H, I, E, K = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
+    if inputs is None:
+        inputs = layer_inputs(torch, cfg, dev)[:4]
+    x, g, w1, w2 = inputs
+    q1, s1, q2, s2 = w8a8_weights(torch, moe, w1, w2)
+    ws8 = torch.empty(moe.moe_forward_w8a8_workspace_size(T, H, I, E, K), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty_like(x)
+    ms8 = wall_steps(torch, lambda: moe.moe_forward_w8a8(x, g, q1, s1, q2, s2, K, out=out,
+                                                         workspace=ws8), steps, warmup)
+    flops = 6.0 * T * K * H * I
+    return dict(ms=ms8, tops=flops / ms8 * 1e-9, frac_int8=flops / ms8 * 1e-9 / PEAK_INT8_TOPS)
+
+
 def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True, before=None):
     """The prefill layer.  before() runs right before the warm-up steps (the
     calibration GEMMs: GPU work that brings the clock up after the host-side
@@ -227,14 +247,7 @@ def bench_prefill(torch, moe, dev, steps, warmup, timer, plain=True, before=None
         ms_plain = wall_steps(torch, step_plain, steps, warmup)
         res["plain_weights"] = dict(ms=ms_plain, tflops=flops / ms_plain * 1e-9)
         # the same layer with int8 weights and int8 activations (moe_forward_w8a8)
-        q1, s1, q2, s2 = w8a8_weights(torch, moe, w1_plain, w2_plain)
-        ws8 = torch.empty(moe.moe_forward_w8a8_workspace_size(T, H, I, E, K), dtype=torch.uint8,
-                          device=dev)
-        ms8 = wall_steps(torch, lambda: moe.moe_forward_w8a8(x, g, q1, s1, q2, s2, K, out=out,
-                                                             workspace=ws8), steps, warmup)
-        res["w8a8"] = dict(ms=ms8, tops=flops / ms8 * 1e-9,
-                           frac_int8=flops / ms8 * 1e-9 / PEAK_INT8_TOPS)
-        del q1, q2, ws8
+        res["w8a8"] = bench_w8a8(torch, moe, dev, steps, warmup, (x, g, w1_plain, w2_plain))
 
     # Per-kernel breakdown: the launches moe_forward makes (route, the
     # two-kernel alignment, gate_up with SiLU*up, down with the routing
@@ -498,7 +511,8 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="prefill headline only")
-    ap.add_argument("--component", choices=["decode16", "decode64", "int8gmm", "routing", "tiny"],
+    ap.add_argument("--component", choices=["decode16", "decode64", "int8gmm", "routing", "tiny",
+                                            "w8a8"],
                     help="run this secondary measurement alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true",
@@ -525,7 +539,8 @@ def main():
                                                timer),
               "int8gmm": lambda: bench_int8(torch, moe, dev, args.steps, args.warmup, timer),
               "routing": lambda: bench_routing(torch, moe, dev, args.steps, args.warmup, timer),
-              "tiny": lambda: bench_tiny(torch, moe, dev, args.steps, args.warmup, timer)}
+              "tiny": lambda: bench_tiny(torch, moe, dev, args.steps, args.warmup, timer),
+              "w8a8": lambda: bench_w8a8(torch, moe, dev, args.steps, args.warmup)}
         res = fn[args.component]()
         if args.copy_calibration:
             copy_calibration(torch, dev)

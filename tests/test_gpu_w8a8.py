@@ -121,10 +121,10 @@ def _device_quantize(w):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["prefill", "decode16"])
+@pytest.mark.parametrize("name", ["prefill", "decode16", "decode64"])
 def test_w8a8_layer_full(moe, dev, name):
-    """Every output row of the int8 layer at the prefill and decode (T=16)
-    shapes, packed weights, against the oracle's int8 layer run on the
+    """Every output row of the int8 layer at the prefill and decode (T=16 and
+    T=64) shapes, packed weights, against the oracle's int8 layer run on the
     routing the GPU accepted (itself checked against the oracle's)."""
     cfg = synth.CONFIGS[name]
     d = layer_inputs(cfg, dev)

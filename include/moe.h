@@ -30,6 +30,8 @@
  *     events).
  *   - Process-wide state, all of it set once and never freed:
  *       * each kernel's dynamic-LDS limit is raised on its first launch;
+ *       * the compute-unit count of each device (it sizes the persistent
+ *         grid of the expert-wide GEMMs), read on its first use there;
  *       * the static scratch of moe_forward_noalloc (one array per device,
  *         its address looked up once per device).
  */

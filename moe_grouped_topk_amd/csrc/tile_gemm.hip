@@ -17,8 +17,8 @@
 //  * Token rows are gathered straight from x into LDS by pair index; the
 //    gathered tensor never exists in HBM.  Placeholder rows are masked at
 //    the store.
-//  * Main path (bf16 and int8 operands, moe_gemm_dma_kernel,
-//    gmm_i8_tile_kernel): BN = 256 weight rows x BM =
+//  * Tile kernels (bf16 and int8 operands, moe_gemm_dma_kernel: decode and
+//    experts with few rows; gmm_i8_tile_kernel): BN = 256 weight rows x BM =
 //    64/128/256 tokens per tile, loaded with direct-to-LDS loads
 //    (global_load_lds_dwordx4) into an NSTAGE ring of 64-byte K stages, with
 //    no staging registers.  Weights may come pre-packed (moe_pack_weights) so
@@ -26,6 +26,13 @@
 //    workgroups per CU at BM 64/128: one workgroup's MFMAs run while the
 //    other waits for its loads.  Epilogues stage 16-bit output through LDS
 //    and store whole 16-byte pieces of each output row.
+//  * Expert-wide tiles (moe_gemm_wide_kernel: the prefill path, bf16 or
+//    int8 operands): up to 10 token blocks (320 rows) of one expert against
+//    256 weight rows, so each weight slice streams once per expert; one
+//    persistent workgroup per CU; weight and token rings of their own (4 + 4
+//    stages), loads issued between the MFMAs; the next tile's first weight
+//    stages go out before the epilogue, which is staged in the LDS the next
+//    tile does not use yet.
 //  * float32 tokens (moe_gemm_tile_kernel): 4 waves in a 2 x 2 grid, global
 //    -> registers (rounded to bf16) -> LDS with 128-byte K stages, LDS rows
 //    padded to 144 bytes so every group of 8 lanes reading 16 bytes hits 8

@@ -630,6 +630,18 @@ __device__ __forceinline__ f32x4_t acc4(const i32x16_t& a, int g, float as, cons
   return f32x4_t{(float)a[4 * g] * as * bs[0], (float)a[4 * g + 1] * as * bs[1],
                  (float)a[4 * g + 2] * as * bs[2], (float)a[4 * g + 3] * as * bs[3]};
 }
+// Outputs 4g .. 4g+3 of a row without the SiLU epilogue (the down GEMM):
+// the bf16 MFMA sums times the row's routing weight w, or the exact int32
+// sums times the row factor rf = a_scales[row] * w (one product per row),
+// then the four channel scales: two multiplies per output, all epilogues
+// of this GEMM in the same order.
+__device__ __forceinline__ f32x4_t row4(const f32x16_t& a, int g, float w, const f32x4_t&) {
+  return f32x4_t{a[4 * g] * w, a[4 * g + 1] * w, a[4 * g + 2] * w, a[4 * g + 3] * w};
+}
+__device__ __forceinline__ f32x4_t row4(const i32x16_t& a, int g, float rf, const f32x4_t& bs) {
+  return f32x4_t{(float)a[4 * g] * rf * bs[0], (float)a[4 * g + 1] * rf * bs[1],
+                 (float)a[4 * g + 2] * rf * bs[2], (float)a[4 * g + 3] * rf * bs[3]};
+}
 
 // Epilogue.  32x32 MFMA output: lane holds token column (lane & 31) and, for
 // g = 0..3, rows 8 g + 4 (lane >> 5) + [0, 4) of its 32-row block.
@@ -683,8 +695,8 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs& a, const MoeTile
           if (col < a.N) {
             f32x4_t sc = one4;
             if constexpr (KIND != 0) sc = *reinterpret_cast<const f32x4_t*>(bsc + col);
-            const f32x4_t v = acc4(acc[rb][cb], g, as, sc);
-            store4<CDT>(rowp + col * ce, v[0] * w, v[1] * w, v[2] * w, v[3] * w);
+            const f32x4_t v = row4(acc[rb][cb], g, KIND ? as * w : w, sc);
+            store4<CDT>(rowp + col * ce, v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -882,8 +894,8 @@ __device__ __forceinline__ void plain_epilogue_staged(const MoeGemmArgs& a, cons
           const int64_t gc = t.c0 + wrow[rb] + 8 * g + rsub;
           sc = *reinterpret_cast<const f32x4_t*>(bsc + (gc < a.N ? gc : 0));   // past N: never stored
         }
-        const f32x4_t v = acc4(acc[rb][cb], g, as, sc);
-        const float a0 = v[0] * w, a1 = v[1] * w, a2 = v[2] * w, a3 = v[3] * w;
+        const f32x4_t v = row4(acc[rb][cb], g, KIND ? as * w : w, sc);
+        const float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
         const uint2 o = CDT == 1 ? make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3))
                                  : make_uint2(pack_f16x2(a0, a1), pack_f16x2(a2, a3));
         *reinterpret_cast<uint2*>(dst + (wrow[rb] + 8 * g + rsub) * 2) = o;
@@ -1870,14 +1882,15 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
             }
           } else {
             const float wt = s_w[trow];
+            const float rf = KIND ? as * wt : wt;
 #pragma unroll
             for (int rb = 0; rb < kWideRB; ++rb) {
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
                 const int c = wrow[rb] + 8 * g + rsub;
-                const f32x4_t v = acc4(acc[rb][cb], g, as, col_scale(c));
+                const f32x4_t v = row4(acc[rb][cb], g, rf, col_scale(c));
                 *reinterpret_cast<uint2*>(dst + c * 2) = make_uint2(
-                    pack_bf16x2(v[0] * wt, v[1] * wt), pack_bf16x2(v[2] * wt, v[3] * wt));
+                    pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
               }
             }
           }

@@ -29,7 +29,9 @@
  *     write the same buffers must be ordered by the caller (same stream, or
  *     events).
  *   - Process-wide state, all of it set once and never freed:
- *       * each kernel's dynamic-LDS limit is raised on its first launch;
+ *       * each kernel's dynamic-LDS limit is raised on its first launch on a
+ *         device that needs more than 64 KiB (again only if a later launch
+ *         needs more), with a table of the limits raised;
  *       * the compute-unit count of each device (it sizes the persistent
  *         grid of the expert-wide GEMMs), read on its first use there;
  *       * the static scratch of moe_forward_noalloc (one array per device,

@@ -576,11 +576,8 @@ hipError_t launch_align_ws(const int32_t* topk_ids, int64_t P, int E, int B, int
                 int32_t*, int, int32_t*) =
       self ? align_place_kernel<true> : align_place_kernel<false>;
   const size_t lds = sizeof(int) * ((size_t)(E + 1) + (size_t)kPlaceWaves * E + E + 2 * kPlaceWaves);
-  if (lds > 65536) {
-    st = hipFuncSetAttribute((const void*)place, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)lds);
-    if (st != hipSuccess) return st;
-  }
+  st = raise_lds_limit(reinterpret_cast<const void*>(place), lds);
+  if (st != hipSuccess) return st;
   hipLaunchKernelGGL(place, dim3(nchunk), dim3(kPlaceThreads), lds, stream, topk_ids,
                      (int)P, E, B, (int)chunk, nchunk, hist, sorted_ids, expert_ids, total,
                      (int)max_padded, wide_table);
@@ -598,19 +595,15 @@ hipError_t launch_align(const int32_t* topk_ids, int64_t P, int E, int B,
     const bool cache = with_cache <= 160 * 1024;
     const size_t lds = cache ? with_cache : base;
     auto k = cache ? align_expert_kernel<true> : align_expert_kernel<false>;
-    if (lds > 65536) {
-      const hipError_t st =
-          hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (st != hipSuccess) return st;
-    }
+    const hipError_t st = raise_lds_limit(reinterpret_cast<const void*>(k), lds);
+    if (st != hipSuccess) return st;
     hipLaunchKernelGGL(k, dim3(E), dim3(kAlignEThreads), lds, stream, topk_ids, (int)P, E, B,
                        sorted_ids, expert_ids, total, (int)max_padded);
     return hipGetLastError();
   }
   const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E + (E + 1) + 2 * kAlignWaves);
-  if (lds > 65536) {
-    const hipError_t st = hipFuncSetAttribute(
-        (const void*)align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t st = raise_lds_limit(reinterpret_cast<const void*>(align_kernel), lds);
     if (st != hipSuccess) return st;
   }
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), lds, stream, topk_ids,

@@ -21,6 +21,12 @@ struct RouteExtra {
   int64_t nzero;
 };
 
+// Raises `kernel`'s dynamic-LDS limit on the current device to `bytes` when
+// a launch needs more than 64 KiB and more than was raised there before
+// (hipFuncSetAttribute once per kernel, device and larger size; the sizes
+// already raised are kept in a table for the life of the process).
+hipError_t raise_lds_limit(const void* kernel, size_t bytes);
+
 hipError_t launch_route(const float* gating, int64_t T, int E, int topk, int G,
                         int topk_group, int scoring, int renormalize, float scale,
                         float* out_w, int32_t* out_ids, hipStream_t stream,

@@ -49,7 +49,10 @@
 #include "launch.hpp"
 
 #include <atomic>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -1915,9 +1918,7 @@ moe_gemm_wide_kernel(MoeGemmArgs a, const int32_t* __restrict__ table) {
 // Dynamic LDS beyond 64 KiB has to be requested per kernel.
 template <typename K>
 hipError_t ensure_lds(K kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+  return raise_lds_limit(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 template <class C, int EPI, bool TF32, int CDT, int KIND = 0>
@@ -2025,6 +2026,21 @@ hipError_t launch_wide_prep(const int32_t* expert_ids, const int32_t* total, int
   hipLaunchKernelGGL(wide_prep_kernel, dim3(1), dim3(kWidePrepThreads), 0, stream, expert_ids,
                      total, E, (int)(max_padded / kWideBlk), table);
   return hipGetLastError();
+}
+
+hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t st = hipGetDevice(&dev);
+  if (st != hipSuccess) return st;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = raised[std::make_pair(kernel, dev)];
+  if (have >= bytes) return hipSuccess;
+  st = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (st == hipSuccess) have = bytes;
+  return st;
 }
 
 namespace {

@@ -150,6 +150,17 @@ def wall_steps(torch, fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def graph_of(torch, fn):
+    """fn (after one eager call) captured in a HIP graph, for replay."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
 def layer_inputs(torch, cfg, dev):
     import synth
     sub = cfg.extra.get("sub", 0)
@@ -450,7 +461,13 @@ def bench_tiny(torch, moe, dev, steps, warmup, timer):
 
     ms = wall_steps(torch, step, steps * 10, warmup)
     mean, med = timer.run(step, 100)
-    return dict(ms_wall=ms, event_median_us=med * 1e3)
+    # the same call captured once in a HIP graph and replayed (one graph
+    # launch per layer instead of one launch per kernel)
+    graph = graph_of(torch, step)
+    ms_g = wall_steps(torch, graph.replay, steps * 10, warmup)
+    _, med_g = timer.run(graph.replay, 100)
+    return dict(ms_wall=ms, event_median_us=med * 1e3, graph_ms_wall=ms_g,
+                graph_event_median_us=med_g * 1e3)
 
 
 def cpu_baseline(torch, prefill_inputs, target_s=12.0):
